@@ -1,0 +1,228 @@
+"""The synthetic workloads of the blockwise-attention hot path, with their accounting.
+
+Each workload is named for what it is.  Inputs are drawn by ``synth`` (seeded
+PCG64 normals rounded once to bf16, or kept fp32).  Algorithmic work is the
+minimum the method must do:
+
+* FLOPs = 4 * D * (number of visible (query row, key) pairs), the two matrix
+  products QK^T and PV of the per-step count 4 B^2 d in "RingAttention and
+  Context Parallelism", section 4; masked pairs are not counted.
+* Bytes = Q read once + every K/V row a query can see read once + the output
+  (or, for state-producing steps, the state) written once.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+
+from . import synth
+
+
+@dataclass
+class BlockwiseWorkload:
+    """A stationary query block walking K/V blocks in a given order."""
+
+    name: str
+    dtype: str                  # "bf16" or "f32" (Q, K, V storage)
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    q_len: int
+    q_pos0: int                 # absolute position of query row 0
+    block_len: int
+    n_blocks: int               # K/V blocks cover positions [0, n_blocks*block_len)
+    order: List[int]
+    causal: bool
+    seed: int
+    q_scale: float = 1.0
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+    note: str = ""
+
+    @property
+    def kv_len(self) -> int:
+        return self.block_len * self.n_blocks
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.head_dim))
+
+    @property
+    def rows(self) -> int:
+        return self.q_len * self.n_q_heads
+
+    def visible_keys_per_row(self, block: int) -> np.ndarray:
+        """Visible keys of ``block`` for each query token (length q_len)."""
+        pos0 = block * self.block_len
+        if not self.causal:
+            return np.full(self.q_len, self.block_len, dtype=np.int64)
+        q_pos = self.q_pos0 + np.arange(self.q_len, dtype=np.int64)
+        return np.clip(q_pos - pos0 + 1, 0, self.block_len)
+
+    def pairs(self) -> int:
+        """Visible (query token, key) pairs over the visited blocks, per query head."""
+        return int(sum(self.visible_keys_per_row(b).sum() for b in self.order))
+
+    def flops(self) -> float:
+        return 4.0 * self.head_dim * self.n_q_heads * self.pairs()
+
+    def visited_nonempty(self) -> List[int]:
+        return [b for b in self.order if self.visible_keys_per_row(b).max() > 0]
+
+    def bytes(self) -> int:
+        esz = 2 if self.dtype == "bf16" else 4
+        q = self.q_len * self.n_q_heads * self.head_dim * esz
+        kv = 2 * len(self.visited_nonempty()) * self.block_len * self.n_kv_heads * self.head_dim * esz
+        out = self.q_len * self.n_q_heads * self.head_dim * esz
+        return q + kv + out
+
+    def make_inputs(self):
+        """(q, k, v) synth.Tensors: q [q_len, Hq, D]; k, v [kv_len, Hkv, D]."""
+        g = synth.rng(self.seed)
+        q = synth.normal(g, (self.q_len, self.n_q_heads, self.head_dim), self.q_scale, self.dtype)
+        k = synth.normal(g, (self.kv_len, self.n_kv_heads, self.head_dim), self.k_scale, self.dtype)
+        v = synth.normal(g, (self.kv_len, self.n_kv_heads, self.head_dim), self.v_scale, self.dtype)
+        return q, k, v
+
+
+@dataclass
+class FanoutWorkload:
+    """Shared-prefix fan-out decode: one new query token per branch."""
+
+    name: str
+    n_branches: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    prefix_len: int
+    suffix_len: int
+    seed: int
+    q_scale: float = 0.5
+    k_scale: float = 0.5
+    v_scale: float = 0.5
+    dtype: str = "bf16"
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.head_dim))
+
+    @property
+    def rows(self) -> int:
+        return self.n_branches * self.n_q_heads
+
+    def flops(self) -> float:
+        keys = self.prefix_len + self.suffix_len
+        return 4.0 * self.head_dim * self.rows * keys
+
+    def bytes(self) -> int:
+        e = 2
+        q = self.rows * self.head_dim * e
+        prefix = 2 * self.prefix_len * self.n_kv_heads * self.head_dim * e
+        suffix = 2 * self.n_branches * self.suffix_len * self.n_kv_heads * self.head_dim * e
+        out = self.rows * self.head_dim * e
+        return q + prefix + suffix + out
+
+    def make_inputs(self):
+        """q [nb, Hq, D], prefix k/v [P, Hkv, D], suffix k/v [nb, S, Hkv, D], drawn in that order."""
+        g = synth.rng(self.seed)
+        D, Hq, Hkv = self.head_dim, self.n_q_heads, self.n_kv_heads
+        q = synth.normal(g, (self.n_branches, Hq, D), self.q_scale, self.dtype)
+        pk = synth.normal(g, (self.prefix_len, Hkv, D), self.k_scale, self.dtype)
+        pv = synth.normal(g, (self.prefix_len, Hkv, D), self.v_scale, self.dtype)
+        sk = synth.normal(g, (self.n_branches, self.suffix_len, Hkv, D), self.k_scale, self.dtype)
+        sv = synth.normal(g, (self.n_branches, self.suffix_len, Hkv, D), self.v_scale, self.dtype)
+        return q, pk, pv, sk, sv
+
+
+@dataclass
+class ShardMergeWorkload:
+    """Per-shard partial states of a few query rows, then an n-way LSE merge.
+
+    The query rows are ``n_branches`` tokens x ``n_q_heads`` heads of one KV
+    head group; the K/V sequence of that group is split into ``n_shards``
+    contiguous shards.
+    """
+
+    name: str
+    n_branches: int
+    n_q_heads: int
+    head_dim: int
+    kv_len: int
+    n_shards: int
+    seed: int
+    q_scale: float = 0.5
+    k_scale: float = 12.0
+    v_scale: float = 0.5
+    dtype: str = "bf16"
+    n_kv_heads: int = 1
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.head_dim))
+
+    @property
+    def shard_len(self) -> int:
+        return self.kv_len // self.n_shards
+
+    @property
+    def rows(self) -> int:
+        return self.n_branches * self.n_q_heads
+
+    def flops(self) -> float:
+        return 4.0 * self.head_dim * self.rows * self.kv_len
+
+    def sweep_bytes(self) -> int:
+        """K/V read once + Q read + every shard's fp32 partial written once and read once."""
+        kv = 2 * self.kv_len * self.n_kv_heads * self.head_dim * 2
+        q = self.rows * self.head_dim * 2
+        partials = 2 * self.n_shards * self.rows * (self.head_dim + 2) * 4
+        out = self.rows * self.head_dim * 2
+        return kv + q + partials + out
+
+    def merge_bytes(self) -> int:
+        return (self.n_shards + 1) * self.rows * (self.head_dim + 2) * 4
+
+    def make_inputs(self):
+        """q [nb, Hq, D]; k, v [kv_len, 1, D]; drawn Q, K, V."""
+        g = synth.rng(self.seed)
+        q = synth.normal(g, (self.n_branches, self.n_q_heads, self.head_dim), self.q_scale, self.dtype)
+        k = synth.normal(g, (self.kv_len, self.n_kv_heads, self.head_dim), self.k_scale, self.dtype)
+        v = synth.normal(g, (self.kv_len, self.n_kv_heads, self.head_dim), self.v_scale, self.dtype)
+        return q, k, v
+
+
+def ring_order(k: int, n: int) -> List[int]:
+    """Blocks device k visits, (k - t) mod n at step t (ring direction of the llms.blog page, section 3)."""
+    return [(k - t) % n for t in range(n)]
+
+
+TINY_EXACT = BlockwiseWorkload(
+    name="tiny_exact_f32: 1 head, D64, fp32, 256 queries vs 4 blocks of 256 keys, order 1,2,3,0",
+    dtype="f32", n_q_heads=1, n_kv_heads=1, head_dim=64, q_len=256, q_pos0=0,
+    block_len=256, n_blocks=4, order=[1, 2, 3, 0], causal=False, seed=1)
+
+CAUSAL_PREFILL = BlockwiseWorkload(
+    name="causal_prefill_32k: bf16 GQA 64/8 D128, query block 7 of 8x4096, causal",
+    dtype="bf16", n_q_heads=64, n_kv_heads=8, head_dim=128, q_len=4096, q_pos0=7 * 4096,
+    block_len=4096, n_blocks=8, order=ring_order(7, 8), causal=True, seed=2,
+    q_scale=0.5, k_scale=0.5, v_scale=0.5)
+
+RING_SHARE = BlockwiseWorkload(
+    name="ring_share_256k: bf16 GQA 64/8 D128, query block 12 of 16x16384, causal, one call per visit",
+    dtype="bf16", n_q_heads=64, n_kv_heads=8, head_dim=128, q_len=16384, q_pos0=12 * 16384,
+    block_len=16384, n_blocks=16, order=ring_order(12, 16), causal=True, seed=3,
+    q_scale=0.5, k_scale=0.5, v_scale=0.5)
+
+FANOUT_DECODE = FanoutWorkload(
+    name="fanout_decode_64k: bf16 GQA 64/8 D128, prefix 65536, 16 branches x 512 suffix, 1 token each",
+    n_branches=16, n_q_heads=64, n_kv_heads=8, head_dim=128, prefix_len=65536,
+    suffix_len=512, seed=4)
+
+SHARD_MERGE = ShardMergeWorkload(
+    name="shard_merge_1m: bf16 D128, 8 branches x 8 heads of one KV group, 1048576 keys in 32 shards, logits ~ +-30",
+    n_branches=8, n_q_heads=8, head_dim=128, kv_len=1048576, n_shards=32, seed=5)
+
+ALL = [TINY_EXACT, CAUSAL_PREFILL, RING_SHARE, FANOUT_DECODE, SHARD_MERGE]

@@ -1,0 +1,115 @@
+"""Plant plausible mistakes in the oracle (CPU only) and check a pin catches each.
+
+A pin set that a dropped term, a wrong sign or index, or a transposed operand
+slips through would not be pinning anything.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import attention as ora
+from tests import oracle_pins
+
+_orig_state_fn = ora.softmax_state
+_orig_merge = ora.merge
+_orig_online_step = ora.online_step
+_orig_finalize = ora.finalize
+
+
+def _no_scale(q_rows, k_rows, scale):
+    return q_rows @ k_rows.T
+
+
+def _strict_causal(q_pos, k_pos):
+    return k_pos[None, :] < q_pos[:, None]
+
+
+def _reversed_causal(q_pos, k_pos):
+    return k_pos[None, :] >= q_pos[:, None]
+
+
+def _modulo_gqa(h, n_q_heads, n_kv_heads):
+    return h % n_kv_heads
+
+
+def _unshifted_softmax(z, v_rows):
+    with np.errstate(over="ignore", invalid="ignore"):
+        w = np.exp(z)
+        m = z.max(axis=1) if z.shape[1] else np.full(z.shape[0], -np.inf)
+        l = w.sum(axis=1) * np.exp(-m)
+        o = (w @ v_rows) * np.exp(-m)[:, None]
+    return m, l, o
+
+
+def _v_is_k(z, v_rows):
+    m, l, o = _orig_state_fn(z, v_rows)
+    return m, l, o[:, ::-1].copy()
+
+
+def _dropped_l_term(z, v_rows):
+    m, l, o = _orig_state_fn(z, v_rows)
+    return m, np.ones_like(l), o
+
+
+def _merge_no_weights(parts):
+    ms = np.stack([p[0] for p in parts])
+    return ms.max(axis=0), sum(p[1] for p in parts), sum(p[2] for p in parts)
+
+
+def _merge_min(parts):
+    ms = np.stack([np.asarray(p[0]) for p in parts])
+    m_star = np.where(np.isneginf(ms), np.inf, ms).min(axis=0)
+    m_star = np.where(np.isinf(m_star), -np.inf, m_star)
+    base = np.where(np.isneginf(m_star), 0.0, m_star)
+    w = np.where(np.isneginf(ms), 0.0, np.exp(ms - base[None]))
+    return m_star, (w * np.stack([p[1] for p in parts])).sum(0), (w[..., None] * np.stack([p[2] for p in parts])).sum(0)
+
+
+def _online_no_alpha_on_o(st, q, k_blk, v_blk, scale, q_pos=None, k_pos_blk=None, causal=False):
+    m_old, l_old, o_old = st
+    m_new, l_new, o_new = _orig_online_step(st, q, k_blk, v_blk, scale, q_pos, k_pos_blk, causal)
+    fresh = _orig_online_step(ora.init_state(*o_old.shape), q, k_blk, v_blk, scale, q_pos, k_pos_blk, causal)
+    # O_new = O_old + P V (rescale of the old accumulator dropped)
+    base = np.where(np.isneginf(m_new), 0.0, m_new)
+    fb = np.where(np.isneginf(fresh[0]), 0.0, fresh[0])
+    pv = fresh[2] * np.exp(fb - base)[..., None]
+    return m_new, l_new, o_old + pv
+
+
+def _finalize_no_log(m, l, o):
+    a, lse = _orig_finalize(m, l, o)
+    return a, np.where(np.isneginf(lse), lse, m + l)
+
+
+def _ring_wrong_direction(k, n):
+    return [(k + t) % n for t in range(n)]
+
+
+MUTATIONS = {
+    "dropped scale": ("scaled_logits", _no_scale),
+    "diagonal excluded from causal mask": ("causal_visible", _strict_causal),
+    "causal mask reversed": ("causal_visible", _reversed_causal),
+    "GQA head mapping h % Hkv": ("kv_head_of", _modulo_gqa),
+    "softmax without max shift": ("softmax_state", _unshifted_softmax),
+    "output accumulates a permuted V": ("softmax_state", _v_is_k),
+    "denominator term dropped": ("softmax_state", _dropped_l_term),
+    "merge without exp(m_s - m*) weights": ("merge", _merge_no_weights),
+    "merge takes the min": ("merge", _merge_min),
+    "recurrence drops the O rescale": ("online_step", _online_no_alpha_on_o),
+    "LSE without the log": ("finalize", _finalize_no_log),
+    "ring rotates the wrong way": ("ring_order", _ring_wrong_direction),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(ora, attr, fn)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except (AssertionError, FloatingPointError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake: {name}"
