@@ -1,0 +1,357 @@
+"""Benchmark of the blockwise-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--no-secondary]
+
+A step is one pass of the hot path over one batch of synthetic input: the
+headline workload is causal prefill of one 4096-token query block (GQA 64/8,
+head_dim 128, bf16) against 8 K/V blocks of 4096 visited in ring order
+7, 6, ..., 0 with fp32 (m, l, O) state, then finalisation to bf16.  ``value``
+is algorithmic TFLOP/s (4 * D * Hq * visible (query, key) pairs per step).
+
+The line also carries the roofline of the dominant kernel (measured live with
+HIP events on the stream it runs on), the CPU oracle timed on a bounded
+sample of the same workload, and secondary measurements of the other
+workloads (ring share, fan-out decode, sharded merge, scaled merge).
+Prints exactly one JSON line (on stdout); progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "attention fwd TFLOP/s + MFMA util %; fan-out decode HBM GB/s (1 GPU)"
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def traffic_record(kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match the current sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(kernel)
+    if not entry:
+        return None
+    from exact_blockwise_long_amd import build
+    if entry.get("source_sha256") != build.sources_digest():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+class Timer:
+    """HIP events on the current stream, i.e. the stream the library launches on."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, e0):
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e1.record()
+        self.pairs.append((e0, e1))
+
+    def mean_ms(self):
+        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs]))
+
+    def median_ms(self):
+        return float(np.median([a.elapsed_time(b) for a, b in self.pairs]))
+
+
+def bench_prefill(torch, ba, H, w, steps, warmup):
+    """Headline: fwd_block over all visits in one call + finalize."""
+    log(f"inputs: {w.name}")
+    q, k, v = w.make_inputs()
+    qd, kd, vd = H.to_device(q), H.to_device(k), H.to_device(v)
+    blocks = [(kd[b * w.block_len:(b + 1) * w.block_len], vd[b * w.block_len:(b + 1) * w.block_len],
+               b * w.block_len) for b in range(w.n_blocks)]
+    st = ba.new_state(w.rows, w.head_dim)
+    out = torch.empty(w.rows, w.head_dim, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(w.rows, dtype=torch.float32, device="cuda")
+
+    def step(timer=None):
+        e0 = timer.start() if timer else None
+        ba.fwd_block(qd, blocks, w.order, st, reset=True, n_kv_heads=w.n_kv_heads, q_pos0=w.q_pos0,
+                     causal=w.causal)
+        if timer:
+            timer.stop(e0)
+        ba.finalize(st, out=out, lse=lse)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(timer)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / steps
+    flops = w.flops()
+    kernel_ms = timer.mean_ms()
+    log(f"prefill: {ms_step:.3f} ms/step, walk kernel {kernel_ms:.3f} ms, {flops / ms_step / 1e9:.1f} TFLOP/s")
+    return dict(q=q, k=k, v=v, ms_step=ms_step, kernel_ms=kernel_ms, flops=flops)
+
+
+def bench_ring_share(torch, ba, H, w, steps, warmup):
+    """One fwd_block call per ring visit (state carried in HBM) + finalize."""
+    log(f"inputs: {w.name}")
+    q, k, v = w.make_inputs()
+    qd, kd, vd = H.to_device(q), H.to_device(k), H.to_device(v)
+    del q, k, v
+    blocks = [(kd[b * w.block_len:(b + 1) * w.block_len], vd[b * w.block_len:(b + 1) * w.block_len],
+               b * w.block_len) for b in range(w.n_blocks)]
+    st = ba.new_state(w.rows, w.head_dim)
+    out = torch.empty(w.rows, w.head_dim, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(w.rows, dtype=torch.float32, device="cuda")
+
+    def step():
+        for i, j in enumerate(w.order):
+            ba.fwd_block(qd, blocks, [j], st, reset=(i == 0), n_kv_heads=w.n_kv_heads, q_pos0=w.q_pos0,
+                         causal=w.causal)
+        ba.finalize(st, out=out, lse=lse)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    tf = w.flops() / ms / 1e9
+    log(f"ring share: {ms:.2f} ms/step, {tf:.1f} TFLOP/s")
+    return {"workload": w.name, "ms_per_step": round(ms, 3), "TFLOP/s": round(tf, 1),
+            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "visits": len(w.order),
+            "calls": "one fwd_block per visit, state carried in HBM"}
+
+
+def flush_buffer(torch):
+    return torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+
+def bench_fanout(torch, ba, H, w, steps, warmup):
+    log(f"inputs: {w.name}")
+    ins = w.make_inputs()
+    dev = [H.to_device(t) for t in ins]
+    nb, Hq, D = dev[0].shape
+    out = torch.empty(nb, Hq, D, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(nb, Hq, dtype=torch.float32, device="cuda")
+    ws = torch.empty(ba.fanout_workspace_bytes(nb, Hq, w.n_kv_heads, D, w.prefix_len, w.suffix_len),
+                     dtype=torch.uint8, device="cuda")
+    flush = flush_buffer(torch)
+    for _ in range(warmup):
+        ba.fanout_prefix_decode(*dev, workspace=ws, out=out, lse=lse)
+    timer = Timer(torch)
+    for _ in range(steps):
+        flush.fill_(1)  # evicts L2 and the 256 MB infinity cache between timed calls
+        e0 = timer.start()
+        ba.fanout_prefix_decode(*dev, workspace=ws, out=out, lse=lse)
+        timer.stop(e0)
+    torch.cuda.synchronize()
+    ms = timer.median_ms()
+    gbs = w.bytes() / ms / 1e6
+    log(f"fanout: {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
+    return {"workload": w.name, "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": w.bytes(),
+            "timing": "median over steps, HIP events around the call, 1 GiB cache flush between calls"}
+
+
+def bench_shard_merge(torch, ba, H, w, steps, warmup):
+    log(f"inputs: {w.name}")
+    q, k, v = w.make_inputs()
+    qd, kd, vd = H.to_device(q), H.to_device(k), H.to_device(v)
+    sl = w.shard_len
+    blocks = [(kd[i * sl:(i + 1) * sl], vd[i * sl:(i + 1) * sl], i * sl) for i in range(w.n_shards)]
+    states = [ba.new_state(w.rows, w.head_dim) for _ in range(w.n_shards)]
+    merged = ba.new_state(w.rows, w.head_dim)
+    out = torch.empty(w.rows, w.head_dim, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(w.rows, dtype=torch.float32, device="cuda")
+    flush = flush_buffer(torch)
+    t_all, t_merge = Timer(torch), Timer(torch)
+
+    def step(timed):
+        e0 = t_all.start() if timed else None
+        ba.shard_states(qd, blocks, states, n_kv_heads=1)
+        e1 = t_merge.start() if timed else None
+        ba.merge_states(states, merged)
+        if timed:
+            t_merge.stop(e1)
+        ba.finalize(merged, out=out, lse=lse)
+        if timed:
+            t_all.stop(e0)
+
+    for _ in range(warmup):
+        step(False)
+    for _ in range(steps):
+        flush.fill_(1)
+        step(True)
+    torch.cuda.synchronize()
+    ms = t_all.median_ms()
+    gbs = w.sweep_bytes() / ms / 1e6
+    merge_us = t_merge.median_ms() * 1e3
+    log(f"shard merge: sweep {ms * 1e3:.1f} us ({gbs:.0f} GB/s), 32-way merge {merge_us:.1f} us")
+    return {"workload": w.name, "sweep_us": round(ms * 1e3, 2), "sweep_GB/s": round(gbs, 1),
+            "sweep_frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "merge_us": round(merge_us, 2),
+            "merge_bytes": w.merge_bytes()}
+
+
+def bench_merge_scaled(torch, ba, steps, warmup, n_parts=32, rows=131072, D=128):
+    """Merge kernel at a bandwidth-visible size: 32 parts x 131072 rows x D=128 fp32."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(6)
+    parts = []
+    for _ in range(n_parts):
+        m = torch.randn(rows, device="cuda", generator=g) * 5
+        l = torch.rand(rows, device="cuda", generator=g) + 0.5
+        o = torch.randn(rows, D, device="cuda", generator=g)
+        parts.append((m, l, o))
+    out = ba.new_state(rows, D)
+    flush = flush_buffer(torch)
+    for _ in range(warmup):
+        ba.merge_states(parts, out)
+    timer = Timer(torch)
+    for _ in range(steps):
+        flush.fill_(1)
+        e0 = timer.start()
+        ba.merge_states(parts, out)
+        timer.stop(e0)
+    torch.cuda.synchronize()
+    ms = timer.median_ms()
+    nbytes = (n_parts + 1) * rows * (D + 2) * 4
+    gbs = nbytes / ms / 1e6
+    log(f"merge scaled: {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
+    return {"workload": f"{n_parts}-way merge, {rows} rows, D={D}, fp32", "us": round(ms * 1e3, 2),
+            "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes}
+
+
+def cpu_baseline(w, q, k, v, budget_s):
+    """The oracle, as it stands, on a bounded sample of query tokens of the headline workload."""
+    from threadpoolctl import threadpool_info
+
+    from exact_blockwise_long_amd import synth
+    from oracle import attention as ora
+
+    g = np.random.Generator(np.random.PCG64(1234))
+    order = g.permutation(w.q_len)
+    k64 = synth.Tensor(k.storage, k.dtype).f64()
+    v64 = synth.Tensor(v.storage, v.dtype).f64()
+    done, flops = 0, 0.0
+    t0 = time.perf_counter()
+    batch = 8
+    while time.perf_counter() - t0 < budget_s and done < w.q_len:
+        toks = np.sort(order[done:done + batch])
+        q64 = synth.Tensor(q.storage[toks], q.dtype).f64()
+        ora.attend(q64, k64, v64, w.scale, w.q_pos0 + toks, None, w.causal)
+        vis = np.minimum(w.kv_len, np.maximum(0, w.q_pos0 + toks + 1)) if w.causal else np.full(len(toks), w.kv_len)
+        flops += 4.0 * w.head_dim * w.n_q_heads * float(vis.sum())
+        done += len(toks)
+    el = time.perf_counter() - t0
+    threads = max([t.get("num_threads", 1) for t in threadpool_info() if t.get("user_api") == "blas"] or [1])
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {w.q_len} query tokens (all {w.n_q_heads} heads, every visible key) of the "
+                      f"headline workload, fp64 NumPy, {el:.1f} s; host has {os.cpu_count()} logical CPUs"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "causal_prefill", "ring_share", "fanout", "shard_merge", "merge_scaled"])
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build has no "
+              "multi-GPU path: the ring is emulated as the K/V visit order on one device)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(3)
+    from exact_blockwise_long_amd import blockattn as ba
+    from exact_blockwise_long_amd import workloads as wl
+    from tests import helpers as H
+    ba.load()
+    log(f"device: {torch.cuda.get_device_name(0)}; HIP runtime {ba.hip_runtimes_loaded()}")
+
+    secondary = {}
+    only = args.workload
+    if only in ("ring_share",):
+        secondary["ring_share"] = bench_ring_share(torch, ba, H, wl.RING_SHARE, max(1, args.steps // 10), 1)
+    if only == "fanout":
+        secondary["fanout_decode"] = bench_fanout(torch, ba, H, wl.FANOUT_DECODE, args.steps, args.warmup)
+    if only == "shard_merge":
+        secondary["shard_merge"] = bench_shard_merge(torch, ba, H, wl.SHARD_MERGE, args.steps, args.warmup)
+    if only == "merge_scaled":
+        secondary["merge_scaled"] = bench_merge_scaled(torch, ba, args.steps, args.warmup)
+    if only not in ("all", "causal_prefill"):
+        print(json.dumps({"metric": METRIC, "partial": only, "secondary": secondary}), flush=True)
+        return
+
+    w = wl.CAUSAL_PREFILL
+    res = bench_prefill(torch, ba, H, w, args.steps, args.warmup)
+    value = res["flops"] / res["ms_step"] / 1e9
+    achieved = res["flops"] / res["kernel_ms"] / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)*0.5, rounded to bf16)",
+        "config": {"workload": w.name, "q_tokens": w.q_len, "q_pos0": w.q_pos0, "kv_blocks": w.n_blocks,
+                   "block_len": w.block_len, "order": w.order, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "causal": w.causal,
+                   "algorithmic_flops_per_step": w.flops()},
+        "roofline": {"kernel": "walk_kernel<128> (bf16 fwd_block, one launch per step)", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_record("walk_kernel_causal_prefill"),
+                     "kernel_ms_mean": round(res["kernel_ms"], 4)},
+    }
+    if not args.no_secondary and only == "all":
+        secondary["fanout_decode"] = bench_fanout(torch, ba, H, wl.FANOUT_DECODE, args.steps, args.warmup)
+        secondary["shard_merge"] = bench_shard_merge(torch, ba, H, wl.SHARD_MERGE, args.steps, args.warmup)
+        secondary["merge_scaled"] = bench_merge_scaled(torch, ba, args.steps, args.warmup)
+        secondary["ring_share"] = bench_ring_share(torch, ba, H, wl.RING_SHARE, 2, 1)
+    if secondary:
+        line["secondary"] = secondary
+    if not args.no_cpu:
+        log("timing the CPU oracle on a sample")
+        line["cpu_baseline"] = cpu_baseline(w, res["q"], res["k"], res["v"], args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,287 @@
+"""Thin ctypes binding of libblockattn.so (argument marshalling only).
+
+Every step of the computation runs in the library's HIP kernels.  PyTorch is
+used only to own device memory and to name the current stream; this module
+turns tensors into pointers, strides and sizes, allocates the workspace the
+library asks for, and raises ``BlockAttnError`` on a non-zero status.  There
+is no CPU path: if the built library is missing, ``load()`` raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libblockattn.so")
+
+BA_F32, BA_BF16 = 0, 1
+MAX_VISITS = 32
+MAX_MERGE_PARTS = 64
+
+STATUS = {0: "BA_OK", 1: "BA_ERR_NULL", 2: "BA_ERR_SHAPE", 3: "BA_ERR_UNSUPPORTED",
+          4: "BA_ERR_ORDER", 5: "BA_ERR_WORKSPACE", 6: "BA_ERR_HIP"}
+
+
+class BlockAttnError(RuntimeError):
+    def __init__(self, status: int, func: str, msg: str):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        super().__init__(f"{func}: {self.name}: {msg}")
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [
+        ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("q_len", ctypes.c_int32), ("q_pos0", ctypes.c_int64),
+        ("q_stride_token", ctypes.c_int64), ("q_stride_head", ctypes.c_int64),
+        ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("causal", ctypes.c_int32),
+        ("split_mode", ctypes.c_int32),
+    ]
+
+
+class KVBlock(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("len", ctypes.c_int32), ("pos0", ctypes.c_int64),
+        ("k_stride_token", ctypes.c_int64), ("k_stride_head", ctypes.c_int64),
+        ("v_stride_token", ctypes.c_int64), ("v_stride_head", ctypes.c_int64),
+    ]
+
+
+class State(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_void_p), ("l", ctypes.c_void_p), ("o", ctypes.c_void_p)]
+
+
+class Fanout(ctypes.Structure):
+    _fields_ = [
+        ("n_branches", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("prefix_len", ctypes.c_int32), ("suffix_len", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+    ]
+
+
+EXPORTS = [
+    "blockattn_fwd_block", "blockattn_fwd_workspace_bytes", "blockattn_shard_states",
+    "blockattn_shard_workspace_bytes", "blockattn_merge_states", "blockattn_finalize",
+    "fanout_prefix_decode", "fanout_workspace_bytes", "blockattn_status_str",
+    "blockattn_last_error", "blockattn_abi_version",
+]
+
+_lib = None
+
+
+def hip_runtimes_loaded() -> List[str]:
+    """Paths of every libamdhip64 mapped into this process."""
+    paths = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) >= 6 and "libamdhip64" in parts[5]:
+                paths.add(parts[5])
+    return sorted(paths)
+
+
+def load():
+    """Load the library (after torch, so both use torch's HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m exact_blockwise_long_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    vp, sz, i32, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
+    lib.blockattn_fwd_block.argtypes = [P(Problem), vp, P(KVBlock), i32, P(i32), i32, State, i32, vp, sz, vp]
+    lib.blockattn_fwd_block.restype = i32
+    lib.blockattn_fwd_workspace_bytes.argtypes = [P(Problem), P(KVBlock), i32, P(i32), i32]
+    lib.blockattn_fwd_workspace_bytes.restype = sz
+    lib.blockattn_shard_states.argtypes = [P(Problem), vp, P(KVBlock), i32, P(State), vp, sz, vp]
+    lib.blockattn_shard_states.restype = i32
+    lib.blockattn_shard_workspace_bytes.argtypes = [P(Problem), P(KVBlock), i32]
+    lib.blockattn_shard_workspace_bytes.restype = sz
+    lib.blockattn_merge_states.argtypes = [i32, P(State), i64, i32, State, vp]
+    lib.blockattn_merge_states.restype = i32
+    lib.blockattn_finalize.argtypes = [State, i64, i32, vp, i32, i64, vp, vp]
+    lib.blockattn_finalize.restype = i32
+    lib.fanout_prefix_decode.argtypes = [P(Fanout), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.fanout_prefix_decode.restype = i32
+    lib.fanout_workspace_bytes.argtypes = [P(Fanout)]
+    lib.fanout_workspace_bytes.restype = sz
+    lib.blockattn_status_str.argtypes = [i32]
+    lib.blockattn_status_str.restype = ctypes.c_char_p
+    lib.blockattn_last_error.argtypes = []
+    lib.blockattn_last_error.restype = ctypes.c_char_p
+    lib.blockattn_abi_version.argtypes = []
+    lib.blockattn_abi_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(status: int, func: str):
+    if status != 0:
+        raise BlockAttnError(status, func, load().blockattn_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BA_BF16
+    if t.dtype == torch.float32:
+        return BA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dim_contig(t: torch.Tensor, name: str):
+    if t.dim() != 3 or t.stride(2) != 1:
+        raise ValueError(f"{name} must be [tokens, heads, head_dim] with a contiguous head_dim axis")
+
+
+def new_state(rows: int, head_dim: int, device="cuda") -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Uninitialised fp32 state buffers (m [rows], l [rows], o [rows, D])."""
+    return (torch.empty(rows, dtype=torch.float32, device=device),
+            torch.empty(rows, dtype=torch.float32, device=device),
+            torch.empty(rows, head_dim, dtype=torch.float32, device=device))
+
+
+def _state(st) -> State:
+    m, l, o = st
+    return State(m.data_ptr(), l.data_ptr(), o.data_ptr())
+
+
+def make_problem(q: torch.Tensor, n_kv_heads: int, q_pos0: int = 0, causal: bool = False,
+                 scale: float = 0.0, split_mode: int = 0) -> Problem:
+    _dim_contig(q, "q")
+    T, Hq, D = q.shape
+    return Problem(Hq, n_kv_heads, D, T, q_pos0, q.stride(0), q.stride(1), _dtype_code(q), scale,
+                   1 if causal else 0, split_mode)
+
+
+def make_blocks(blocks: Sequence[Tuple[torch.Tensor, torch.Tensor, int]]):
+    arr = (KVBlock * max(1, len(blocks)))()
+    for i, (k, v, pos0) in enumerate(blocks):
+        _dim_contig(k, "k")
+        _dim_contig(v, "v")
+        if k.shape != v.shape:
+            raise ValueError("k and v blocks must have the same shape")
+        arr[i] = KVBlock(k.data_ptr(), v.data_ptr(), k.shape[0], pos0, k.stride(0), k.stride(1),
+                         v.stride(0), v.stride(1))
+    return arr
+
+
+def fwd_block(q: torch.Tensor, blocks: Sequence[Tuple[torch.Tensor, torch.Tensor, int]],
+              order: Optional[Sequence[int]], state, reset: bool, *, n_kv_heads: int, q_pos0: int = 0,
+              causal: bool = False, scale: float = 0.0, split_mode: int = 0,
+              workspace: Optional[torch.Tensor] = None, stream=None):
+    """blockattn_fwd_block: walk ``blocks`` in ``order`` updating ``state`` (m, l, o) in place."""
+    lib = load()
+    p = make_problem(q, n_kv_heads, q_pos0, causal, scale, split_mode)
+    arr = make_blocks(blocks)
+    n_visit = len(order) if order is not None else len(blocks)
+    order_arr = (ctypes.c_int32 * max(1, n_visit))(*(order or []))
+    order_ptr = order_arr if order is not None else None
+    need = lib.blockattn_fwd_workspace_bytes(ctypes.byref(p), arr, len(blocks), order_ptr, n_visit)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.blockattn_fwd_block(ctypes.byref(p), _ptr(q), arr, len(blocks), order_ptr, n_visit,
+                                   _state(state), 1 if reset else 0, _ptr(workspace), ws_bytes,
+                                   _stream(stream)), "blockattn_fwd_block")
+    return state
+
+
+def fwd_workspace_bytes(q, blocks, order, *, n_kv_heads, q_pos0=0, causal=False, split_mode=0) -> int:
+    lib = load()
+    p = make_problem(q, n_kv_heads, q_pos0, causal, 0.0, split_mode)
+    arr = make_blocks(blocks)
+    n_visit = len(order) if order is not None else len(blocks)
+    order_arr = (ctypes.c_int32 * max(1, n_visit))(*(order or []))
+    return lib.blockattn_fwd_workspace_bytes(ctypes.byref(p), arr, len(blocks),
+                                             order_arr if order is not None else None, n_visit)
+
+
+def shard_states(q: torch.Tensor, blocks, states_out, *, n_kv_heads: int, q_pos0: int = 0,
+                 causal: bool = False, scale: float = 0.0, workspace: Optional[torch.Tensor] = None,
+                 stream=None):
+    """blockattn_shard_states: one partial state per block into ``states_out``."""
+    lib = load()
+    p = make_problem(q, n_kv_heads, q_pos0, causal, scale, 0)
+    arr = make_blocks(blocks)
+    sts = (State * len(blocks))(*[_state(s) for s in states_out])
+    need = lib.blockattn_shard_workspace_bytes(ctypes.byref(p), arr, len(blocks))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.blockattn_shard_states(ctypes.byref(p), _ptr(q), arr, len(blocks), sts, _ptr(workspace),
+                                      ws_bytes, _stream(stream)), "blockattn_shard_states")
+    return states_out
+
+
+def merge_states(parts, out, stream=None):
+    """blockattn_merge_states over a list of (m, l, o) states into ``out``."""
+    lib = load()
+    rows, D = out[2].shape
+    arr = (State * len(parts))(*[_state(s) for s in parts])
+    _check(lib.blockattn_merge_states(len(parts), arr, rows, D, _state(out), _stream(stream)),
+           "blockattn_merge_states")
+    return out
+
+
+def finalize(state, out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None, want_lse: bool = True,
+             lse: Optional[torch.Tensor] = None, stream=None):
+    """blockattn_finalize: returns (A [rows, D], lse [rows] or None)."""
+    lib = load()
+    m, l, o = state
+    rows, D = o.shape
+    if out is None:
+        out = torch.empty(rows, D, dtype=out_dtype, device=o.device)
+    if lse is None and want_lse:
+        lse = torch.empty(rows, dtype=torch.float32, device=o.device)
+    code = BA_BF16 if out.dtype == torch.bfloat16 else BA_F32
+    _check(lib.blockattn_finalize(_state(state), rows, D, _ptr(out), code, out.stride(0), _ptr(lse),
+                                  _stream(stream)), "blockattn_finalize")
+    return out, lse
+
+
+def fanout_prefix_decode(q, prefix_k, prefix_v, suffix_k, suffix_v, scale: float = 0.0,
+                         workspace: Optional[torch.Tensor] = None, want_lse: bool = True,
+                         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, stream=None):
+    """fanout_prefix_decode: q [nb, Hq, D]; prefix [P, Hkv, D]; suffix [nb, S, Hkv, D] (all contiguous bf16)."""
+    lib = load()
+    nb, Hq, D = q.shape
+    Hkv = prefix_k.shape[1] if prefix_k is not None else suffix_k.shape[2]
+    P = prefix_k.shape[0] if prefix_k is not None else 0
+    S = suffix_k.shape[1] if suffix_k is not None else 0
+    for name, t in (("q", q), ("prefix_k", prefix_k), ("prefix_v", prefix_v), ("suffix_k", suffix_k),
+                    ("suffix_v", suffix_v)):
+        if t is not None and (not t.is_contiguous() or t.dtype != torch.bfloat16):
+            raise ValueError(f"{name} must be contiguous bf16")
+    f = Fanout(nb, Hq, Hkv, D, P, S, scale)
+    need = lib.fanout_workspace_bytes(ctypes.byref(f))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if out is None:
+        out = torch.empty(nb, Hq, D, dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty(nb, Hq, dtype=torch.float32, device=q.device)
+    _check(lib.fanout_prefix_decode(ctypes.byref(f), _ptr(q), _ptr(prefix_k), _ptr(prefix_v), _ptr(suffix_k),
+                                    _ptr(suffix_v), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+                                    _stream(stream)), "fanout_prefix_decode")
+    return out, lse
+
+
+def fanout_workspace_bytes(n_branches, n_q_heads, n_kv_heads, head_dim, prefix_len, suffix_len) -> int:
+    f = Fanout(n_branches, n_q_heads, n_kv_heads, head_dim, prefix_len, suffix_len, 0.0)
+    return load().fanout_workspace_bytes(ctypes.byref(f))

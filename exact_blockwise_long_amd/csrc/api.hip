@@ -1,0 +1,605 @@
+// C-ABI front end of libblockattn.so: argument checks, work splitting and
+// kernel dispatch.  Every check runs before anything is enqueued; the library
+// allocates nothing and never synchronises.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <vector>
+
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ba_status fail(ba_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+ba_status ok() {
+  g_err[0] = '\0';
+  return BA_OK;
+}
+
+ba_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(BA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Workgroups a split launch aims for: 4 per compute unit of a 256-CU part.
+constexpr int kTargetWorkgroups = 1024;
+// Below this many (row tile x KV head) workgroups the keys are split.
+constexpr int kWalkMinWorkgroups = 512;
+constexpr int kMaxChunks = 8192;
+
+float resolve_scale(float s, int D) { return s > 0.f ? s : 1.0f / sqrtf((float)D); }
+
+ba_status check_problem(const ba_problem* p, const void* q) {
+  if (!p) return fail(BA_ERR_NULL, "problem is NULL");
+  if (p->dtype != BA_F32 && p->dtype != BA_BF16) return fail(BA_ERR_UNSUPPORTED, "dtype %d", p->dtype);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(BA_ERR_SHAPE, "head_dim %d (64 or 128 supported)", p->head_dim);
+  if (p->n_q_heads <= 0 || p->n_kv_heads <= 0 || p->n_q_heads % p->n_kv_heads != 0)
+    return fail(BA_ERR_SHAPE, "n_q_heads %d must be a positive multiple of n_kv_heads %d", p->n_q_heads,
+                p->n_kv_heads);
+  if (p->q_len < 0) return fail(BA_ERR_SHAPE, "q_len %d < 0", p->q_len);
+  if ((int64_t)p->q_len * p->n_q_heads > (int64_t)1 << 30) return fail(BA_ERR_SHAPE, "too many query rows");
+  if (p->q_len > 0) {
+    if (!q) return fail(BA_ERR_NULL, "q is NULL");
+    if (p->q_stride_token <= 0 || p->q_stride_head <= 0) return fail(BA_ERR_SHAPE, "q strides must be positive");
+    if (p->dtype == BA_BF16) {
+      if (((uintptr_t)q % 16) != 0) return fail(BA_ERR_SHAPE, "q not 16-byte aligned");
+      if (p->q_stride_token % 8 != 0 || p->q_stride_head % 8 != 0)
+        return fail(BA_ERR_SHAPE, "bf16 q strides must be multiples of 8 elements");
+    }
+  }
+  if (p->split_mode < 0 || p->split_mode > 2) return fail(BA_ERR_SHAPE, "split_mode %d", p->split_mode);
+  return BA_OK;
+}
+
+ba_status check_block(const ba_kv_block& b, int i, int dtype) {
+  if (b.len < 0) return fail(BA_ERR_SHAPE, "block %d: len %d < 0", i, b.len);
+  if (b.len == 0) return BA_OK;
+  if (!b.k || !b.v) return fail(BA_ERR_NULL, "block %d: k or v is NULL", i);
+  if (b.k_stride_token <= 0 || b.k_stride_head <= 0 || b.v_stride_token <= 0 || b.v_stride_head <= 0)
+    return fail(BA_ERR_SHAPE, "block %d: strides must be positive", i);
+  if (dtype == BA_BF16) {
+    if (((uintptr_t)b.k % 16) != 0 || ((uintptr_t)b.v % 16) != 0)
+      return fail(BA_ERR_SHAPE, "block %d: k/v not 16-byte aligned", i);
+    if (b.k_stride_token % 8 || b.k_stride_head % 8 || b.v_stride_token % 8 || b.v_stride_head % 8)
+      return fail(BA_ERR_SHAPE, "block %d: bf16 strides must be multiples of 8 elements", i);
+  }
+  return BA_OK;
+}
+
+ba_status check_state(const ba_state& s, const char* what) {
+  if (!s.m || !s.l || !s.o) return fail(BA_ERR_NULL, "%s: m, l or o is NULL", what);
+  if (((uintptr_t)s.o % 16) != 0) return fail(BA_ERR_SHAPE, "%s: o not 16-byte aligned", what);
+  return BA_OK;
+}
+
+// Resolved visit list.
+struct Visits {
+  std::vector<int> idx;
+};
+
+ba_status resolve_order(int n_blocks, const int32_t* order, int n_visit, Visits& v) {
+  if (n_visit < 0) return fail(BA_ERR_ORDER, "n_visit %d < 0", n_visit);
+  if (n_visit > BLOCKATTN_MAX_VISITS)
+    return fail(BA_ERR_ORDER, "n_visit %d > %d per call", n_visit, BLOCKATTN_MAX_VISITS);
+  if (n_visit > n_blocks) return fail(BA_ERR_ORDER, "n_visit %d > n_blocks %d", n_visit, n_blocks);
+  std::vector<char> seen(n_blocks > 0 ? n_blocks : 1, 0);
+  v.idx.clear();
+  for (int t = 0; t < n_visit; ++t) {
+    int j = order ? order[t] : t;
+    if (j < 0 || j >= n_blocks) return fail(BA_ERR_ORDER, "order[%d] = %d out of range [0, %d)", t, j, n_blocks);
+    if (seen[j]) return fail(BA_ERR_ORDER, "order[%d] = %d repeats a block", t, j);
+    seen[j] = 1;
+    v.idx.push_back(j);
+  }
+  return BA_OK;
+}
+
+ba::QSide make_qside(const ba_problem* p, const void* q) {
+  ba::QSide qs;
+  qs.q = q;
+  qs.qs_t = p->q_stride_token;
+  qs.qs_h = p->q_stride_head;
+  qs.q_pos0 = p->q_pos0;
+  qs.Hq = p->n_q_heads;
+  qs.Hkv = p->n_kv_heads;
+  qs.G = p->n_q_heads / p->n_kv_heads;
+  qs.q_len = p->q_len;
+  qs.c = resolve_scale(p->scale, p->head_dim) * ba::kLog2e;
+  qs.causal = p->causal ? 1 : 0;
+  return qs;
+}
+
+ba::Seg make_seg(const ba_kv_block& b) {
+  ba::Seg s;
+  s.k = b.k;
+  s.v = b.v;
+  s.ks_t = b.k_stride_token;
+  s.ks_h = b.k_stride_head;
+  s.vs_t = b.v_stride_token;
+  s.vs_h = b.v_stride_head;
+  s.pos0 = b.pos0;
+  s.n = b.len;
+  s.pad_ = 0;
+  return s;
+}
+
+// Keys of a block some query of the whole block can see.
+int64_t usable_keys(const ba_problem* p, const ba_kv_block& b) {
+  if (!p->causal || p->q_len == 0) return b.len;
+  int64_t qmax = p->q_pos0 + p->q_len - 1;
+  int64_t lim = qmax - b.pos0 + 1;
+  if (lim <= 0) return 0;
+  return lim < b.len ? lim : b.len;
+}
+
+int row_tiles(const ba_problem* p) {
+  int64_t flat = (int64_t)p->q_len * (p->n_q_heads / p->n_kv_heads);
+  return (int)((flat + ba::kTileRows - 1) / ba::kTileRows) * p->n_kv_heads;
+}
+
+// Split plan: chunk length and per-visit chunk offsets.
+struct SplitPlan {
+  int chunk_len = 0;
+  int n_chunks = 0;
+  std::vector<int> begin;  // size n_seg + 1
+};
+
+SplitPlan plan_split(const std::vector<int64_t>& keys, int tiles) {
+  SplitPlan sp;
+  int64_t total = 0;
+  for (int64_t k : keys) total += k;
+  int64_t want = (kTargetWorkgroups + tiles - 1) / (tiles > 0 ? tiles : 1);
+  if (want < 1) want = 1;
+  int64_t cl = (total + want - 1) / want;
+  cl = (cl + 63) / 64 * 64;
+  if (cl < 256) cl = 256;
+  for (;;) {
+    int64_t n = 0;
+    for (int64_t k : keys) n += (k + cl - 1) / cl;
+    if (n <= kMaxChunks) break;
+    cl *= 2;
+  }
+  sp.chunk_len = (int)cl;
+  sp.begin.push_back(0);
+  for (int64_t k : keys) {
+    sp.n_chunks += (int)((k + cl - 1) / cl);
+    sp.begin.push_back(sp.n_chunks);
+  }
+  return sp;
+}
+
+size_t partial_bytes(int64_t slots, int64_t R, int D) {
+  size_t ml = align_up((size_t)slots * R * sizeof(float));
+  return 2 * ml + align_up((size_t)slots * R * D * sizeof(float));
+}
+
+void partial_ptrs(void* ws, int64_t slots, int64_t R, float** m, float** l, float** o) {
+  size_t ml = align_up((size_t)slots * R * sizeof(float));
+  char* b = (char*)ws;
+  *m = (float*)b;
+  *l = (float*)(b + ml);
+  *o = (float*)(b + 2 * ml);
+}
+
+bool fwd_uses_split(const ba_problem* p) {
+  if (p->dtype != BA_BF16) return false;
+  if (p->split_mode == 1) return false;
+  if (p->split_mode == 2) return true;
+  return row_tiles(p) < kWalkMinWorkgroups;
+}
+
+// Full validation of a forward call; fills the visit list and split plan.
+ba_status prepare_fwd(const ba_problem* p, const void* q, const ba_kv_block* blocks, int n_blocks,
+                      const int32_t* order, int n_visit, Visits& v, SplitPlan& sp, bool& split) {
+  ba_status st = check_problem(p, q);
+  if (st) return st;
+  if (n_blocks < 0) return fail(BA_ERR_SHAPE, "n_blocks %d < 0", n_blocks);
+  if (n_visit > 0 && !blocks) return fail(BA_ERR_NULL, "blocks is NULL");
+  st = resolve_order(n_blocks, order, n_visit, v);
+  if (st) return st;
+  for (int j : v.idx) {
+    st = check_block(blocks[j], j, p->dtype);
+    if (st) return st;
+  }
+  split = fwd_uses_split(p);
+  if (split) {
+    std::vector<int64_t> keys;
+    for (int j : v.idx) keys.push_back(usable_keys(p, blocks[j]));
+    sp = plan_split(keys, row_tiles(p));
+  }
+  return BA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* blockattn_status_str(int32_t s) {
+  switch (s) {
+    case BA_OK: return "ok";
+    case BA_ERR_NULL: return "a required pointer is NULL";
+    case BA_ERR_SHAPE: return "inconsistent or out-of-range sizes or strides";
+    case BA_ERR_UNSUPPORTED: return "unsupported request";
+    case BA_ERR_ORDER: return "invalid visit order";
+    case BA_ERR_WORKSPACE: return "workspace missing or too small";
+    case BA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* blockattn_last_error(void) { return g_err; }
+
+int32_t blockattn_abi_version(void) { return BLOCKATTN_ABI_VERSION; }
+
+size_t blockattn_fwd_workspace_bytes(const ba_problem* p, const ba_kv_block* blocks, int32_t n_blocks,
+                                     const int32_t* order, int32_t n_visit) {
+  Visits v;
+  SplitPlan sp;
+  bool split = false;
+  if (prepare_fwd(p, p ? (const void*)256 : nullptr, blocks, n_blocks, order, n_visit, v, sp, split) != BA_OK)
+    return 0;
+  if (!split || p->q_len == 0) return 0;
+  return partial_bytes(sp.n_chunks, (int64_t)p->q_len * p->n_q_heads, p->head_dim);
+}
+
+ba_status blockattn_fwd_block(const ba_problem* p, const void* q, const ba_kv_block* blocks, int32_t n_blocks,
+                              const int32_t* order, int32_t n_visit, ba_state state, int32_t reset_state,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Visits v;
+  SplitPlan sp;
+  bool split = false;
+  ba_status st = prepare_fwd(p, q, blocks, n_blocks, order, n_visit, v, sp, split);
+  if (st) return st;
+  if (p->q_len == 0) return ok();
+  st = check_state(state, "state");
+  if (st) return st;
+  const int D = p->head_dim;
+  const int64_t R = (int64_t)p->q_len * p->n_q_heads;
+
+  if (!split) {
+    ba::WalkArgs a;
+    memset(&a, 0, sizeof(a));
+    a.qs = make_qside(p, q);
+    a.m = state.m;
+    a.l = state.l;
+    a.o = state.o;
+    a.reset = reset_state ? 1 : 0;
+    a.n_seg = 0;
+    for (int j : v.idx) {
+      // blocks no query of the block can see (causal future, or empty) are skipped
+      if (usable_keys(p, blocks[j]) == 0) continue;
+      a.seg[a.n_seg++] = make_seg(blocks[j]);
+    }
+    if (!a.reset && a.n_seg == 0) return ok();
+    hipError_t e = (p->dtype == BA_BF16) ? ba::launch_walk_bf16(a, D, stream) : ba::launch_walk_f32(a, D, stream);
+    return hip_status(e, "fwd_block walk launch");
+  }
+
+  const size_t need = partial_bytes(sp.n_chunks, R, D);
+  if (sp.n_chunks > 0 && (!workspace || workspace_bytes < need))
+    return fail(BA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+  if (sp.n_chunks > 0 && ((uintptr_t)workspace % 16) != 0) return fail(BA_ERR_WORKSPACE, "workspace not 16-byte aligned");
+  float *wm = nullptr, *wl = nullptr, *wo = nullptr;
+  if (sp.n_chunks > 0) {
+    partial_ptrs(workspace, sp.n_chunks, R, &wm, &wl, &wo);
+    ba::SplitArgs a;
+    memset(&a, 0, sizeof(a));
+    a.qs = make_qside(p, q);
+    a.ws_m = wm;
+    a.ws_l = wl;
+    a.ws_o = wo;
+    a.R = R;
+    a.chunk_len = sp.chunk_len;
+    a.n_seg = (int)v.idx.size();
+    for (int i = 0; i < a.n_seg; ++i) {
+      a.seg[i] = make_seg(blocks[v.idx[i]]);
+      a.chunk_begin[i] = sp.begin[i];
+    }
+    a.chunk_begin[a.n_seg] = sp.begin[a.n_seg];
+    hipError_t e = ba::launch_split_bf16(a, sp.n_chunks, D, stream);
+    if (e != hipSuccess) return hip_status(e, "fwd_block split launch");
+  }
+  if (!reset_state && sp.n_chunks == 0) return ok();
+  ba::MergeGroupArgs mg;
+  memset(&mg, 0, sizeof(mg));
+  mg.pm = wm;
+  mg.pl = wl;
+  mg.po = wo;
+  mg.R = R;
+  mg.n_groups = 1;
+  mg.has_init = reset_state ? 0 : 1;
+  mg.part_begin[0] = 0;
+  mg.part_begin[1] = sp.n_chunks;
+  mg.out_m[0] = state.m;
+  mg.out_l[0] = state.l;
+  mg.out_o[0] = state.o;
+  return hip_status(ba::launch_merge_groups(mg, D, stream), "fwd_block merge launch");
+}
+
+size_t blockattn_shard_workspace_bytes(const ba_problem* p, const ba_kv_block* blocks, int32_t n_blocks) {
+  if (check_problem(p, (const void*)256) != BA_OK || !blocks || n_blocks <= 0 || n_blocks > BLOCKATTN_MAX_VISITS)
+    return 0;
+  if (p->dtype != BA_BF16 || p->q_len == 0) return 0;
+  std::vector<int64_t> keys;
+  for (int i = 0; i < n_blocks; ++i) {
+    if (check_block(blocks[i], i, p->dtype) != BA_OK) return 0;
+    keys.push_back(usable_keys(p, blocks[i]));
+  }
+  SplitPlan sp = plan_split(keys, row_tiles(p));
+  return partial_bytes(sp.n_chunks, (int64_t)p->q_len * p->n_q_heads, p->head_dim);
+}
+
+ba_status blockattn_shard_states(const ba_problem* p, const void* q, const ba_kv_block* blocks, int32_t n_blocks,
+                                 const ba_state* states_out, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  ba_status st = check_problem(p, q);
+  if (st) return st;
+  if (p->dtype != BA_BF16) return fail(BA_ERR_UNSUPPORTED, "shard_states supports bf16 only");
+  if (n_blocks <= 0 || n_blocks > BLOCKATTN_MAX_VISITS)
+    return fail(BA_ERR_ORDER, "n_blocks %d outside [1, %d]", n_blocks, BLOCKATTN_MAX_VISITS);
+  if (!blocks || !states_out) return fail(BA_ERR_NULL, "blocks or states_out is NULL");
+  std::vector<int64_t> keys;
+  for (int i = 0; i < n_blocks; ++i) {
+    st = check_block(blocks[i], i, p->dtype);
+    if (st) return st;
+    st = check_state(states_out[i], "states_out");
+    if (st) return st;
+    keys.push_back(usable_keys(p, blocks[i]));
+  }
+  if (p->q_len == 0) return ok();
+  const int D = p->head_dim;
+  const int64_t R = (int64_t)p->q_len * p->n_q_heads;
+  SplitPlan sp = plan_split(keys, row_tiles(p));
+  const size_t need = partial_bytes(sp.n_chunks, R, D);
+  float *wm = nullptr, *wl = nullptr, *wo = nullptr;
+  if (sp.n_chunks > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(BA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+    if (((uintptr_t)workspace % 16) != 0) return fail(BA_ERR_WORKSPACE, "workspace not 16-byte aligned");
+    partial_ptrs(workspace, sp.n_chunks, R, &wm, &wl, &wo);
+    ba::SplitArgs a;
+    memset(&a, 0, sizeof(a));
+    a.qs = make_qside(p, q);
+    a.ws_m = wm;
+    a.ws_l = wl;
+    a.ws_o = wo;
+    a.R = R;
+    a.chunk_len = sp.chunk_len;
+    a.n_seg = n_blocks;
+    for (int i = 0; i < n_blocks; ++i) {
+      a.seg[i] = make_seg(blocks[i]);
+      a.chunk_begin[i] = sp.begin[i];
+    }
+    a.chunk_begin[n_blocks] = sp.begin[n_blocks];
+    hipError_t e = ba::launch_split_bf16(a, sp.n_chunks, D, stream);
+    if (e != hipSuccess) return hip_status(e, "shard_states split launch");
+  }
+  ba::MergeGroupArgs mg;
+  memset(&mg, 0, sizeof(mg));
+  mg.pm = wm;
+  mg.pl = wl;
+  mg.po = wo;
+  mg.R = R;
+  mg.n_groups = n_blocks;
+  mg.has_init = 0;
+  for (int i = 0; i <= n_blocks; ++i) mg.part_begin[i] = sp.begin[i];
+  for (int i = 0; i < n_blocks; ++i) {
+    mg.out_m[i] = states_out[i].m;
+    mg.out_l[i] = states_out[i].l;
+    mg.out_o[i] = states_out[i].o;
+  }
+  return hip_status(ba::launch_merge_groups(mg, D, stream), "shard_states merge launch");
+}
+
+ba_status blockattn_merge_states(int32_t n_parts, const ba_state* parts, int64_t rows, int32_t head_dim,
+                                 ba_state out, hipStream_t stream) {
+  if (n_parts < 1 || n_parts > BLOCKATTN_MAX_MERGE_PARTS)
+    return fail(BA_ERR_SHAPE, "n_parts %d outside [1, %d]", n_parts, BLOCKATTN_MAX_MERGE_PARTS);
+  if (!parts) return fail(BA_ERR_NULL, "parts is NULL");
+  if (head_dim != 64 && head_dim != 128) return fail(BA_ERR_SHAPE, "head_dim %d", head_dim);
+  if (rows < 0) return fail(BA_ERR_SHAPE, "rows %lld < 0", (long long)rows);
+  ba_status st = check_state(out, "out");
+  if (st) return st;
+  ba::MergePtrArgs a;
+  memset(&a, 0, sizeof(a));
+  a.n_parts = n_parts;
+  a.R = rows;
+  for (int i = 0; i < n_parts; ++i) {
+    st = check_state(parts[i], "parts");
+    if (st) return st;
+    if (((uintptr_t)parts[i].o % 16) != 0) return fail(BA_ERR_SHAPE, "parts[%d].o not 16-byte aligned", i);
+    a.m[i] = parts[i].m;
+    a.l[i] = parts[i].l;
+    a.o[i] = parts[i].o;
+  }
+  if (((uintptr_t)out.o % 16) != 0) return fail(BA_ERR_SHAPE, "out.o not 16-byte aligned");
+  if (rows == 0) return ok();
+  a.out_m = out.m;
+  a.out_l = out.l;
+  a.out_o = out.o;
+  return hip_status(ba::launch_merge_ptrs(a, head_dim, stream), "merge_states launch");
+}
+
+ba_status blockattn_finalize(ba_state s, int64_t rows, int32_t head_dim, void* out, int32_t out_dtype,
+                             int64_t out_row_stride, float* lse, hipStream_t stream) {
+  ba_status st = check_state(s, "state");
+  if (st) return st;
+  if (!out) return fail(BA_ERR_NULL, "out is NULL");
+  if (head_dim != 64 && head_dim != 128) return fail(BA_ERR_SHAPE, "head_dim %d", head_dim);
+  if (rows < 0) return fail(BA_ERR_SHAPE, "rows < 0");
+  if (out_dtype != BA_F32 && out_dtype != BA_BF16) return fail(BA_ERR_UNSUPPORTED, "out_dtype %d", out_dtype);
+  if (out_row_stride < head_dim) return fail(BA_ERR_SHAPE, "out_row_stride %lld < head_dim", (long long)out_row_stride);
+  if (out_row_stride % 4 != 0) return fail(BA_ERR_SHAPE, "out_row_stride must be a multiple of 4");
+  if (((uintptr_t)s.o % 16) != 0) return fail(BA_ERR_SHAPE, "state o not 16-byte aligned");
+  if (((uintptr_t)out % (out_dtype == BA_BF16 ? 8 : 16)) != 0) return fail(BA_ERR_SHAPE, "out misaligned");
+  if (rows == 0) return ok();
+  ba::FinalizeArgs a;
+  a.m = s.m;
+  a.l = s.l;
+  a.o = s.o;
+  a.R = rows;
+  a.out = out;
+  a.out_bf16 = out_dtype == BA_BF16;
+  a.out_stride = out_row_stride;
+  a.lse = lse;
+  return hip_status(ba::launch_finalize(a, head_dim, stream), "finalize launch");
+}
+
+}  // extern "C"
+
+namespace {
+
+ba_status check_fanout(const ba_fanout* f) {
+  if (!f) return fail(BA_ERR_NULL, "fanout descriptor is NULL");
+  if (f->head_dim != 64 && f->head_dim != 128) return fail(BA_ERR_SHAPE, "head_dim %d", f->head_dim);
+  if (f->n_q_heads <= 0 || f->n_kv_heads <= 0 || f->n_q_heads % f->n_kv_heads != 0)
+    return fail(BA_ERR_SHAPE, "bad head counts %d / %d", f->n_q_heads, f->n_kv_heads);
+  if (f->n_branches < 0 || f->prefix_len < 0 || f->suffix_len < 0) return fail(BA_ERR_SHAPE, "negative size");
+  if (f->n_branches > 0 && f->prefix_len + f->suffix_len == 0) return fail(BA_ERR_SHAPE, "no keys to attend to");
+  return BA_OK;
+}
+
+struct FanoutPlan {
+  SplitPlan prefix;
+  int slots = 0;
+  int suffix_slot = -1;
+};
+
+FanoutPlan plan_fanout(const ba_fanout* f) {
+  FanoutPlan fp;
+  ba_problem p;
+  memset(&p, 0, sizeof(p));
+  p.n_q_heads = f->n_q_heads;
+  p.n_kv_heads = f->n_kv_heads;
+  p.q_len = f->n_branches;
+  std::vector<int64_t> keys;
+  if (f->prefix_len > 0) keys.push_back(f->prefix_len);
+  // Aim for about two workgroups per compute unit over the prefix: enough to
+  // hide HBM latency while keeping the partial states small.
+  if (!keys.empty()) {
+    int tiles = row_tiles(&p);
+    int64_t want = (512 + tiles - 1) / tiles;
+    int64_t cl = (f->prefix_len + want - 1) / want;
+    cl = (cl + 63) / 64 * 64;
+    if (cl < 256) cl = 256;
+    fp.prefix.chunk_len = (int)cl;
+    fp.prefix.n_chunks = (int)((f->prefix_len + cl - 1) / cl);
+    fp.prefix.begin = {0, fp.prefix.n_chunks};
+  }
+  fp.slots = fp.prefix.n_chunks;
+  if (f->suffix_len > 0) fp.suffix_slot = fp.slots++;
+  return fp;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fanout_workspace_bytes(const ba_fanout* f) {
+  if (check_fanout(f) != BA_OK || f->n_branches == 0) return 0;
+  FanoutPlan fp = plan_fanout(f);
+  return partial_bytes(fp.slots, (int64_t)f->n_branches * f->n_q_heads, f->head_dim);
+}
+
+ba_status fanout_prefix_decode(const ba_fanout* f, const void* q, const void* prefix_k, const void* prefix_v,
+                               const void* suffix_k, const void* suffix_v, void* out, float* lse, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  ba_status st = check_fanout(f);
+  if (st) return st;
+  if (f->n_branches == 0) return ok();
+  if (!q || !out) return fail(BA_ERR_NULL, "q or out is NULL");
+  if (f->prefix_len > 0 && (!prefix_k || !prefix_v)) return fail(BA_ERR_NULL, "prefix k/v is NULL");
+  if (f->suffix_len > 0 && (!suffix_k || !suffix_v)) return fail(BA_ERR_NULL, "suffix k/v is NULL");
+  const int D = f->head_dim;
+  const int64_t R = (int64_t)f->n_branches * f->n_q_heads;
+  FanoutPlan fp = plan_fanout(f);
+  const size_t need = partial_bytes(fp.slots, R, D);
+  if (!workspace || workspace_bytes < need)
+    return fail(BA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+  if (((uintptr_t)workspace % 16) != 0) return fail(BA_ERR_WORKSPACE, "workspace not 16-byte aligned");
+  float *wm, *wl, *wo;
+  partial_ptrs(workspace, fp.slots, R, &wm, &wl, &wo);
+
+  ba_problem p;
+  memset(&p, 0, sizeof(p));
+  p.n_q_heads = f->n_q_heads;
+  p.n_kv_heads = f->n_kv_heads;
+  p.head_dim = D;
+  p.q_len = f->n_branches;
+  p.q_pos0 = 0;
+  p.q_stride_token = (int64_t)f->n_q_heads * D;
+  p.q_stride_head = D;
+  p.dtype = BA_BF16;
+  p.scale = f->scale;
+  p.causal = 0;
+  const ba::QSide qs = make_qside(&p, q);
+
+  if (fp.prefix.n_chunks > 0) {
+    ba::SplitArgs a;
+    memset(&a, 0, sizeof(a));
+    a.qs = qs;
+    a.ws_m = wm;
+    a.ws_l = wl;
+    a.ws_o = wo;
+    a.R = R;
+    a.chunk_len = fp.prefix.chunk_len;
+    a.n_seg = 1;
+    ba_kv_block b;
+    b.k = prefix_k;
+    b.v = prefix_v;
+    b.len = f->prefix_len;
+    b.pos0 = 0;
+    b.k_stride_token = b.v_stride_token = (int64_t)f->n_kv_heads * D;
+    b.k_stride_head = b.v_stride_head = D;
+    a.seg[0] = make_seg(b);
+    a.chunk_begin[0] = 0;
+    a.chunk_begin[1] = fp.prefix.n_chunks;
+    hipError_t e = ba::launch_split_bf16(a, fp.prefix.n_chunks, D, stream);
+    if (e != hipSuccess) return hip_status(e, "fanout prefix launch");
+  }
+  if (fp.suffix_slot >= 0) {
+    ba::SuffixArgs a;
+    memset(&a, 0, sizeof(a));
+    a.qs = qs;
+    a.sk = suffix_k;
+    a.sv = suffix_v;
+    a.S = f->suffix_len;
+    a.slot = fp.suffix_slot;
+    a.ws_m = wm;
+    a.ws_l = wl;
+    a.ws_o = wo;
+    a.R = R;
+    hipError_t e = ba::launch_suffix_bf16(a, f->n_branches, D, stream);
+    if (e != hipSuccess) return hip_status(e, "fanout suffix launch");
+  }
+  ba::MergeGroupArgs mg;
+  memset(&mg, 0, sizeof(mg));
+  mg.pm = wm;
+  mg.pl = wl;
+  mg.po = wo;
+  mg.R = R;
+  mg.n_groups = 1;
+  mg.has_init = 0;
+  mg.part_begin[0] = 0;
+  mg.part_begin[1] = fp.slots;
+  mg.fin_out = (uint16_t*)out;
+  mg.fin_lse = lse;
+  return hip_status(ba::launch_merge_groups(mg, D, stream), "fanout merge launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,121 @@
+// fp32 blockwise attention with running online-softmax state (the fp32 path).
+//
+// Same recurrence as the bf16 kernels -- "RingAttention and Context
+// Parallelism" (llms.blog), section 2 state-transition box, from the section 3
+// initial state, causal rule of section 5 -- with every product, sum and
+// exponential in fp32 on the vector ALUs.  One lane owns one query row and
+// keeps q, O, m, l in registers; 32-key K/V tiles are staged in LDS and read
+// by broadcast.  Meant for exactness checks at small sizes, not for speed.
+#include "internal.h"
+
+namespace ba {
+namespace {
+
+constexpr int kRows = 64;   // one wave, one row per lane
+constexpr int kKeys = 32;   // keys per LDS tile
+
+template <int D>
+__global__ __launch_bounds__(kRows) void walk_f32_kernel(WalkArgs a) {
+  __shared__ float ks[kKeys][D];
+  __shared__ float vs[kKeys][D];
+  const QSide& qs = a.qs;
+  const int g = blockIdx.x % qs.Hkv;
+  const int tile = blockIdx.x / qs.Hkv;
+  const int total = qs.q_len * qs.G;
+  const int f0 = tile * kRows;
+  const int f1 = min(f0 + kRows, total);
+  const int lane = threadIdx.x;
+  const int f = f0 + lane;
+  const bool valid = f < f1;
+  const int fc = min(f, f1 - 1);
+  const int t = fc / qs.G;
+  const int h = g * qs.G + (fc - t * qs.G);
+  const int64_t qpos = qs.q_pos0 + t;
+  const int64_t qpos_max = qs.q_pos0 + (f1 - 1) / qs.G;
+  const int64_t srow = (int64_t)t * qs.Hq + h;
+
+  float q[D], o[D];
+  const float* qp = (const float*)qs.q + (int64_t)t * qs.qs_t + (int64_t)h * qs.qs_h;
+#pragma unroll
+  for (int d = 0; d < D; ++d) q[d] = qp[d];
+  float m2, l;
+  if (a.reset) {
+    m2 = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int d = 0; d < D; ++d) o[d] = 0.f;
+  } else {
+    float mm = a.m[srow];
+    m2 = (mm == -INFINITY) ? -INFINITY : mm * kLog2e;
+    l = a.l[srow];
+#pragma unroll
+    for (int d = 0; d < D; ++d) o[d] = a.o[srow * D + d];
+  }
+
+  for (int si = 0; si < a.n_seg; ++si) {
+    const Seg& s = a.seg[si];
+    int n = s.n;
+    if (qs.causal) {
+      int64_t lim = qpos_max - s.pos0 + 1;
+      n = (int)max((int64_t)0, min((int64_t)n, lim));
+    }
+    const float* kb = (const float*)s.k + (int64_t)g * s.ks_h;
+    const float* vb = (const float*)s.v + (int64_t)g * s.vs_h;
+    for (int k0 = 0; k0 < n; k0 += kKeys) {
+      const int nv = min(kKeys, n - k0);
+      __syncthreads();
+      for (int e = lane; e < kKeys * D; e += kRows) {
+        int j = e / D, d = e % D;
+        int jj = min(j, nv - 1);
+        ks[j][d] = kb[(int64_t)(k0 + jj) * s.ks_t + d];
+        vs[j][d] = vb[(int64_t)(k0 + jj) * s.vs_t + d];
+      }
+      __syncthreads();
+      float sc[kKeys];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < kKeys; ++j) {
+        float acc = 0.f;
+#pragma unroll
+        for (int d = 0; d < D; ++d) acc = __builtin_fmaf(q[d], ks[j][d], acc);
+        bool vis = j < nv && (!qs.causal || s.pos0 + k0 + j <= qpos);
+        sc[j] = vis ? acc * qs.c : -INFINITY;
+        mx = fmaxf(mx, sc[j]);
+      }
+      const float m_new = fmaxf(m2, mx);
+      const float base = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m2 - base);
+      m2 = m_new;
+      float sum = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) o[d] *= alpha;
+#pragma unroll
+      for (int j = 0; j < kKeys; ++j) {
+        float p = __builtin_amdgcn_exp2f(sc[j] - base);
+        sum += p;
+#pragma unroll
+        for (int d = 0; d < D; ++d) o[d] = __builtin_fmaf(p, vs[j][d], o[d]);
+      }
+      l = l * alpha + sum;
+    }
+  }
+  if (!valid) return;
+  a.m[srow] = (m2 == -INFINITY) ? -INFINITY : m2 * kLn2;
+  a.l[srow] = l;
+#pragma unroll
+  for (int d = 0; d < D; ++d) a.o[srow * D + d] = o[d];
+}
+
+}  // namespace
+
+hipError_t launch_walk_f32(const WalkArgs& a, int D, hipStream_t s) {
+  const int tiles = (a.qs.q_len * a.qs.G + kRows - 1) / kRows;
+  dim3 grid(tiles * a.qs.Hkv);
+  if (D == 128)
+    hipLaunchKernelGGL(walk_f32_kernel<128>, grid, dim3(kRows), 0, s, a);
+  else
+    hipLaunchKernelGGL(walk_f32_kernel<64>, grid, dim3(kRows), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace ba

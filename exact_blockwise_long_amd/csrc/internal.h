@@ -1,0 +1,135 @@
+// Internal interface between the C-ABI front end (api.hip) and the kernel
+// translation units.  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/blockattn.h"
+
+namespace ba {
+
+constexpr int kMaxSeg = BLOCKATTN_MAX_VISITS;
+constexpr int kMaxParts = BLOCKATTN_MAX_MERGE_PARTS;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// One contiguous key range: keys [0, n) of this segment sit at absolute
+// positions pos0 + i; k/v point at key 0 of the range.
+struct Seg {
+  const void* k;
+  const void* v;
+  int64_t ks_t, ks_h, vs_t, vs_h;
+  int64_t pos0;
+  int32_t n;
+  int32_t pad_;
+};
+
+// The query side shared by every attention kernel.  Query "flat rows" of KV
+// head g are f = t * G + j for token t < q_len and group member j < G; flat
+// row f reads q head g * G + j of token t, sits at position q_pos0 + t, and
+// owns state row t * Hq + g * G + j.
+struct QSide {
+  const void* q;
+  int64_t qs_t, qs_h;
+  int64_t q_pos0;
+  int32_t Hq, Hkv, G, q_len;
+  float c;        // logit scale * log2(e): the kernels work in base 2
+  int32_t causal;
+};
+
+// Walk: each workgroup owns one tile of flat rows of one KV head and visits
+// seg[0..n_seg) in order, carrying the state in registers.
+struct WalkArgs {
+  QSide qs;
+  float* m;
+  float* l;
+  float* o;
+  int32_t reset;
+  int32_t n_seg;
+  Seg seg[kMaxSeg];
+};
+
+// Split: workgroup (row tile, KV head) x chunk; chunk c of the segment table
+// lies in segment s with chunk_begin[s] <= c < chunk_begin[s+1] and covers
+// keys [(c - chunk_begin[s]) * chunk_len, ...) of it.  Each writes the partial
+// state of its rows over its chunk into slot c of the workspace:
+// ws_m[c * R + r], ws_l[c * R + r], ws_o[(c * R + r) * D + d] with R = q_len * Hq.
+struct SplitArgs {
+  QSide qs;
+  float* ws_m;
+  float* ws_l;
+  float* ws_o;
+  int64_t R;
+  int32_t chunk_len;
+  int32_t n_seg;
+  int32_t chunk_begin[kMaxSeg + 1];
+  Seg seg[kMaxSeg];
+};
+
+// Fan-out suffix jobs: job (b, g) owns flat rows [b*G, b*G + G) of KV head g and
+// the keys of branch b's private suffix; writes slot `slot` of the workspace.
+struct SuffixArgs {
+  QSide qs;
+  const void* sk;
+  const void* sv;
+  int32_t S;       // suffix keys per branch
+  int32_t slot;
+  float* ws_m;
+  float* ws_l;
+  float* ws_o;
+  int64_t R;
+};
+
+// Merge of strided workspace partials: group i merges slots
+// [part_begin[i], part_begin[i+1]) (plus the current contents of out[i] when
+// has_init) into out[i]; or, with fin_out set, finalises straight to bf16.
+struct MergeGroupArgs {
+  const float* pm;
+  const float* pl;
+  const float* po;
+  int64_t R;
+  int32_t n_groups;
+  int32_t has_init;
+  int32_t part_begin[kMaxSeg + 1];
+  float* out_m[kMaxSeg];
+  float* out_l[kMaxSeg];
+  float* out_o[kMaxSeg];
+  uint16_t* fin_out;  // bf16 [R, D] when not null (finalise instead of out_*)
+  float* fin_lse;     // optional with fin_out
+};
+
+struct MergePtrArgs {
+  int32_t n_parts;
+  int64_t R;
+  const float* m[kMaxParts];
+  const float* l[kMaxParts];
+  const float* o[kMaxParts];
+  float* out_m;
+  float* out_l;
+  float* out_o;
+};
+
+struct FinalizeArgs {
+  const float* m;
+  const float* l;
+  const float* o;
+  int64_t R;
+  void* out;
+  int32_t out_bf16;
+  int64_t out_stride;
+  float* lse;
+};
+
+// Rows per workgroup tile of the bf16 attention kernels.
+constexpr int kTileRows = 128;
+
+hipError_t launch_walk_bf16(const WalkArgs& a, int D, hipStream_t s);
+hipError_t launch_split_bf16(const SplitArgs& a, int n_chunks, int D, hipStream_t s);
+hipError_t launch_suffix_bf16(const SuffixArgs& a, int n_branches, int D, hipStream_t s);
+hipError_t launch_walk_f32(const WalkArgs& a, int D, hipStream_t s);
+hipError_t launch_merge_groups(const MergeGroupArgs& a, int D, hipStream_t s);
+hipError_t launch_merge_ptrs(const MergePtrArgs& a, int D, hipStream_t s);
+hipError_t launch_finalize(const FinalizeArgs& a, int D, hipStream_t s);
+
+}  // namespace ba

@@ -1,0 +1,244 @@
+/*
+ * blockattn.h -- C ABI of the exact blockwise attention library (libblockattn.so).
+ *
+ * The library computes exact softmax attention for a stationary query block
+ * by walking K/V blocks in a caller-given order while carrying the per-row
+ * online-softmax state (running max m, denominator l, unnormalised output O);
+ * it merges partial states of the same rows by log-sum-exp, finalises a state
+ * into the attention output and its log-sum-exp, and runs shared-prefix
+ * fan-out decode.  Sources (page title, section):
+ *
+ *   [RAC]  "RingAttention and Context Parallelism: Mathematical Foundations,
+ *          Block-Wise Exact Attention Over Ring Topologies ..." (llms.blog):
+ *          s.1 attention definition and causal mask; s.2 online-softmax
+ *          recurrence and final normalisation; s.3 state initialisation and the
+ *          ring schedule (device k holds block (k - t) mod N at step t);
+ *          s.5 causal rule; s.7 log-sum-exp statistic L = m + ln l.
+ *   [RAS]  "Ring Attention: Blockwise Transformers for Near-Infinite Context"
+ *          (daily summary), "The mechanism": the order of the K/V walk for a
+ *          fixed query block does not change the result.
+ *   [AHBM] "AHBM Agentic Runtime Architecture": s.1.3 / s.3.2 query rows of
+ *          several branches batched against one shared KV; s.3.3 per-shard row
+ *          state; s.3.4 merge by matching row index only; s.3.5 hierarchical
+ *          reduction with one merge primitive.
+ *   [TEX]  "Supporting Agentic Workloads": Stationary-KV policy -- query rows
+ *          logically replicated over a stationary, sequence-sharded KV.
+ *
+ * Conventions for every entry point
+ *   - Every tensor pointer is a DEVICE pointer allocated and owned by the
+ *     caller.  The library never allocates, frees or retains memory and never
+ *     synchronises; all work is enqueued on `stream` (0 = the null stream) and
+ *     runs asynchronously.  Argument arrays marked HOST are read before the
+ *     call returns and may be freed afterwards.
+ *   - All argument checks run on the host before anything is enqueued.  A
+ *     failed check returns a non-zero ba_status, enqueues nothing, and leaves a
+ *     message for blockattn_last_error().  A kernel launch failure returns
+ *     BA_ERR_HIP; faults inside kernels surface at the caller's next
+ *     synchronisation.
+ *   - Strides are in elements.  The head_dim axis is always contiguous.
+ *     bf16 tensors need 16-byte aligned base pointers and strides that are
+ *     multiples of 8 elements; state `o` arrays need 16-byte alignment.
+ *   - A "state" is three fp32 arrays indexed by row r = token * n_q_heads +
+ *     q_head: m[rows], l[rows], o[rows * head_dim] (row-major, o unnormalised).
+ *     m is in natural-log units of the scaled logit.  The initial state of
+ *     [RAC] s.3 is m = -inf, l = 0, o = 0; a row that has seen no key keeps it.
+ *   - GQA: query head h reads KV head h / (n_q_heads / n_kv_heads).
+ *   - Causal: a key at absolute position p_k is visible to a query at absolute
+ *     position p_q iff p_k <= p_q ([RAC] s.5).  K/V blocks or chunks that no
+ *     query of a tile can see are skipped.
+ *   - Results are bitwise reproducible for identical inputs, arguments and
+ *     device (no floating-point atomics).
+ *   - Calls are thread-safe; calls that write the same buffers concurrently race.
+ */
+#ifndef BLOCKATTN_H
+#define BLOCKATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BLOCKATTN_ABI_VERSION 1
+#define BLOCKATTN_MAX_VISITS 32      /* max K/V blocks visited by one fwd call   */
+#define BLOCKATTN_MAX_MERGE_PARTS 64 /* max partial states merged by one call    */
+
+typedef enum {
+  BA_OK = 0,
+  BA_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  BA_ERR_SHAPE = 2,       /* inconsistent or out-of-range sizes or strides      */
+  BA_ERR_UNSUPPORTED = 3, /* valid request this build does not implement        */
+  BA_ERR_ORDER = 4,       /* visit order has a duplicate or out-of-range index  */
+  BA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required         */
+  BA_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed         */
+} ba_status;
+
+typedef enum { BA_F32 = 0, BA_BF16 = 1 } ba_dtype;
+
+/* The stationary query block ([RAC] s.3: Q_k stays on its device).
+ * q is [q_len, n_q_heads, head_dim] with the given token and head strides;
+ * query row t sits at absolute position q_pos0 + t. */
+typedef struct {
+  int32_t n_q_heads;      /* Hq, a multiple of n_kv_heads                      */
+  int32_t n_kv_heads;     /* Hkv                                               */
+  int32_t head_dim;       /* D: 64 or 128                                      */
+  int32_t q_len;          /* query tokens (0 is a no-op)                       */
+  int64_t q_pos0;         /* absolute position of query token 0                */
+  int64_t q_stride_token; /* elements between consecutive tokens of q         */
+  int64_t q_stride_head;  /* elements between consecutive heads of q          */
+  int32_t dtype;          /* ba_dtype of Q, K and V                            */
+  float scale;            /* logit scale; <= 0 selects 1/sqrt(head_dim)        */
+  int32_t causal;         /* non-zero: apply the causal rule                   */
+  int32_t split_mode;     /* 0: automatic; 1: never split the keys (one pass in
+                             visit order); 2: always split (bf16 only).  Only
+                             rounding differs between the modes.              */
+} ba_problem;
+
+/* One K/V block: k and v are [len, n_kv_heads, head_dim]; key i sits at
+ * absolute position pos0 + i ([RAC] s.3, contiguous blocks of the sequence). */
+typedef struct {
+  const void* k;
+  const void* v;
+  int32_t len;
+  int64_t pos0;
+  int64_t k_stride_token, k_stride_head;
+  int64_t v_stride_token, v_stride_head;
+} ba_kv_block;
+
+/* fp32 online-softmax state; see the conventions above. */
+typedef struct {
+  float* m;
+  float* l;
+  float* o;
+} ba_state;
+
+/* Shared-prefix fan-out decode shapes ([AHBM] s.1.1, s.3.1-3.2). */
+typedef struct {
+  int32_t n_branches;  /* branches, one new query token each                   */
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;    /* 64 or 128                                             */
+  int32_t prefix_len;  /* shared prefix keys (>= 0)                             */
+  int32_t suffix_len;  /* private keys per branch, incl. the new token (>= 0)  */
+  float scale;         /* <= 0 selects 1/sqrt(head_dim)                         */
+} ba_fanout;
+
+/* Walk K/V blocks for one stationary query block, updating `state` in place.
+ *
+ * Visits blocks[order[0]], blocks[order[1]], ..., blocks[order[n_visit-1]]
+ * (order is a HOST array of distinct indices < n_blocks; NULL means
+ * 0, 1, ..., n_visit-1) and applies the online-softmax step of [RAC] s.2 to
+ * every query row: m_new = max(m_old, max_j s_j); P = exp(s - m_new);
+ * l_new = exp(m_old - m_new) l_old + sum_j P_j; O_new = exp(m_old - m_new) O_old
+ * + P V, with s = scale * q . k.  With reset_state != 0 the state is first
+ * set to (-inf, 0, 0) ([RAC] s.3); otherwise the caller's state is continued,
+ * so one call per ring step carries the state between steps.  The order only
+ * affects rounding ([RAS]).  bf16 runs QK^T and PV on bf16 matrix cores with
+ * fp32 accumulation and rounds P to bf16 (nearest-even) before PV; f32 runs
+ * every step in fp32.
+ *
+ * When the query block has too few rows to fill the GPU (bf16 only) the keys
+ * are split into chunks computed in parallel and merged by log-sum-exp; that
+ * needs `workspace` of blockattn_fwd_workspace_bytes() bytes (device memory,
+ * 256-byte aligned).  Otherwise workspace may be NULL.
+ *
+ * Errors: BA_ERR_NULL (p, q, blocks with n_visit > 0, a block's k/v with
+ * len > 0, or a state array); BA_ERR_SHAPE (bad head counts, head_dim, negative
+ * lengths, non-positive strides); BA_ERR_ORDER (duplicate/out-of-range order
+ * entry, n_visit > BLOCKATTN_MAX_VISITS or > n_blocks); BA_ERR_UNSUPPORTED
+ * (dtype); BA_ERR_WORKSPACE. */
+ba_status blockattn_fwd_block(const ba_problem* p, const void* q,
+                              const ba_kv_block* blocks, int32_t n_blocks,
+                              const int32_t* order, int32_t n_visit,
+                              ba_state state, int32_t reset_state,
+                              void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/* Bytes of workspace blockattn_fwd_block needs for these arguments (0 when
+ * none).  Returns 0 as well for arguments blockattn_fwd_block would reject. */
+size_t blockattn_fwd_workspace_bytes(const ba_problem* p, const ba_kv_block* blocks,
+                                     int32_t n_blocks, const int32_t* order,
+                                     int32_t n_visit);
+
+/* Per-shard partial states ([AHBM] s.3.3; [TEX] Stationary-KV policy).
+ *
+ * For every block i < n_blocks, writes states_out[i] = the online-softmax
+ * state of all query rows over block i alone (as if blockattn_fwd_block
+ * visited only block i from the initial state).  states_out is a HOST array
+ * of n_blocks states; they must not overlap.  bf16 only.  Needs
+ * blockattn_shard_workspace_bytes() bytes of workspace.  Errors as for
+ * blockattn_fwd_block; n_blocks <= BLOCKATTN_MAX_VISITS. */
+ba_status blockattn_shard_states(const ba_problem* p, const void* q,
+                                 const ba_kv_block* blocks, int32_t n_blocks,
+                                 const ba_state* states_out,
+                                 void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+size_t blockattn_shard_workspace_bytes(const ba_problem* p, const ba_kv_block* blocks,
+                                       int32_t n_blocks);
+
+/* Row-wise n-way log-sum-exp merge of partial states ([AHBM] s.3.4-3.5).
+ *
+ * parts is a HOST array of n_parts states over the same `rows` rows (each
+ * computed over a disjoint key set).  For every row r:
+ *   m* = max_s m_s[r];  w_s = exp(m_s[r] - m*) (0 when m_s[r] = -inf);
+ *   l* = sum_s w_s l_s[r];  o*[r,:] = sum_s w_s o_s[r,:].
+ * Parts whose m is -inf contribute nothing and their o is not read.  Rows are
+ * never combined with other rows.  `out` may be one of the parts (in place);
+ * it must not partially overlap any part.  1 <= n_parts <=
+ * BLOCKATTN_MAX_MERGE_PARTS; merge more by merging merged states (the same
+ * primitive at every level, [AHBM] s.3.5).  Errors: BA_ERR_NULL, BA_ERR_SHAPE. */
+ba_status blockattn_merge_states(int32_t n_parts, const ba_state* parts,
+                                 int64_t rows, int32_t head_dim,
+                                 ba_state out, hipStream_t stream);
+
+/* Final normalisation ([RAC] s.2: A = O / l) and log-sum-exp ([RAC] s.7).
+ *
+ * out[r * out_row_stride + d] = o[r, d] / l[r] stored as out_dtype (bf16
+ * rounds to nearest even); lse[r] = m[r] + ln l[r] (lse may be NULL).  Rows
+ * with l == 0 give out = 0 and lse = -inf.  Errors: BA_ERR_NULL, BA_ERR_SHAPE
+ * (out_row_stride < head_dim), BA_ERR_UNSUPPORTED (out_dtype). */
+ba_status blockattn_finalize(ba_state st, int64_t rows, int32_t head_dim,
+                             void* out, int32_t out_dtype, int64_t out_row_stride,
+                             float* lse, hipStream_t stream);
+
+/* Shared-prefix fan-out decode ([AHBM] s.1.1-1.3, s.3.1-3.4; [TEX]).
+ *
+ * q [n_branches, n_q_heads, head_dim] bf16 holds one new query token per
+ * branch; prefix_k/v [prefix_len, n_kv_heads, head_dim] bf16 is the shared
+ * prefix, read once for all branches; suffix_k/v [n_branches, suffix_len,
+ * n_kv_heads, head_dim] bf16 holds each branch's private keys (including the
+ * new token's own K/V).  All contiguous.  Branch b attends, without a mask,
+ * to the prefix followed by its own suffix.  The query rows of every branch
+ * that share a KV head are batched into one matrix against each prefix chunk;
+ * each branch's suffix gives its own partial; the partials of each row are
+ * merged by log-sum-exp and finalised.  Writes out [n_branches, n_q_heads,
+ * head_dim] bf16 and, if lse is not NULL, lse [n_branches, n_q_heads] fp32.
+ * Needs fanout_workspace_bytes() bytes of workspace.  Errors: BA_ERR_NULL,
+ * BA_ERR_SHAPE (no keys at all, bad heads or head_dim), BA_ERR_WORKSPACE. */
+ba_status fanout_prefix_decode(const ba_fanout* f, const void* q,
+                               const void* prefix_k, const void* prefix_v,
+                               const void* suffix_k, const void* suffix_v,
+                               void* out, float* lse,
+                               void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+size_t fanout_workspace_bytes(const ba_fanout* f);
+
+/* Static description of a status code; never NULL. */
+const char* blockattn_status_str(int32_t status);
+
+/* Message of the last failed check on the calling thread ("" if none). */
+const char* blockattn_last_error(void);
+
+/* BLOCKATTN_ABI_VERSION of the loaded library. */
+int32_t blockattn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BLOCKATTN_H */

@@ -1,0 +1,178 @@
+"""The C-ABI library loads, exports every declared entry point, shares
+torch's HIP runtime, and rejects bad arguments on the host before any launch.
+
+No GPU is needed: every call here fails validation before anything is
+enqueued (pointers are never dereferenced on the host).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch  # noqa: F401  (load torch's HIP runtime first)
+
+from exact_blockwise_long_amd import blockattn as ba
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "blockattn.h")
+
+FAKE = 0x100000  # a 256-byte aligned non-null address that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:blockattn|fanout)_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ba.LIB_PATH):
+        pytest.skip("libblockattn.so not built")
+    return ba.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert "blockattn_fwd_block" in names and "fanout_prefix_decode" in names
+    assert set(names) == set(ba.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_single_hip_runtime(lib):
+    loaded = ba.hip_runtimes_loaded()
+    assert len(loaded) == 1, loaded
+
+
+def test_version_and_status_strings(lib):
+    assert lib.blockattn_abi_version() == 1
+    for s in range(7):
+        assert lib.blockattn_status_str(s)
+    assert lib.blockattn_status_str(99) == b"unknown status"
+
+
+def _problem(**kw):
+    p = ba.Problem(8, 2, 128, 16, 0, 8 * 128, 128, ba.BA_BF16, 0.0, 0, 0)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def _blocks(n, length=64):
+    arr = (ba.KVBlock * n)()
+    for i in range(n):
+        arr[i] = ba.KVBlock(FAKE, FAKE, length, i * length, 2 * 128, 128, 2 * 128, 128)
+    return arr
+
+
+def _state():
+    return ba.State(FAKE, FAKE, FAKE)
+
+
+def _fwd(lib, p, blocks, n_blocks, order, n_visit, ws=None, ws_bytes=0, state=None, q=FAKE):
+    o = None
+    if order is not None:
+        o = (ctypes.c_int32 * len(order))(*order)
+    return lib.blockattn_fwd_block(ctypes.byref(p) if p is not None else None, q, blocks, n_blocks, o, n_visit,
+                                   state or _state(), 1, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(head_dim=96), 2), (dict(n_q_heads=6, n_kv_heads=4), 2), (dict(n_kv_heads=0), 2),
+    (dict(q_len=-1), 2), (dict(dtype=7), 3), (dict(q_stride_token=0), 2), (dict(split_mode=5), 2),
+    (dict(q_stride_head=12), 2),
+])
+def test_fwd_rejects_bad_problem(lib, kw, expect):
+    assert _fwd(lib, _problem(**kw), _blocks(2), 2, [0, 1], 2) == expect
+    assert lib.blockattn_last_error()
+
+
+def test_fwd_null_arguments(lib):
+    assert _fwd(lib, None, _blocks(1), 1, None, 1) == 1
+    assert _fwd(lib, _problem(), _blocks(1), 1, None, 1, q=None) == 1
+    assert _fwd(lib, _problem(), None, 1, None, 1) == 1
+    assert _fwd(lib, _problem(split_mode=1), _blocks(1), 1, None, 1, state=ba.State(FAKE, None, FAKE)) == 1
+    bad = _blocks(1)
+    bad[0].k = None
+    assert _fwd(lib, _problem(), bad, 1, None, 1) == 1
+
+
+@pytest.mark.parametrize("order,n_blocks", [([0, 0], 2), ([0, 2], 2), ([-1], 2), (list(range(33)), 40)])
+def test_fwd_rejects_bad_order(lib, order, n_blocks):
+    assert _fwd(lib, _problem(), _blocks(n_blocks), n_blocks, order, len(order)) == 4
+
+
+def test_fwd_rejects_misaligned(lib):
+    bad = _blocks(1)
+    bad[0].k = FAKE + 2
+    assert _fwd(lib, _problem(), bad, 1, None, 1) == 2
+    assert _fwd(lib, _problem(), _blocks(1), 1, None, 1, q=FAKE + 4) == 2
+    assert _fwd(lib, _problem(split_mode=1), _blocks(1), 1, None, 1, state=ba.State(FAKE, FAKE, FAKE + 4)) == 2
+
+
+def test_split_needs_workspace(lib):
+    p = _problem(split_mode=2)
+    need = lib.blockattn_fwd_workspace_bytes(ctypes.byref(p), _blocks(3), 3, None, 3)
+    assert need > 0
+    assert _fwd(lib, p, _blocks(3), 3, None, 3) == 5
+    assert _fwd(lib, p, _blocks(3), 3, None, 3, ws=FAKE, ws_bytes=need - 1) == 5
+    # walk mode needs none
+    assert lib.blockattn_fwd_workspace_bytes(ctypes.byref(_problem(split_mode=1)), _blocks(3), 3, None, 3) == 0
+    # the f32 path never splits
+    assert lib.blockattn_fwd_workspace_bytes(ctypes.byref(_problem(dtype=ba.BA_F32, split_mode=0)),
+                                             _blocks(3), 3, None, 3) == 0
+
+
+def test_shard_states_validation(lib):
+    p = _problem()
+    sts = (ba.State * 2)(_state(), _state())
+    assert lib.blockattn_shard_states(ctypes.byref(p), FAKE, _blocks(2), 0, sts, None, 0, None) == 4
+    assert lib.blockattn_shard_states(ctypes.byref(_problem(dtype=ba.BA_F32)), FAKE, _blocks(2), 2, sts,
+                                      None, 0, None) == 3
+    assert lib.blockattn_shard_states(ctypes.byref(p), FAKE, _blocks(2), 2, sts, None, 0, None) == 5
+    assert lib.blockattn_shard_workspace_bytes(ctypes.byref(p), _blocks(2), 2) > 0
+
+
+def test_merge_validation(lib):
+    parts = (ba.State * 2)(_state(), _state())
+    assert lib.blockattn_merge_states(0, parts, 10, 128, _state(), None) == 2
+    assert lib.blockattn_merge_states(65, parts, 10, 128, _state(), None) == 2
+    assert lib.blockattn_merge_states(2, None, 10, 128, _state(), None) == 1
+    assert lib.blockattn_merge_states(2, parts, 10, 100, _state(), None) == 2
+    assert lib.blockattn_merge_states(2, parts, 10, 128, ba.State(None, FAKE, FAKE), None) == 1
+    # zero rows is a valid no-op that launches nothing
+    assert lib.blockattn_merge_states(2, parts, 0, 128, _state(), None) == 0
+
+
+def test_finalize_validation(lib):
+    assert lib.blockattn_finalize(_state(), 4, 128, None, ba.BA_BF16, 128, None, None) == 1
+    assert lib.blockattn_finalize(_state(), 4, 128, FAKE, ba.BA_BF16, 64, None, None) == 2
+    assert lib.blockattn_finalize(_state(), 4, 128, FAKE, 9, 128, None, None) == 3
+    assert lib.blockattn_finalize(_state(), 0, 128, FAKE, ba.BA_BF16, 128, None, None) == 0
+
+
+def test_fanout_validation(lib):
+    def call(f, ws=None, ws_bytes=0, **ptrs):
+        a = dict(q=FAKE, pk=FAKE, pv=FAKE, sk=FAKE, sv=FAKE, out=FAKE)
+        a.update(ptrs)
+        return lib.fanout_prefix_decode(ctypes.byref(f), a["q"], a["pk"], a["pv"], a["sk"], a["sv"], a["out"],
+                                        None, ws, ws_bytes, None)
+    assert call(ba.Fanout(4, 8, 3, 128, 100, 10, 0.0)) == 2
+    assert call(ba.Fanout(4, 8, 2, 128, 0, 0, 0.0)) == 2
+    assert call(ba.Fanout(4, 8, 2, 128, 100, 10, 0.0), q=None) == 1
+    assert call(ba.Fanout(4, 8, 2, 128, 100, 10, 0.0), pk=None) == 1
+    f = ba.Fanout(4, 8, 2, 128, 100, 10, 0.0)
+    need = lib.fanout_workspace_bytes(ctypes.byref(f))
+    assert need > 0
+    assert call(f) == 5
+    assert call(f, ws=FAKE, ws_bytes=need - 16) == 5
+    assert call(ba.Fanout(0, 8, 2, 128, 100, 10, 0.0)) == 0   # no branches: no-op
+
+
+def test_workspace_sizes_are_deterministic(lib):
+    f = ba.Fanout(16, 64, 8, 128, 65536, 512, 0.0)
+    a = lib.fanout_workspace_bytes(ctypes.byref(f))
+    b = lib.fanout_workspace_bytes(ctypes.byref(f))
+    assert a == b and a % 256 == 0
