@@ -10,21 +10,28 @@
 // Mapping onto CDNA4:
 //  * A workgroup is 4 waves and owns 128 "flat rows" (query token x member of
 //    one GQA group) that all read the same KV head, so one K/V tile in LDS
-//    serves 8 query heads ([AHBM] s.1.3: rows batched against shared KV).
+//    serves every query head of the group ("AHBM Agentic Runtime
+//    Architecture" s.1.3: rows batched against shared KV).
+//  * K/V tiles of 64 keys go HBM -> LDS with buffer_load_dwordx4 ... lds (no
+//    register staging), double-buffered: the next tile's loads are in flight
+//    while the current one is multiplied.  16-byte chunks of every LDS row are
+//    XOR-swizzled by row so both operand reads below are bank-conflict free.
 //  * Each wave owns 32 rows.  Scores are formed transposed, S^T = K Q^T, with
-//    v_mfma_f32_16x16x32_bf16: K (from LDS) is the A operand and Q (kept in
-//    registers for the whole kernel) the B operand.  The S^T accumulator then
-//    holds, per lane, 4 consecutive keys of one query row -- exactly the
-//    B-operand layout of the second product O^T = V^T P^T, so P never leaves
-//    registers.  V is staged into LDS transposed (V^T) for the A operand.
-//  * Softmax statistics are per query column: every lane of a 16-lane column
-//    group holds one query row, the row max needs two cross-lane exchanges,
-//    and the row sum is kept as per-lane partial sums until the end.
-//  * exp is computed as exp2 on v_exp_f32 with the logit scale folded into a
-//    single multiply by scale*log2(e); the state's m is converted to natural
-//    units at load/store.
-//  * K/V tiles of 64 keys are double-buffered in LDS: the next tile's global
-//    loads are in flight while the current tile is multiplied.
+//    v_mfma_f32_16x16x32_bf16: K (ds_read_b128 from LDS) is the A operand and
+//    Q (kept in registers for the whole kernel) the B operand.  The S^T
+//    accumulator holds, per lane, 4 consecutive keys of one query row --
+//    exactly the B-operand layout of O^T = V^T P^T, so P never leaves
+//    registers.  The V^T A-operand comes straight from the row-major V tile
+//    through the LDS transpose read ds_read_b64_tr_b16.
+//  * Softmax statistics are per query column: the 4 lanes of a column share a
+//    row, the row max needs two cross-lane exchanges, and the row sum is kept
+//    as per-lane partial sums until the end.  exp is exp2 on v_exp_f32 with
+//    the logit scale folded into one FMA by scale*log2(e).
+//  * Lazy rescaling: a row's reference max only moves when a tile's max
+//    exceeds it by more than kTau (base 2), so exp2 arguments stay <= kTau and
+//    the O rescale is skipped for the whole wave in almost every tile.  The
+//    true running max is tracked alongside and the state is renormalised to it
+//    when written, so the stored (m, l, O) is exactly the recurrence's.
 #include "internal.h"
 
 namespace ba {
@@ -33,27 +40,34 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kThreads = 256;
 constexpr int kTileKeys = 64;
+constexpr float kTau = 8.0f;   // lazy-rescale headroom, log2 units
 
 template <int D>
 struct Cfg {
-  static constexpr int KSTR = D + 8;           // bf16 elements per K row in LDS
-  static constexpr int VSTR = kTileKeys + 4;   // bf16 elements per V^T row in LDS
-  static constexpr int K_ELEMS = kTileKeys * KSTR;
-  static constexpr int V_ELEMS = D * VSTR;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;
-  static constexpr int DC = D / 32;            // 32-wide d chunks (QK^T K-dim steps)
-  static constexpr int DB = D / 16;            // 16-wide d blocks of O^T
-  static constexpr int CPK = D / 8;            // 16-byte chunks per K row
-  static constexpr int K_PER_THREAD = kTileKeys * CPK / kThreads;
-  static constexpr int V_ITEMS = (kTileKeys / 4) * (D / 8);   // (4 keys x 8 d) items
+  static constexpr int ROWB = D * 2;                  // bytes per K or V row in LDS
+  static constexpr int CPR = D / 8;                   // 16-byte chunks per row
+  static constexpr int TILEB = kTileKeys * ROWB;      // bytes of one K (or V) tile
+  static constexpr int STAGEB = 2 * TILEB;            // K tile then V tile
+  static constexpr int RPI = 64 / CPR;                // rows per wave-wide 1 KiB load
+  static constexpr int LPW = kTileKeys / RPI / 4;     // loads per wave per tile (each of K and V)
+  static constexpr int DC = D / 32;                   // 32-wide d chunks (QK^T K-dim steps)
+  static constexpr int DB = D / 16;                   // 16-wide d blocks of O^T
 };
 
+// Chunk swizzles (XOR on the 16-byte chunk index within a row).
+template <int D>
+__device__ inline int swz_k(int row) { return D == 128 ? (row & 15) : (row & 7); }
+template <int D>
+__device__ inline int swz_v(int row) { return D == 128 ? ((row & 7) << 1) : ((row & 3) << 1); }
+
 __device__ inline float wave_max_cols(float x) {
-  // max over the 4 lanes that share lane % 16
   x = fmaxf(x, __shfl_xor(x, 16));
   x = fmaxf(x, __shfl_xor(x, 32));
   return x;
@@ -72,10 +86,9 @@ __device__ inline unsigned pack_bf16x2(float a, float b) {
          ((unsigned)__builtin_bit_cast(unsigned short, y) << 16);
 }
 
-// The 4-key group index of a 64-key tile row of V^T is XOR-swizzled with
-// (d / 8) % 16 so that both the transposing stores and the operand loads
-// spread over the LDS banks.
-__device__ inline int vt_col(int d, int group) { return ((group ^ ((d >> 3) & 15)) << 2); }
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
 
 // Per-workgroup description of the query rows.
 struct RowCtx {
@@ -87,75 +100,70 @@ struct RowCtx {
 // Per-lane registers of the running state for the wave's 2 column blocks.
 template <int D>
 struct Acc {
-  f32x4 o[Cfg<D>::DB][2];  // O^T[16*db + 4*(lane/16) + i][query col]
-  float m2[2];             // running max in base-2 units (scaled logit * log2 e)
-  float lp[2];             // per-lane partial of the denominator
+  f32x4 o[Cfg<D>::DB][2];  // O^T[16*db + 4*(lane/16) + i][query col], relative to m2
+  float m2[2];             // reference max (base 2): exp2 arguments are <= kTau
+  float mt[2];             // true running max (base 2)
+  float lp[2];             // per-lane partial of the denominator, relative to m2
+};
+
+// A key range as the kernels see it: buffer resources over K and V of one KV
+// head, the byte stride between keys, the absolute position of key 0 and the
+// number of keys.  Reads past the range return zeros (buffer range check).
+struct KVSrc {
+  __amdgpu_buffer_rsrc_t k, v;
+  uint32_t kst, vst;       // bytes between consecutive keys
+  int64_t pos0;
+  int n;
 };
 
 template <int D>
-__device__ inline void load_tile_regs(const Seg& s, int g, int k_off, int n_valid, int tid,
-                                      u32x4 (&kr)[Cfg<D>::K_PER_THREAD], u32x4 (&vr)[4]) {
+__device__ inline KVSrc make_src(const Seg& s, int g) {
+  KVSrc r;
+  const char* kb = (const char*)s.k + (int64_t)g * s.ks_h * 2;
+  const char* vb = (const char*)s.v + (int64_t)g * s.vs_h * 2;
+  r.kst = (uint32_t)(s.ks_t * 2);
+  r.vst = (uint32_t)(s.vs_t * 2);
+  r.k = make_rsrc(kb, s.n > 0 ? (uint32_t)((s.n - 1) * (int64_t)r.kst + D * 2) : 0u);
+  r.v = make_rsrc(vb, s.n > 0 ? (uint32_t)((s.n - 1) * (int64_t)r.vst + D * 2) : 0u);
+  r.pos0 = s.pos0;
+  r.n = s.n;
+  return r;
+}
+
+// Issue the HBM -> LDS loads of keys [k0, k0 + n_valid) of `src` into one stage.
+// Rows past n_valid repeat the last valid key (their scores are masked).  Each
+// wave-wide load moves RPI whole rows; lane (row r, chunk position p) fetches
+// the global chunk p ^ swizzle(r), which is where operand reads look for it.
+template <int D>
+__device__ inline void issue_tile(const KVSrc& src, int k0, int n_valid, char* stage, int wave, int lane) {
   using C = Cfg<D>;
-  const uint16_t* kb = (const uint16_t*)s.k + (int64_t)g * s.ks_h;
-  const uint16_t* vb = (const uint16_t*)s.v + (int64_t)g * s.vs_h;
+  const int rsub = lane / C::CPR;
+  const int p = lane % C::CPR;
+  const uint32_t soff_k = (uint32_t)k0 * src.kst;
+  const uint32_t soff_v = (uint32_t)k0 * src.vst;
 #pragma unroll
-  for (int i = 0; i < C::K_PER_THREAD; ++i) {
-    int c = tid + i * kThreads;
-    int key = c / C::CPK;
-    int col = (c % C::CPK) * 8;
-    int kk = min(key, n_valid - 1);
-    kr[i] = *(const u32x4*)(kb + (int64_t)(k_off + kk) * s.ks_t + col);
-  }
-  if (tid < C::V_ITEMS) {
-    int dq = tid % (D / 8);
-    int kq = tid / (D / 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int kk = min(4 * kq + i, n_valid - 1);
-      vr[i] = *(const u32x4*)(vb + (int64_t)(k_off + kk) * s.vs_t + dq * 8);
-    }
+  for (int j = 0; j < C::LPW; ++j) {
+    const int rbase = (wave * C::LPW + j) * C::RPI;
+    const int row = rbase + rsub;
+    const int rr = min(row, n_valid - 1);
+    const uint32_t vk = (uint32_t)rr * src.kst + (uint32_t)((p ^ swz_k<D>(row)) * 16);
+    const uint32_t vv = (uint32_t)rr * src.vst + (uint32_t)((p ^ swz_v<D>(row)) * 16);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, (lds_void*)(stage + rbase * C::ROWB), 16, vk, soff_k, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.v, (lds_void*)(stage + C::TILEB + rbase * C::ROWB), 16, vv,
+                                             soff_v, 0, 0);
   }
 }
 
-template <int D>
-__device__ inline void store_tile_lds(uint16_t* st, int tid, const u32x4 (&kr)[Cfg<D>::K_PER_THREAD],
-                                      const u32x4 (&vr)[4]) {
-  using C = Cfg<D>;
-  uint16_t* kl = st;
-  uint16_t* vl = st + C::K_ELEMS;
-#pragma unroll
-  for (int i = 0; i < C::K_PER_THREAD; ++i) {
-    int c = tid + i * kThreads;
-    int key = c / C::CPK;
-    int col = (c % C::CPK) * 8;
-    *(u32x4*)(kl + key * C::KSTR + col) = kr[i];
-  }
-  if (tid < C::V_ITEMS) {
-    int dq = tid % (D / 8);
-    int kq = tid / (D / 8);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      // dword w of each loaded row holds d = 8*dq + 2w (low half) and 8*dq + 2w + 1 (high half)
-      unsigned lo01 = (vr[0][w] & 0xffffu) | (vr[1][w] << 16);
-      unsigned lo23 = (vr[2][w] & 0xffffu) | (vr[3][w] << 16);
-      unsigned hi01 = (vr[0][w] >> 16) | (vr[1][w] & 0xffff0000u);
-      unsigned hi23 = (vr[2][w] >> 16) | (vr[3][w] & 0xffff0000u);
-      int d0 = 8 * dq + 2 * w;
-      int d1 = d0 + 1;
-      *(u32x2*)(vl + d0 * C::VSTR + vt_col(d0, kq)) = u32x2{lo01, lo23};
-      *(u32x2*)(vl + d1 * C::VSTR + vt_col(d1, kq)) = u32x2{hi01, hi23};
-    }
-  }
-}
+__device__ inline void wait_tile_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // One 64-key tile for one wave: S^T = K Q^T, online-softmax update, O^T += V^T P^T.
 template <int D>
-__device__ inline void tile_compute(const uint16_t* st, int lane, const bf16x8 (&qf)[2][Cfg<D>::DC],
+__device__ inline void tile_compute(const char* stage, int lane, const bf16x8 (&qf)[2][Cfg<D>::DC],
                                     Acc<D>& acc, float c, bool need_mask, bool causal, int n_valid,
                                     int64_t kpos0, const int64_t (&qpos)[2]) {
   using C = Cfg<D>;
-  const uint16_t* kl = st;
-  const uint16_t* vl = st + C::K_ELEMS;
+  const char* kl = stage;
+  const char* vl = stage + C::TILEB;
   const int lr = lane & 15;
   const int lg = lane >> 4;
 
@@ -169,7 +177,8 @@ __device__ inline void tile_compute(const uint16_t* st, int lane, const bf16x8 (
   for (int dc = 0; dc < C::DC; ++dc) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      bf16x8 kf = *(const bf16x8*)(kl + (16 * kb + lr) * C::KSTR + 32 * dc + 8 * lg);
+      const int row = 16 * kb + lr;
+      const bf16x8 kf = *(const bf16x8*)(kl + row * C::ROWB + (((4 * dc + lg) ^ swz_k<D>(row)) * 16));
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
         s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][dc], s[kb][qb], 0, 0, 0);
@@ -182,8 +191,8 @@ __device__ inline void tile_compute(const uint16_t* st, int lane, const bf16x8 (
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        int kk = 16 * kb + 4 * lg + i;
-        int64_t kp = kpos0 + kk;
+        const int kk = 16 * kb + 4 * lg + i;
+        const int64_t kp = kpos0 + kk;
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
           if (kk >= n_valid || (causal && kp > qpos[qb])) s[kb][qb][i] = -INFINITY;
@@ -196,16 +205,24 @@ __device__ inline void tile_compute(const uint16_t* st, int lane, const bf16x8 (
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
+      mx = fmaxf(mx, fmaxf(fmaxf(s[kb][qb][0], s[kb][qb][1]), fmaxf(s[kb][qb][2], s[kb][qb][3])));
+    mx = wave_max_cols(mx) * c;            // tile max of this lane's row, base 2
+    acc.mt[qb] = fmaxf(acc.mt[qb], mx);
+    const float m_old = acc.m2[qb];
+    // Move the reference only when the tile max is more than kTau above it
+    // (always the case while the row has seen no key: m_old = -inf).
+    const bool move = mx > m_old + kTau;
+    if (__ballot(move) != 0) {
+      const float m_new = move ? mx : m_old;
+      const float alpha = __builtin_amdgcn_exp2f(m_old - m_new);  // 0 when m_old = -inf; 1 if unchanged
+      acc.m2[qb] = m_new;
+      acc.lp[qb] *= alpha;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][qb][i]);
-    mx = wave_max_cols(mx);
-    float m_old = acc.m2[qb];
-    float m_new = fmaxf(m_old, mx * c);
-    float base = (m_new == -INFINITY) ? 0.f : m_new;
-    float alpha = __builtin_amdgcn_exp2f(m_old - base);  // exp2(-inf) = 0 covers m_old = -inf
-    acc.m2[qb] = m_new;
-    float sum = 0.f;
+      for (int db = 0; db < C::DB; ++db) acc.o[db][qb] *= alpha;
+    }
+    const float base = (acc.m2[qb] == -INFINITY) ? 0.f : acc.m2[qb];
     float p[4][4];
+    float sum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -213,9 +230,7 @@ __device__ inline void tile_compute(const uint16_t* st, int lane, const bf16x8 (
         p[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][i], c, -base));
         sum += p[kb][i];
       }
-    acc.lp[qb] = acc.lp[qb] * alpha + sum;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db) acc.o[db][qb] *= alpha;
+    acc.lp[qb] += sum;
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch) {
       u32x4 w;
@@ -229,17 +244,24 @@ __device__ inline void tile_compute(const uint16_t* st, int lane, const bf16x8 (
 
   // O^T[d][q] += sum_key V^T[d][key] P^T[key][q].  MFMA k-slot 8*lg + i of key chunk ch
   // is key 32*ch + 4*lg + i (i < 4) or 32*ch + 16 + 4*lg + (i - 4) (i >= 4) -- the
-  // layout pf was packed in; the V^T operand is read with the same mapping.
+  // layout pf was packed in.  A transposing read hands lane j of a 16-lane group
+  // element j%4 of the 8-byte pieces addressed by lanes j/4 + 4i (i = 0..3); lane a
+  // addresses row key0 + a/4, columns 16*db + 4*(a%4) .. +3, so lane (lg, lr) gets
+  // keys key0 + {0..3} at d = 16*db + lr.
 #pragma unroll
   for (int ch = 0; ch < 2; ++ch) {
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) {
-      int d = 16 * db + lr;
-      const uint16_t* row = vl + d * C::VSTR;
-      u32x2 a = *(const u32x2*)(row + vt_col(d, 8 * ch + lg));
-      u32x2 b = *(const u32x2*)(row + vt_col(d, 8 * ch + 4 + lg));
-      u32x4 w = u32x4{a[0], a[1], b[0], b[1]};
-      bf16x8 vf = __builtin_bit_cast(bf16x8, w);
+      const int row0 = 32 * ch + 4 * lg + (lr >> 2);
+      const int row1 = row0 + 16;
+      const int cidx = 2 * db + ((lr & 3) >> 1);
+      const int half = (lr & 1) * 8;
+      const char* a0 = vl + row0 * C::ROWB + ((cidx ^ swz_v<D>(row0)) * 16) + half;
+      const char* a1 = vl + row1 * C::ROWB + ((cidx ^ swz_v<D>(row1)) * 16) + half;
+      const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a0);
+      const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a1);
+      const s16x8 xx = s16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, xx);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
         acc.o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[ch][qb], acc.o[db][qb], 0, 0, 0);
@@ -294,6 +316,7 @@ __device__ inline void init_acc(Acc<D>& acc) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     acc.m2[qb] = -INFINITY;
+    acc.mt[qb] = -INFINITY;
     acc.lp[qb] = 0.f;
 #pragma unroll
     for (int db = 0; db < Cfg<D>::DB; ++db) acc.o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -309,6 +332,7 @@ __device__ inline void load_acc(Acc<D>& acc, const LaneRows& lr, int lane, const
     int64_t r = lr.srow[qb];
     float mm = m[r];
     acc.m2[qb] = (mm == -INFINITY) ? -INFINITY : mm * kLog2e;
+    acc.mt[qb] = acc.m2[qb];
     acc.lp[qb] = (lg == 0) ? l[r] : 0.f;
 #pragma unroll
     for (int db = 0; db < Cfg<D>::DB; ++db)
@@ -316,22 +340,25 @@ __device__ inline void load_acc(Acc<D>& acc, const LaneRows& lr, int lane, const
   }
 }
 
+// Renormalise to the true running max and write the state of valid rows.
 template <int D>
-__device__ inline void store_acc(const Acc<D>& acc, const LaneRows& lr, int lane, float* m, float* l, float* o,
+__device__ inline void store_acc(Acc<D>& acc, const LaneRows& lr, int lane, float* m, float* l, float* o,
                                  int64_t row_base) {
   const int lg = lane >> 4;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    float lt = wave_sum_cols(acc.lp[qb]);
+    const float mt = acc.mt[qb];
+    const float ref = acc.m2[qb];
+    const float f = (mt == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(ref - mt);
+    const float lt = wave_sum_cols(acc.lp[qb]) * f;
     if (!lr.valid[qb]) continue;
-    int64_t r = row_base + lr.srow[qb];
+    const int64_t r = row_base + lr.srow[qb];
     if (lg == 0) {
-      float mm = acc.m2[qb];
-      m[r] = (mm == -INFINITY) ? -INFINITY : mm * kLn2;
+      m[r] = (mt == -INFINITY) ? -INFINITY : mt * kLn2;
       l[r] = lt;
     }
 #pragma unroll
-    for (int db = 0; db < Cfg<D>::DB; ++db) *(f32x4*)(o + r * D + 16 * db + 4 * lg) = acc.o[db][qb];
+    for (int db = 0; db < Cfg<D>::DB; ++db) *(f32x4*)(o + r * D + 16 * db + 4 * lg) = acc.o[db][qb] * f;
   }
 }
 
@@ -339,10 +366,10 @@ __device__ inline void store_acc(const Acc<D>& acc, const LaneRows& lr, int lane
 template <int D, class GetSeg>
 __device__ inline void run_segments(const QSide& qs, const RowCtx& rc, const LaneRows& lr, int n_seg,
                                     GetSeg get_seg, const bf16x8 (&qf)[2][Cfg<D>::DC], Acc<D>& acc,
-                                    uint16_t* lds, bool wave_active) {
+                                    char* lds, bool wave_active) {
   using C = Cfg<D>;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
 
   // cursor: segment index, key offset, effective key count of that segment
   int cs = 0, ck = 0, cn = 0;
@@ -357,32 +384,27 @@ __device__ inline void run_segments(const QSide& qs, const RowCtx& rc, const Lan
   seek(cs, ck, cn);
   if (cs >= n_seg) return;
 
-  u32x4 kr[C::K_PER_THREAD];
-  u32x4 vr[4];
-  {
-    Seg s = get_seg(cs);
-    load_tile_regs<D>(s, rc.g, ck, min(kTileKeys, cn - ck), tid, kr, vr);
-    store_tile_lds<D>(lds, tid, kr, vr);
-  }
+  KVSrc src = make_src<D>(get_seg(cs), rc.g);
+  issue_tile<D>(src, ck, min(kTileKeys, cn - ck), lds, wave, lane);
+  wait_tile_loads();
   __syncthreads();
   int buf = 0;
   while (cs < n_seg) {
     int ns = cs, nk = ck + kTileKeys, nn = cn;
     seek(ns, nk, nn);
     const bool has_next = ns < n_seg;
+    const int n_valid = min(kTileKeys, cn - ck);
+    const int64_t kpos0 = src.pos0 + ck;
     if (has_next) {
-      Seg s = get_seg(ns);
-      load_tile_regs<D>(s, rc.g, nk, min(kTileKeys, nn - nk), tid, kr, vr);
+      if (ns != cs) src = make_src<D>(get_seg(ns), rc.g);
+      issue_tile<D>(src, nk, min(kTileKeys, nn - nk), lds + (buf ^ 1) * C::STAGEB, wave, lane);
     }
     if (wave_active) {
-      Seg s = get_seg(cs);
-      int n_valid = min(kTileKeys, cn - ck);
-      int64_t kpos0 = s.pos0 + ck;
-      bool need_mask = (n_valid < kTileKeys) || (qs.causal && kpos0 + kTileKeys - 1 > rc.qpos_min);
-      tile_compute<D>(lds + buf * C::STAGE, lane, qf, acc, qs.c, need_mask, qs.causal != 0, n_valid, kpos0,
+      const bool need_mask = (n_valid < kTileKeys) || (qs.causal && kpos0 + kTileKeys - 1 > rc.qpos_min);
+      tile_compute<D>(lds + buf * C::STAGEB, lane, qf, acc, qs.c, need_mask, qs.causal != 0, n_valid, kpos0,
                       lr.qpos);
     }
-    if (has_next) store_tile_lds<D>(lds + (buf ^ 1) * C::STAGE, tid, kr, vr);
+    wait_tile_loads();
     __syncthreads();
     buf ^= 1;
     cs = ns;
@@ -402,8 +424,8 @@ __device__ inline RowCtx make_rowctx(const QSide& qs, int f0, int f1, int g) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void walk_kernel(WalkArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * Cfg<D>::STAGE];
+__global__ __launch_bounds__(kThreads, 2) void walk_kernel(WalkArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[2 * Cfg<D>::STAGEB];
   const int Hkv = a.qs.Hkv;
   const int g = blockIdx.x % Hkv;          // consecutive workgroups land on different XCDs;
   const int tile = blockIdx.x / Hkv;       // with Hkv = 8 each XCD serves one KV head
@@ -430,8 +452,8 @@ __global__ __launch_bounds__(kThreads, 1) void walk_kernel(WalkArgs a) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * Cfg<D>::STAGE];
+__global__ __launch_bounds__(kThreads, 2) void split_kernel(SplitArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[2 * Cfg<D>::STAGEB];
   const int Hkv = a.qs.Hkv;
   const int g = blockIdx.x % Hkv;
   const int tile = blockIdx.x / Hkv;
@@ -464,8 +486,8 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void suffix_kernel(SuffixArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * Cfg<D>::STAGE];
+__global__ __launch_bounds__(kThreads, 2) void suffix_kernel(SuffixArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[2 * Cfg<D>::STAGEB];
   const int Hkv = a.qs.Hkv;
   const int g = blockIdx.x % Hkv;
   const int b = blockIdx.x / Hkv;
