@@ -475,34 +475,36 @@ ba_status check_fanout(const ba_fanout* f) {
 }
 
 struct FanoutPlan {
-  SplitPlan prefix;
-  int slots = 0;
+  int row_tiles = 0;   // 128-row tiles of one KV head's rows (n_branches * G)
+  int chunk_len = 0;
+  int n_chunks = 0;    // prefix chunks
+  int suffix_jobs = 0;
+  int slots = 0;       // workspace partial slots
   int suffix_slot = -1;
+  int n_jobs = 0;
 };
 
+// Prefix chunks are sized so that prefix-chunk jobs plus suffix jobs come to
+// about kFanoutTargetWorkgroups: enough to cover every compute unit and hide
+// HBM latency while keeping the partial states (one per chunk and row) small.
 FanoutPlan plan_fanout(const ba_fanout* f) {
   FanoutPlan fp;
-  ba_problem p;
-  memset(&p, 0, sizeof(p));
-  p.n_q_heads = f->n_q_heads;
-  p.n_kv_heads = f->n_kv_heads;
-  p.q_len = f->n_branches;
-  std::vector<int64_t> keys;
-  if (f->prefix_len > 0) keys.push_back(f->prefix_len);
-  // Aim for about two workgroups per compute unit over the prefix: enough to
-  // hide HBM latency while keeping the partial states small.
-  if (!keys.empty()) {
-    int tiles = row_tiles(&p);
-    int64_t want = (512 + tiles - 1) / tiles;
+  const int G = f->n_q_heads / f->n_kv_heads;
+  fp.row_tiles = (int)(((int64_t)f->n_branches * G + ba::kTileRows - 1) / ba::kTileRows);
+  const int xs = fp.row_tiles * f->n_kv_heads;
+  fp.suffix_jobs = f->suffix_len > 0 ? f->n_branches * f->n_kv_heads : 0;
+  if (f->prefix_len > 0) {
+    int64_t want = (ba::kFanoutTargetWorkgroups - fp.suffix_jobs) / xs;
+    if (want < 1) want = 1;
     int64_t cl = (f->prefix_len + want - 1) / want;
     cl = (cl + 63) / 64 * 64;
     if (cl < 256) cl = 256;
-    fp.prefix.chunk_len = (int)cl;
-    fp.prefix.n_chunks = (int)((f->prefix_len + cl - 1) / cl);
-    fp.prefix.begin = {0, fp.prefix.n_chunks};
+    fp.chunk_len = (int)cl;
+    fp.n_chunks = (int)((f->prefix_len + cl - 1) / cl);
   }
-  fp.slots = fp.prefix.n_chunks;
+  fp.slots = fp.n_chunks;
   if (f->suffix_len > 0) fp.suffix_slot = fp.slots++;
+  fp.n_jobs = xs * fp.n_chunks + fp.suffix_jobs;
   return fp;
 }
 
@@ -549,44 +551,30 @@ ba_status fanout_prefix_decode(const ba_fanout* f, const void* q, const void* pr
   p.causal = 0;
   const ba::QSide qs = make_qside(&p, q);
 
-  if (fp.prefix.n_chunks > 0) {
-    ba::SplitArgs a;
-    memset(&a, 0, sizeof(a));
-    a.qs = qs;
-    a.ws_m = wm;
-    a.ws_l = wl;
-    a.ws_o = wo;
-    a.R = R;
-    a.chunk_len = fp.prefix.chunk_len;
-    a.n_seg = 1;
-    ba_kv_block b;
-    b.k = prefix_k;
-    b.v = prefix_v;
-    b.len = f->prefix_len;
-    b.pos0 = 0;
-    b.k_stride_token = b.v_stride_token = (int64_t)f->n_kv_heads * D;
-    b.k_stride_head = b.v_stride_head = D;
-    a.seg[0] = make_seg(b);
-    a.chunk_begin[0] = 0;
-    a.chunk_begin[1] = fp.prefix.n_chunks;
-    hipError_t e = ba::launch_split_bf16(a, fp.prefix.n_chunks, D, stream);
-    if (e != hipSuccess) return hip_status(e, "fanout prefix launch");
-  }
-  if (fp.suffix_slot >= 0) {
-    ba::SuffixArgs a;
-    memset(&a, 0, sizeof(a));
-    a.qs = qs;
-    a.sk = suffix_k;
-    a.sv = suffix_v;
-    a.S = f->suffix_len;
-    a.slot = fp.suffix_slot;
-    a.ws_m = wm;
-    a.ws_l = wl;
-    a.ws_o = wo;
-    a.R = R;
-    hipError_t e = ba::launch_suffix_bf16(a, f->n_branches, D, stream);
-    if (e != hipSuccess) return hip_status(e, "fanout suffix launch");
-  }
+  ba::FanoutArgs a;
+  memset(&a, 0, sizeof(a));
+  a.qs = qs;
+  ba_kv_block b;
+  b.k = prefix_k;
+  b.v = prefix_v;
+  b.len = f->prefix_len;
+  b.pos0 = 0;
+  b.k_stride_token = b.v_stride_token = (int64_t)f->n_kv_heads * D;
+  b.k_stride_head = b.v_stride_head = D;
+  a.prefix = make_seg(b);
+  a.row_tiles = fp.row_tiles;
+  a.chunk_len = fp.chunk_len;
+  a.n_chunks = fp.n_chunks;
+  a.sk = suffix_k;
+  a.sv = suffix_v;
+  a.S = f->suffix_len;
+  a.suffix_slot = fp.suffix_slot;
+  a.ws_m = wm;
+  a.ws_l = wl;
+  a.ws_o = wo;
+  a.R = R;
+  hipError_t e = ba::launch_fanout_bf16(a, fp.n_jobs, D, stream);
+  if (e != hipSuccess) return hip_status(e, "fanout attention launch");
   ba::MergeGroupArgs mg;
   memset(&mg, 0, sizeof(mg));
   mg.pm = wm;

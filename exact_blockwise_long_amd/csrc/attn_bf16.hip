@@ -154,13 +154,11 @@ __device__ inline void issue_tile(const KVSrc& src, int k0, int n_valid, char* s
   }
 }
 
-__device__ inline void wait_tile_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 // One 64-key tile for one wave: S^T = K Q^T, online-softmax update, O^T += V^T P^T.
 template <int D>
 __device__ inline void tile_compute(const char* stage, int lane, const bf16x8 (&qf)[2][Cfg<D>::DC],
                                     Acc<D>& acc, float c, bool need_mask, bool causal, int n_valid,
-                                    int64_t kpos0, const int64_t (&qpos)[2]) {
+                                    int krel, const int (&qrel)[2]) {
   using C = Cfg<D>;
   const char* kl = stage;
   const char* vl = stage + C::TILEB;
@@ -186,16 +184,17 @@ __device__ inline void tile_compute(const char* stage, int lane, const bf16x8 (&
   }
 
   // s[kb][qb][i] = score of key 16*kb + 4*lg + i against query column qb of this lane.
+  // Positions are relative to the tile's first query: key kk sits at krel + kk,
+  // the lane's query rows at qrel[qb].
   if (need_mask) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int kk = 16 * kb + 4 * lg + i;
-        const int64_t kp = kpos0 + kk;
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
-          if (kk >= n_valid || (causal && kp > qpos[qb])) s[kb][qb][i] = -INFINITY;
+          if (kk >= n_valid || (causal && krel + kk > qrel[qb])) s[kb][qb][i] = -INFINITY;
       }
   }
 
@@ -277,9 +276,10 @@ __device__ inline int seg_effective(const Seg& s, const QSide& qs, const RowCtx&
   return (int)min((int64_t)s.n, lim);
 }
 
-// The per-lane row bookkeeping shared by every kernel.
+// The per-lane row bookkeeping shared by every kernel.  Cheap to recompute,
+// so the kernels rebuild it after the key loop instead of keeping it live.
 struct LaneRows {
-  int64_t qpos[2];
+  int qrel[2];       // query position minus the tile's first query position
   int64_t srow[2];   // state row t*Hq + h
   bool valid[2];
   const uint16_t* qptr[2];
@@ -287,6 +287,7 @@ struct LaneRows {
 
 __device__ inline LaneRows lane_rows(const QSide& qs, const RowCtx& rc, int wave, int lane) {
   LaneRows lr;
+  const int t0 = rc.f0 / qs.G;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     int f = rc.f0 + wave * 32 + qb * 16 + (lane & 15);
@@ -295,7 +296,7 @@ __device__ inline LaneRows lane_rows(const QSide& qs, const RowCtx& rc, int wave
     int t = fc / qs.G;
     int j = fc - t * qs.G;
     int h = rc.g * qs.G + j;
-    lr.qpos[qb] = qs.q_pos0 + t;
+    lr.qrel[qb] = t - t0;
     lr.srow[qb] = (int64_t)t * qs.Hq + h;
     lr.qptr[qb] = (const uint16_t*)qs.q + (int64_t)t * qs.qs_t + (int64_t)h * qs.qs_h;
   }
@@ -362,55 +363,90 @@ __device__ inline void store_acc(Acc<D>& acc, const LaneRows& lr, int lane, floa
   }
 }
 
-// The key-tile loop over a list of segments, double-buffered through LDS.
-template <int D, class GetSeg>
+// Wait until at most `ahead` tiles' loads of this wave are still in flight
+// (loads complete in issue order, so the oldest tile is then in LDS).
+template <int D>
+__device__ inline void wait_tiles_ahead(int ahead) {
+  constexpr int LPT = 2 * Cfg<D>::LPW;  // loads per tile per wave
+  if (ahead <= 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else if (LPT == 8) {
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  }
+}
+
+// The key-tile loop over a list of segments.  NST LDS stages: up to NST - 1
+// tiles are loading while one is multiplied.  One barrier per tile: after it,
+// every wave's loads of the tile about to be used have landed and every wave
+// is done with the stage the next load overwrites.
+template <int D, int NST, class GetSeg>
 __device__ inline void run_segments(const QSide& qs, const RowCtx& rc, const LaneRows& lr, int n_seg,
                                     GetSeg get_seg, const bf16x8 (&qf)[2][Cfg<D>::DC], Acc<D>& acc,
                                     char* lds, bool wave_active) {
   using C = Cfg<D>;
+  static_assert(NST == 2 || NST == 3, "two or three stages");
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 
-  // cursor: segment index, key offset, effective key count of that segment
-  int cs = 0, ck = 0, cn = 0;
-  auto seek = [&](int& s_i, int& k_o, int& n_e) {
-    while (s_i < n_seg) {
-      n_e = seg_effective(get_seg(s_i), qs, rc);
-      if (k_o < n_e) return;
-      ++s_i;
-      k_o = 0;
+  // Cursors over (segment, key offset): skip segments no row of the tile can see.
+  struct Cur {
+    int s, k, n;  // segment, key offset, effective key count of the segment
+  };
+  auto seek = [&](Cur& c) {
+    while (c.s < n_seg) {
+      c.n = seg_effective(get_seg(c.s), qs, rc);
+      if (c.k < c.n) return;
+      ++c.s;
+      c.k = 0;
     }
   };
-  seek(cs, ck, cn);
-  if (cs >= n_seg) return;
+  Cur ci{0, 0, 0};
+  seek(ci);
+  if (ci.s >= n_seg) return;
+  Cur cc = ci;  // next tile to compute
+  KVSrc isrc = make_src<D>(get_seg(ci.s), rc.g);
+  int issue_seg = ci.s;
+  int issued = 0, computed = 0;
 
-  KVSrc src = make_src<D>(get_seg(cs), rc.g);
-  issue_tile<D>(src, ck, min(kTileKeys, cn - ck), lds, wave, lane);
-  wait_tile_loads();
-  __syncthreads();
-  int buf = 0;
-  while (cs < n_seg) {
-    int ns = cs, nk = ck + kTileKeys, nn = cn;
-    seek(ns, nk, nn);
-    const bool has_next = ns < n_seg;
-    const int n_valid = min(kTileKeys, cn - ck);
-    const int64_t kpos0 = src.pos0 + ck;
-    if (has_next) {
-      if (ns != cs) src = make_src<D>(get_seg(ns), rc.g);
-      issue_tile<D>(src, nk, min(kTileKeys, nn - nk), lds + (buf ^ 1) * C::STAGEB, wave, lane);
+  auto issue_next = [&]() {
+    if (ci.s != issue_seg) {
+      isrc = make_src<D>(get_seg(ci.s), rc.g);
+      issue_seg = ci.s;
     }
-    if (wave_active) {
-      const bool need_mask = (n_valid < kTileKeys) || (qs.causal && kpos0 + kTileKeys - 1 > rc.qpos_min);
-      tile_compute<D>(lds + buf * C::STAGEB, lane, qf, acc, qs.c, need_mask, qs.causal != 0, n_valid, kpos0,
-                      lr.qpos);
-    }
-    wait_tile_loads();
+    issue_tile<D>(isrc, ci.k, min(kTileKeys, ci.n - ci.k), lds + (issued % NST) * C::STAGEB, wave, lane);
+    ++issued;
+    ci.k += kTileKeys;
+    seek(ci);
+  };
+
+#pragma unroll
+  for (int p = 0; p < NST - 1; ++p)
+    if (ci.s < n_seg) issue_next();
+
+  while (cc.s < n_seg) {
+    wait_tiles_ahead<D>(issued - computed - 1);
     __syncthreads();
-    buf ^= 1;
-    cs = ns;
-    ck = nk;
-    cn = nn;
+    if (ci.s < n_seg) issue_next();
+    if (wave_active) {
+      const Seg& sg = get_seg(cc.s);
+      const int n_valid = min(kTileKeys, cc.n - cc.k);
+      const int64_t kpos0 = sg.pos0 + cc.k;
+      const bool need_mask = (n_valid < kTileKeys) || (qs.causal && kpos0 + kTileKeys - 1 > rc.qpos_min);
+      // Visited keys satisfy kpos0 <= qpos_max, so the offset fits easily in 32 bits
+      // whenever a mask is needed; far-past tiles are clamped (never masked).
+      const int64_t krel64 = kpos0 - rc.qpos_min;
+      const int krel = (int)max((int64_t)-(1 << 30), min((int64_t)(1 << 30), krel64));
+      tile_compute<D>(lds + (computed % NST) * C::STAGEB, lane, qf, acc, qs.c, need_mask, qs.causal != 0,
+                      n_valid, krel, lr.qrel);
+    }
+    ++computed;
+    cc.k += kTileKeys;
+    seek(cc);
   }
+  // Leave no load in flight into LDS that a later phase might reuse.
+  wait_tiles_ahead<D>(0);
 }
 
 __device__ inline RowCtx make_rowctx(const QSide& qs, int f0, int f1, int g) {
@@ -446,14 +482,45 @@ __global__ __launch_bounds__(kThreads, 2) void walk_kernel(WalkArgs a) {
   else
     load_acc<D>(acc, lr, lane, a.m, a.l, a.o);
 
-  run_segments<D>(a.qs, rc, lr, a.n_seg, [&](int i) -> const Seg& { return a.seg[i]; }, qf, acc, lds,
-                  wave_active);
-  store_acc<D>(acc, lr, lane, a.m, a.l, a.o, 0);
+  run_segments<D, 2>(a.qs, rc, lr, a.n_seg, [&](int i) -> const Seg& { return a.seg[i]; }, qf, acc, lds,
+                     wave_active);
+  store_acc<D>(acc, lane_rows(a.qs, rc, wave, lane), lane, a.m, a.l, a.o, 0);
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void split_kernel(SplitArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * Cfg<D>::STAGEB];
+// Chunk `chunk` of the segment table as a segment of its own.
+__device__ inline Seg chunk_seg(const Seg* seg, int n_seg, const int32_t* chunk_begin, int chunk_len, int chunk) {
+  int s_i = 0;
+  while (s_i + 1 < n_seg && chunk_begin[s_i + 1] <= chunk) ++s_i;
+  const Seg& base = seg[s_i];
+  const int k_off = (chunk - chunk_begin[s_i]) * chunk_len;
+  Seg cs = base;
+  cs.k = (const uint16_t*)base.k + (int64_t)k_off * base.ks_t;
+  cs.v = (const uint16_t*)base.v + (int64_t)k_off * base.vs_t;
+  cs.pos0 = base.pos0 + k_off;
+  cs.n = min(chunk_len, base.n - k_off);
+  return cs;
+}
+
+// Partial state of one row tile over one key range, written to a workspace slot.
+template <int D, int NST>
+__device__ inline void partial_job(const QSide& qs, int f0, int f1, int g, const Seg& sg, float* ws_m,
+                                   float* ws_l, float* ws_o, int64_t row_base, char* lds) {
+  const RowCtx rc = make_rowctx(qs, f0, f1, g);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const LaneRows lr = lane_rows(qs, rc, wave, lane);
+  const bool wave_active = f0 + wave * 32 < f1;
+  bf16x8 qf[2][Cfg<D>::DC];
+  load_q<D>(lr, lane, qf);
+  Acc<D> acc;
+  init_acc<D>(acc);
+  run_segments<D, NST>(qs, rc, lr, 1, [&](int) -> const Seg& { return sg; }, qf, acc, lds, wave_active);
+  store_acc<D>(acc, lane_rows(qs, rc, wave, lane), lane, ws_m, ws_l, ws_o, row_base);
+}
+
+template <int D, int NST>
+__global__ __launch_bounds__(kThreads, NST == 2 ? 2 : 1) void split_kernel(SplitArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[NST * Cfg<D>::STAGEB];
   const int Hkv = a.qs.Hkv;
   const int g = blockIdx.x % Hkv;
   const int tile = blockIdx.x / Hkv;
@@ -461,60 +528,60 @@ __global__ __launch_bounds__(kThreads, 2) void split_kernel(SplitArgs a) {
   const int total = a.qs.q_len * a.qs.G;
   const int f0 = tile * kTileRows;
   const int f1 = min(f0 + kTileRows, total);
-  const RowCtx rc = make_rowctx(a.qs, f0, f1, g);
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const LaneRows lr = lane_rows(a.qs, rc, wave, lane);
-  const bool wave_active = f0 + wave * 32 < f1;
-
-  int s_i = 0;
-  while (s_i + 1 < a.n_seg && a.chunk_begin[s_i + 1] <= chunk) ++s_i;
-  const Seg& base = a.seg[s_i];
-  const int k_off = (chunk - a.chunk_begin[s_i]) * a.chunk_len;
-  Seg cs = base;
-  cs.k = (const uint16_t*)base.k + (int64_t)k_off * base.ks_t;
-  cs.v = (const uint16_t*)base.v + (int64_t)k_off * base.vs_t;
-  cs.pos0 = base.pos0 + k_off;
-  cs.n = min(a.chunk_len, base.n - k_off);
-
-  bf16x8 qf[2][Cfg<D>::DC];
-  load_q<D>(lr, lane, qf);
-  Acc<D> acc;
-  init_acc<D>(acc);
-  run_segments<D>(a.qs, rc, lr, 1, [&](int) -> const Seg& { return cs; }, qf, acc, lds, wave_active);
-  store_acc<D>(acc, lr, lane, a.ws_m, a.ws_l, a.ws_o, (int64_t)chunk * a.R);
+  const Seg cs = chunk_seg(a.seg, a.n_seg, a.chunk_begin, a.chunk_len, chunk);
+  partial_job<D, NST>(a.qs, f0, f1, g, cs, a.ws_m, a.ws_l, a.ws_o, (int64_t)chunk * a.R, lds);
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void suffix_kernel(SuffixArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * Cfg<D>::STAGEB];
+// Shared-prefix fan-out decode, one launch for both job kinds ("AHBM Agentic
+// Runtime Architecture" s.3.2-3.4): jobs [0, n_prefix_jobs) are (row tile,
+// KV head, prefix chunk) -- every branch's rows of a KV head against one chunk
+// of the shared prefix, written to slot `chunk`; the remaining jobs are
+// (branch, KV head) -- that branch's rows against its private suffix, written
+// to slot `suffix_slot`.
+template <int D, int NST>
+__global__ __launch_bounds__(kThreads, NST == 2 ? 2 : 1) void fanout_kernel(FanoutArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[NST * Cfg<D>::STAGEB];
   const int Hkv = a.qs.Hkv;
-  const int g = blockIdx.x % Hkv;
-  const int b = blockIdx.x / Hkv;
   const int G = a.qs.G;
-  const RowCtx rc = make_rowctx(a.qs, b * G, b * G + G, g);
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const LaneRows lr = lane_rows(a.qs, rc, wave, lane);
-  const bool wave_active = wave * 32 < G;
-
-  Seg s;
-  const int64_t tok = (int64_t)Hkv * D;
-  s.k = (const uint16_t*)a.sk + (int64_t)b * a.S * tok;
-  s.v = (const uint16_t*)a.sv + (int64_t)b * a.S * tok;
-  s.ks_t = tok;
-  s.vs_t = tok;
-  s.ks_h = D;
-  s.vs_h = D;
-  s.pos0 = 0;
-  s.n = a.S;
-
-  bf16x8 qf[2][Cfg<D>::DC];
-  load_q<D>(lr, lane, qf);
-  Acc<D> acc;
-  init_acc<D>(acc);
-  run_segments<D>(a.qs, rc, lr, 1, [&](int) -> const Seg& { return s; }, qf, acc, lds, wave_active);
-  store_acc<D>(acc, lr, lane, a.ws_m, a.ws_l, a.ws_o, (int64_t)a.slot * a.R);
+  const int total = a.qs.q_len * G;
+  const int xs = a.row_tiles * Hkv;
+  const int n_prefix_jobs = xs * a.n_chunks;
+  const int id = blockIdx.x;
+  int f0, f1, g;
+  int64_t slot;
+  Seg sg;
+  if (id < n_prefix_jobs) {
+    const int x = id % xs;
+    const int chunk = id / xs;
+    g = x % Hkv;
+    f0 = (x / Hkv) * kTileRows;
+    f1 = min(f0 + kTileRows, total);
+    const int k_off = chunk * a.chunk_len;
+    sg = a.prefix;
+    sg.k = (const uint16_t*)sg.k + (int64_t)k_off * sg.ks_t;
+    sg.v = (const uint16_t*)sg.v + (int64_t)k_off * sg.vs_t;
+    sg.pos0 = k_off;
+    sg.n = min(a.chunk_len, a.prefix.n - k_off);
+    slot = chunk;
+  } else {
+    const int j = id - n_prefix_jobs;
+    const int b = j / Hkv;
+    const int64_t tok = (int64_t)Hkv * D;
+    g = j % Hkv;
+    f0 = b * G;
+    f1 = f0 + G;
+    sg.k = (const uint16_t*)a.sk + (int64_t)b * a.S * tok;
+    sg.v = (const uint16_t*)a.sv + (int64_t)b * a.S * tok;
+    sg.ks_t = tok;
+    sg.vs_t = tok;
+    sg.ks_h = D;
+    sg.vs_h = D;
+    sg.pos0 = 0;
+    sg.n = a.S;
+    sg.pad_ = 0;
+    slot = a.suffix_slot;
+  }
+  partial_job<D, NST>(a.qs, f0, f1, g, sg, a.ws_m, a.ws_l, a.ws_o, slot * a.R, lds);
 }
 
 }  // namespace
@@ -533,18 +600,18 @@ hipError_t launch_split_bf16(const SplitArgs& a, int n_chunks, int D, hipStream_
   const int tiles = (a.qs.q_len * a.qs.G + kTileRows - 1) / kTileRows;
   dim3 grid(tiles * a.qs.Hkv, n_chunks);
   if (D == 128)
-    hipLaunchKernelGGL(split_kernel<128>, grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((split_kernel<128, kSplitStages>), grid, dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(split_kernel<64>, grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((split_kernel<64, kSplitStages>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_suffix_bf16(const SuffixArgs& a, int n_branches, int D, hipStream_t s) {
-  dim3 grid(n_branches * a.qs.Hkv);
+hipError_t launch_fanout_bf16(const FanoutArgs& a, int n_jobs, int D, hipStream_t s) {
+  dim3 grid(n_jobs);
   if (D == 128)
-    hipLaunchKernelGGL(suffix_kernel<128>, grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((fanout_kernel<128, kFanoutStages>), grid, dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(suffix_kernel<64>, grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((fanout_kernel<64, kFanoutStages>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -67,14 +67,21 @@ struct SplitArgs {
   Seg seg[kMaxSeg];
 };
 
-// Fan-out suffix jobs: job (b, g) owns flat rows [b*G, b*G + G) of KV head g and
-// the keys of branch b's private suffix; writes slot `slot` of the workspace.
-struct SuffixArgs {
-  QSide qs;
+// Fan-out decode: one launch of prefix-chunk jobs and branch-suffix jobs.
+// Prefix job (row tile, KV head g, chunk c): flat rows of the tile against
+// prefix keys [c * chunk_len, ...), written to workspace slot c.  Suffix job
+// (branch b, KV head g): flat rows [b*G, b*G + G) against branch b's suffix
+// (suffix k/v are [n_branches, S, Hkv, D]), written to slot suffix_slot.
+struct FanoutArgs {
+  QSide qs;          // q_len = n_branches, non-causal
+  Seg prefix;        // the whole shared prefix
+  int32_t row_tiles;
+  int32_t chunk_len;
+  int32_t n_chunks;
   const void* sk;
   const void* sv;
-  int32_t S;       // suffix keys per branch
-  int32_t slot;
+  int32_t S;
+  int32_t suffix_slot;
   float* ws_m;
   float* ws_l;
   float* ws_o;
@@ -124,9 +131,26 @@ struct FinalizeArgs {
 // Rows per workgroup tile of the bf16 attention kernels.
 constexpr int kTileRows = 128;
 
+// LDS stages (tiles loading while one is multiplied, plus one) of the
+// key-split and fan-out kernels.  Tuning constants: 2 stages fit two
+// workgroups per compute unit, 3 stages one.
+#ifndef BA_SPLIT_STAGES
+#define BA_SPLIT_STAGES 2
+#endif
+#ifndef BA_FANOUT_STAGES
+#define BA_FANOUT_STAGES 2
+#endif
+constexpr int kSplitStages = BA_SPLIT_STAGES;
+constexpr int kFanoutStages = BA_FANOUT_STAGES;
+// Workgroups the fan-out planner aims for (prefix-chunk jobs plus suffix jobs).
+#ifndef BA_FANOUT_TARGET_WG
+#define BA_FANOUT_TARGET_WG 512
+#endif
+constexpr int kFanoutTargetWorkgroups = BA_FANOUT_TARGET_WG;
+
 hipError_t launch_walk_bf16(const WalkArgs& a, int D, hipStream_t s);
 hipError_t launch_split_bf16(const SplitArgs& a, int n_chunks, int D, hipStream_t s);
-hipError_t launch_suffix_bf16(const SuffixArgs& a, int n_branches, int D, hipStream_t s);
+hipError_t launch_fanout_bf16(const FanoutArgs& a, int n_jobs, int D, hipStream_t s);
 hipError_t launch_walk_f32(const WalkArgs& a, int D, hipStream_t s);
 hipError_t launch_merge_groups(const MergeGroupArgs& a, int D, hipStream_t s);
 hipError_t launch_merge_ptrs(const MergePtrArgs& a, int D, hipStream_t s);
