@@ -29,6 +29,9 @@ HIPCC_FLAGS = [
     "-Wall",
     "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # No kernel input or intermediate is NaN by construction (infinities are
+    # used and kept); this lets fmaxf map to v_max/v_max3 without canonicalising.
+    "-fno-honor-nans",
 ]
 
 

@@ -14,7 +14,8 @@
 //    Architecture" s.1.3: rows batched against shared KV).
 //  * K/V tiles of 64 keys go HBM -> LDS with buffer_load_dwordx4 ... lds (no
 //    register staging), double-buffered: the next tile's loads are in flight
-//    while the current one is multiplied.  16-byte chunks of every LDS row are
+//    while the current one is multiplied (two LDS stages of 32 KiB fit two
+//    workgroups per compute unit; a deeper third stage measured slower).  16-byte chunks of every LDS row are
 //    XOR-swizzled by row so both operand reads below are bank-conflict free.
 //  * Each wave owns 32 rows.  Scores are formed transposed, S^T = K Q^T, with
 //    v_mfma_f32_16x16x32_bf16: K (ds_read_b128 from LDS) is the A operand and
@@ -43,7 +44,9 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 
 constexpr int kThreads = 256;
 constexpr int kTileKeys = 64;
@@ -67,23 +70,51 @@ __device__ inline int swz_k(int row) { return D == 128 ? (row & 15) : (row & 7);
 template <int D>
 __device__ inline int swz_v(int row) { return D == 128 ? ((row & 7) << 1) : ((row & 3) << 1); }
 
-__device__ inline float wave_max_cols(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+// Reductions over the 4 lanes that share lane % 16 (one query column).
+//
+// v_permlane16_swap(a, b) returns (a with its odd 16-lane rows replaced by
+// b's even rows, b with its even rows replaced by a's odd rows); with a = b = x
+// the two results hold x and its lane ^ 16 partner, so combining them is one
+// butterfly step, and v_permlane32_swap likewise pairs lane ^ 32 (checked on
+// the hardware).  Registers only, no LDS crossbar.  (The two results are
+// copied to scalars before the bit casts: a bit cast applied directly to an
+// element of the returned vector reads element 0 with this compiler.)
+struct PairF {
+  float a, b;
+};
+__device__ inline PairF swap16(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  return PairF{__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1)};
 }
-
-__device__ inline float wave_sum_cols(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+__device__ inline PairF swap32(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  return PairF{__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1)};
 }
+__device__ inline float xor16_pair_max(float x) { const PairF p = swap16(x); return fmaxf(p.a, p.b); }
+__device__ inline float xor32_pair_max(float x) { const PairF p = swap32(x); return fmaxf(p.a, p.b); }
+__device__ inline float xor16_pair_sum(float x) { const PairF p = swap16(x); return p.a + p.b; }
+__device__ inline float xor32_pair_sum(float x) { const PairF p = swap32(x); return p.a + p.b; }
+__device__ inline float wave_max_cols(float x) { return xor32_pair_max(xor16_pair_max(x)); }
+__device__ inline float wave_sum_cols(float x) { return xor32_pair_sum(xor16_pair_sum(x)); }
 
-__device__ inline unsigned pack_bf16x2(float a, float b) {
-  __bf16 x = (__bf16)a;
-  __bf16 y = (__bf16)b;
-  return (unsigned)__builtin_bit_cast(unsigned short, x) |
-         ((unsigned)__builtin_bit_cast(unsigned short, y) << 16);
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to a packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32).
+__device__ inline bf16x2 pack_bf16x2(float a, float b) { return __builtin_convertvector(f32x2{a, b}, bf16x2); }
+
+// One 16-byte-per-lane buffer load straight into LDS (buffer_load_dwordx4 ...
+// lds): lane i's bytes land at dst + 16 * i.  The host compilation pass never
+// runs device code but rejects this builtin in some template contexts, so the
+// call is compiled for the device only.
+__device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t dst, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(size_t)dst, 16, voff, soff, 0, 0);
+#endif
 }
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -130,38 +161,57 @@ __device__ inline KVSrc make_src(const Seg& s, int g) {
   return r;
 }
 
-// Issue the HBM -> LDS loads of keys [k0, k0 + n_valid) of `src` into one stage.
-// Rows past n_valid repeat the last valid key (their scores are masked).  Each
-// wave-wide load moves RPI whole rows; lane (row r, chunk position p) fetches
-// the global chunk p ^ swizzle(r), which is where operand reads look for it.
+// Per-lane byte offsets, within a tile, of the 16-byte chunks this lane moves:
+// wave-wide load j carries RPI whole rows; lane (row r, chunk position p)
+// fetches the global chunk p ^ swizzle(r), which is where the operand reads
+// look for it.  They depend only on the key strides, so they are computed once
+// per segment.
 template <int D>
-__device__ inline void issue_tile(const KVSrc& src, int k0, int n_valid, char* stage, int wave, int lane) {
+struct LaneOffs {
+  uint32_t k[Cfg<D>::LPW];
+  uint32_t v[Cfg<D>::LPW];
+};
+
+template <int D>
+__device__ inline LaneOffs<D> lane_offsets(const KVSrc& src, int wave, int lane) {
   using C = Cfg<D>;
+  LaneOffs<D> o;
   const int rsub = lane / C::CPR;
   const int p = lane % C::CPR;
+#pragma unroll
+  for (int j = 0; j < C::LPW; ++j) {
+    const int row = (wave * C::LPW + j) * C::RPI + rsub;
+    o.k[j] = (uint32_t)row * src.kst + (uint32_t)((p ^ swz_k<D>(row)) * 16);
+    o.v[j] = (uint32_t)row * src.vst + (uint32_t)((p ^ swz_v<D>(row)) * 16);
+  }
+  return o;
+}
+
+// Issue the HBM -> LDS loads of the 64-key tile starting at key k0 of `src`.
+// Keys past the end of the range read as zeros (buffer range check); their
+// scores are masked, so their P is exactly 0.
+// `stage` is the LDS byte address of the stage.
+template <int D>
+__device__ inline void issue_tile(const KVSrc& src, const LaneOffs<D>& offs, int k0, uint32_t stage, int wave) {
+  using C = Cfg<D>;
   const uint32_t soff_k = (uint32_t)k0 * src.kst;
   const uint32_t soff_v = (uint32_t)k0 * src.vst;
 #pragma unroll
   for (int j = 0; j < C::LPW; ++j) {
-    const int rbase = (wave * C::LPW + j) * C::RPI;
-    const int row = rbase + rsub;
-    const int rr = min(row, n_valid - 1);
-    const uint32_t vk = (uint32_t)rr * src.kst + (uint32_t)((p ^ swz_k<D>(row)) * 16);
-    const uint32_t vv = (uint32_t)rr * src.vst + (uint32_t)((p ^ swz_v<D>(row)) * 16);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, (lds_void*)(stage + rbase * C::ROWB), 16, vk, soff_k, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.v, (lds_void*)(stage + C::TILEB + rbase * C::ROWB), 16, vv,
-                                             soff_v, 0, 0);
+    const uint32_t rbase = (uint32_t)((wave * C::LPW + j) * C::RPI);
+    lds_dma16(src.k, stage + rbase * C::ROWB, offs.k[j], soff_k);
+    lds_dma16(src.v, stage + C::TILEB + rbase * C::ROWB, offs.v[j], soff_v);
   }
 }
 
 // One 64-key tile for one wave: S^T = K Q^T, online-softmax update, O^T += V^T P^T.
 template <int D>
-__device__ inline void tile_compute(const char* stage, int lane, const bf16x8 (&qf)[2][Cfg<D>::DC],
+__device__ inline void tile_compute(const lds_char* stage, int lane, const bf16x8 (&qf)[2][Cfg<D>::DC],
                                     Acc<D>& acc, float c, bool need_mask, bool causal, int n_valid,
                                     int krel, const int (&qrel)[2]) {
   using C = Cfg<D>;
-  const char* kl = stage;
-  const char* vl = stage + C::TILEB;
+  const lds_char* kl = stage;
+  const lds_char* vl = stage + C::TILEB;
   const int lr = lane & 15;
   const int lg = lane >> 4;
 
@@ -176,7 +226,7 @@ __device__ inline void tile_compute(const char* stage, int lane, const bf16x8 (&
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int row = 16 * kb + lr;
-      const bf16x8 kf = *(const bf16x8*)(kl + row * C::ROWB + (((4 * dc + lg) ^ swz_k<D>(row)) * 16));
+      const bf16x8 kf = *(const lds_bf16x8*)(kl + row * C::ROWB + (((4 * dc + lg) ^ swz_k<D>(row)) * 16));
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
         s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][dc], s[kb][qb], 0, 0, 0);
@@ -221,24 +271,26 @@ __device__ inline void tile_compute(const char* stage, int lane, const bf16x8 (&
     }
     const float base = (acc.m2[qb] == -INFINITY) ? 0.f : acc.m2[qb];
     float p[4][4];
-    float sum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][i], c, -base));
-        sum += p[kb][i];
-      }
-    acc.lp[qb] += sum;
+      for (int i = 0; i < 4; ++i) p[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][i], c, -base));
+    // P is rounded to bf16 once; the denominator sums exactly the values PV
+    // multiplies (two per v_dot2c_f32_bf16 against (1, 1), fp32 accumulation).
+    const bf16x2 ones = bf16x2{(__bf16)1.0f, (__bf16)1.0f};
+    float sum = 0.f;
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch) {
-      u32x4 w;
+      bf16x2 w[4];
       w[0] = pack_bf16x2(p[2 * ch][0], p[2 * ch][1]);
       w[1] = pack_bf16x2(p[2 * ch][2], p[2 * ch][3]);
       w[2] = pack_bf16x2(p[2 * ch + 1][0], p[2 * ch + 1][1]);
       w[3] = pack_bf16x2(p[2 * ch + 1][2], p[2 * ch + 1][3]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sum = __builtin_amdgcn_fdot2_f32_bf16(w[u], ones, sum, false);
       pf[ch][qb] = __builtin_bit_cast(bf16x8, w);
     }
+    acc.lp[qb] += sum;
   }
 
   // O^T[d][q] += sum_key V^T[d][key] P^T[key][q].  MFMA k-slot 8*lg + i of key chunk ch
@@ -255,8 +307,8 @@ __device__ inline void tile_compute(const char* stage, int lane, const bf16x8 (&
       const int row1 = row0 + 16;
       const int cidx = 2 * db + ((lr & 3) >> 1);
       const int half = (lr & 1) * 8;
-      const char* a0 = vl + row0 * C::ROWB + ((cidx ^ swz_v<D>(row0)) * 16) + half;
-      const char* a1 = vl + row1 * C::ROWB + ((cidx ^ swz_v<D>(row1)) * 16) + half;
+      const lds_char* a0 = vl + row0 * C::ROWB + ((cidx ^ swz_v<D>(row0)) * 16) + half;
+      const lds_char* a1 = vl + row1 * C::ROWB + ((cidx ^ swz_v<D>(row1)) * 16) + half;
       const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a0);
       const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a1);
       const s16x8 xx = s16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
@@ -363,90 +415,90 @@ __device__ inline void store_acc(Acc<D>& acc, const LaneRows& lr, int lane, floa
   }
 }
 
-// Wait until at most `ahead` tiles' loads of this wave are still in flight
-// (loads complete in issue order, so the oldest tile is then in LDS).
-template <int D>
-__device__ inline void wait_tiles_ahead(int ahead) {
-  constexpr int LPT = 2 * Cfg<D>::LPW;  // loads per tile per wave
-  if (ahead <= 0) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  } else if (LPT == 8) {
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  }
-}
+__device__ inline void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// The key-tile loop over a list of segments.  NST LDS stages: up to NST - 1
-// tiles are loading while one is multiplied.  One barrier per tile: after it,
-// every wave's loads of the tile about to be used have landed and every wave
-// is done with the stage the next load overwrites.
-template <int D, int NST, class GetSeg>
+// The key-tile loop over a list of segments, double-buffered through LDS: the
+// next tile loads while the current one is multiplied.  One barrier per tile:
+// after it, every wave's loads of the tile about to be used have landed and
+// every wave is done with the stage the next load overwrites.  The loop is
+// unrolled by two so each stage's LDS offsets are compile-time constants.
+// Segment bookkeeping (visible key count, buffer resources, per-lane offsets)
+// runs only when a cursor crosses into another segment.
+template <int D, class GetSeg>
 __device__ inline void run_segments(const QSide& qs, const RowCtx& rc, const LaneRows& lr, int n_seg,
                                     GetSeg get_seg, const bf16x8 (&qf)[2][Cfg<D>::DC], Acc<D>& acc,
-                                    char* lds, bool wave_active) {
+                                    lds_char* lds, bool wave_active) {
   using C = Cfg<D>;
-  static_assert(NST == 2 || NST == 3, "two or three stages");
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  // Cursors over (segment, key offset): skip segments no row of the tile can see.
-  struct Cur {
-    int s, k, n;  // segment, key offset, effective key count of the segment
+  // First segment at or after s with a key some row of the tile can see.
+  auto next_nonempty = [&](int s, int& n_eff) {
+    for (; s < n_seg; ++s) {
+      n_eff = seg_effective(get_seg(s), qs, rc);
+      if (n_eff > 0) return s;
+    }
+    n_eff = 0;
+    return n_seg;
   };
-  auto seek = [&](Cur& c) {
-    while (c.s < n_seg) {
-      c.n = seg_effective(get_seg(c.s), qs, rc);
-      if (c.k < c.n) return;
-      ++c.s;
-      c.k = 0;
+
+  // issue cursor
+  int is_n = 0;
+  int is = next_nonempty(0, is_n);
+  if (is >= n_seg) return;
+  int ik = 0;
+  KVSrc isrc = make_src<D>(get_seg(is), rc.g);
+  LaneOffs<D> ilo = lane_offsets<D>(isrc, wave, lane);
+  // compute cursor
+  int cs = is, ck = 0, cn = is_n;
+  int64_t cpos0 = get_seg(cs).pos0;
+
+  const uint32_t lds_addr = (uint32_t)(size_t)lds;
+  auto issue_next = [&](int stage_off) {
+    issue_tile<D>(isrc, ilo, ik, lds_addr + (uint32_t)stage_off, wave);
+    ik += kTileKeys;
+    if (ik >= is_n) {
+      is = next_nonempty(is + 1, is_n);
+      ik = 0;
+      if (is < n_seg) {
+        isrc = make_src<D>(get_seg(is), rc.g);
+        ilo = lane_offsets<D>(isrc, wave, lane);
+      }
     }
   };
-  Cur ci{0, 0, 0};
-  seek(ci);
-  if (ci.s >= n_seg) return;
-  Cur cc = ci;  // next tile to compute
-  KVSrc isrc = make_src<D>(get_seg(ci.s), rc.g);
-  int issue_seg = ci.s;
-  int issued = 0, computed = 0;
 
-  auto issue_next = [&]() {
-    if (ci.s != issue_seg) {
-      isrc = make_src<D>(get_seg(ci.s), rc.g);
-      issue_seg = ci.s;
-    }
-    issue_tile<D>(isrc, ci.k, min(kTileKeys, ci.n - ci.k), lds + (issued % NST) * C::STAGEB, wave, lane);
-    ++issued;
-    ci.k += kTileKeys;
-    seek(ci);
-  };
-
-#pragma unroll
-  for (int p = 0; p < NST - 1; ++p)
-    if (ci.s < n_seg) issue_next();
-
-  while (cc.s < n_seg) {
-    wait_tiles_ahead<D>(issued - computed - 1);
+  // One tile: wait for it, let the next one start loading, multiply.
+  auto step = [&](int cur_off, int nxt_off) {
+    wait_all_loads();
     __syncthreads();
-    if (ci.s < n_seg) issue_next();
+    if (is < n_seg) issue_next(nxt_off);
     if (wave_active) {
-      const Seg& sg = get_seg(cc.s);
-      const int n_valid = min(kTileKeys, cc.n - cc.k);
-      const int64_t kpos0 = sg.pos0 + cc.k;
+      const int n_valid = min(kTileKeys, cn - ck);
+      const int64_t kpos0 = cpos0 + ck;
       const bool need_mask = (n_valid < kTileKeys) || (qs.causal && kpos0 + kTileKeys - 1 > rc.qpos_min);
       // Visited keys satisfy kpos0 <= qpos_max, so the offset fits easily in 32 bits
       // whenever a mask is needed; far-past tiles are clamped (never masked).
       const int64_t krel64 = kpos0 - rc.qpos_min;
       const int krel = (int)max((int64_t)-(1 << 30), min((int64_t)(1 << 30), krel64));
-      tile_compute<D>(lds + (computed % NST) * C::STAGEB, lane, qf, acc, qs.c, need_mask, qs.causal != 0,
-                      n_valid, krel, lr.qrel);
+      tile_compute<D>(lds + cur_off, lane, qf, acc, qs.c, need_mask, qs.causal != 0, n_valid, krel, lr.qrel);
     }
-    ++computed;
-    cc.k += kTileKeys;
-    seek(cc);
+    ck += kTileKeys;
+    if (ck >= cn) {
+      cs = next_nonempty(cs + 1, cn);
+      ck = 0;
+      if (cs < n_seg) cpos0 = get_seg(cs).pos0;
+    }
+  };
+
+  issue_next(0);
+  while (true) {
+    step(0, C::STAGEB);
+    if (cs >= n_seg) break;
+    step(C::STAGEB, 0);
+    if (cs >= n_seg) break;
   }
   // Leave no load in flight into LDS that a later phase might reuse.
-  wait_tiles_ahead<D>(0);
+  wait_all_loads();
 }
 
 __device__ inline RowCtx make_rowctx(const QSide& qs, int f0, int f1, int g) {
@@ -470,7 +522,7 @@ __global__ __launch_bounds__(kThreads, 2) void walk_kernel(WalkArgs a) {
   const int f1 = min(f0 + kTileRows, total);
   const RowCtx rc = make_rowctx(a.qs, f0, f1, g);
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const LaneRows lr = lane_rows(a.qs, rc, wave, lane);
   const bool wave_active = f0 + wave * 32 < f1;
 
@@ -482,8 +534,8 @@ __global__ __launch_bounds__(kThreads, 2) void walk_kernel(WalkArgs a) {
   else
     load_acc<D>(acc, lr, lane, a.m, a.l, a.o);
 
-  run_segments<D, 2>(a.qs, rc, lr, a.n_seg, [&](int i) -> const Seg& { return a.seg[i]; }, qf, acc, lds,
-                     wave_active);
+  run_segments<D>(a.qs, rc, lr, a.n_seg, [&](int i) -> const Seg& { return a.seg[i]; }, qf, acc,
+                     (lds_char*)lds, wave_active);
   store_acc<D>(acc, lane_rows(a.qs, rc, wave, lane), lane, a.m, a.l, a.o, 0);
 }
 
@@ -502,25 +554,25 @@ __device__ inline Seg chunk_seg(const Seg* seg, int n_seg, const int32_t* chunk_
 }
 
 // Partial state of one row tile over one key range, written to a workspace slot.
-template <int D, int NST>
+template <int D>
 __device__ inline void partial_job(const QSide& qs, int f0, int f1, int g, const Seg& sg, float* ws_m,
-                                   float* ws_l, float* ws_o, int64_t row_base, char* lds) {
+                                   float* ws_l, float* ws_o, int64_t row_base, lds_char* lds) {
   const RowCtx rc = make_rowctx(qs, f0, f1, g);
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const LaneRows lr = lane_rows(qs, rc, wave, lane);
   const bool wave_active = f0 + wave * 32 < f1;
   bf16x8 qf[2][Cfg<D>::DC];
   load_q<D>(lr, lane, qf);
   Acc<D> acc;
   init_acc<D>(acc);
-  run_segments<D, NST>(qs, rc, lr, 1, [&](int) -> const Seg& { return sg; }, qf, acc, lds, wave_active);
+  run_segments<D>(qs, rc, lr, 1, [&](int) -> const Seg& { return sg; }, qf, acc, lds, wave_active);
   store_acc<D>(acc, lane_rows(qs, rc, wave, lane), lane, ws_m, ws_l, ws_o, row_base);
 }
 
-template <int D, int NST>
-__global__ __launch_bounds__(kThreads, NST == 2 ? 2 : 1) void split_kernel(SplitArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[NST * Cfg<D>::STAGEB];
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void split_kernel(SplitArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[2 * Cfg<D>::STAGEB];
   const int Hkv = a.qs.Hkv;
   const int g = blockIdx.x % Hkv;
   const int tile = blockIdx.x / Hkv;
@@ -529,7 +581,7 @@ __global__ __launch_bounds__(kThreads, NST == 2 ? 2 : 1) void split_kernel(Split
   const int f0 = tile * kTileRows;
   const int f1 = min(f0 + kTileRows, total);
   const Seg cs = chunk_seg(a.seg, a.n_seg, a.chunk_begin, a.chunk_len, chunk);
-  partial_job<D, NST>(a.qs, f0, f1, g, cs, a.ws_m, a.ws_l, a.ws_o, (int64_t)chunk * a.R, lds);
+  partial_job<D>(a.qs, f0, f1, g, cs, a.ws_m, a.ws_l, a.ws_o, (int64_t)chunk * a.R, (lds_char*)lds);
 }
 
 // Shared-prefix fan-out decode, one launch for both job kinds ("AHBM Agentic
@@ -538,9 +590,9 @@ __global__ __launch_bounds__(kThreads, NST == 2 ? 2 : 1) void split_kernel(Split
 // of the shared prefix, written to slot `chunk`; the remaining jobs are
 // (branch, KV head) -- that branch's rows against its private suffix, written
 // to slot `suffix_slot`.
-template <int D, int NST>
-__global__ __launch_bounds__(kThreads, NST == 2 ? 2 : 1) void fanout_kernel(FanoutArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[NST * Cfg<D>::STAGEB];
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void fanout_kernel(FanoutArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[2 * Cfg<D>::STAGEB];
   const int Hkv = a.qs.Hkv;
   const int G = a.qs.G;
   const int total = a.qs.q_len * G;
@@ -581,7 +633,7 @@ __global__ __launch_bounds__(kThreads, NST == 2 ? 2 : 1) void fanout_kernel(Fano
     sg.pad_ = 0;
     slot = a.suffix_slot;
   }
-  partial_job<D, NST>(a.qs, f0, f1, g, sg, a.ws_m, a.ws_l, a.ws_o, slot * a.R, lds);
+  partial_job<D>(a.qs, f0, f1, g, sg, a.ws_m, a.ws_l, a.ws_o, slot * a.R, (lds_char*)lds);
 }
 
 }  // namespace
@@ -600,18 +652,18 @@ hipError_t launch_split_bf16(const SplitArgs& a, int n_chunks, int D, hipStream_
   const int tiles = (a.qs.q_len * a.qs.G + kTileRows - 1) / kTileRows;
   dim3 grid(tiles * a.qs.Hkv, n_chunks);
   if (D == 128)
-    hipLaunchKernelGGL((split_kernel<128, kSplitStages>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((split_kernel<128>), grid, dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((split_kernel<64, kSplitStages>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((split_kernel<64>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_fanout_bf16(const FanoutArgs& a, int n_jobs, int D, hipStream_t s) {
   dim3 grid(n_jobs);
   if (D == 128)
-    hipLaunchKernelGGL((fanout_kernel<128, kFanoutStages>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((fanout_kernel<128>), grid, dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((fanout_kernel<64, kFanoutStages>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((fanout_kernel<64>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -131,17 +131,6 @@ struct FinalizeArgs {
 // Rows per workgroup tile of the bf16 attention kernels.
 constexpr int kTileRows = 128;
 
-// LDS stages (tiles loading while one is multiplied, plus one) of the
-// key-split and fan-out kernels.  Tuning constants: 2 stages fit two
-// workgroups per compute unit, 3 stages one.
-#ifndef BA_SPLIT_STAGES
-#define BA_SPLIT_STAGES 2
-#endif
-#ifndef BA_FANOUT_STAGES
-#define BA_FANOUT_STAGES 2
-#endif
-constexpr int kSplitStages = BA_SPLIT_STAGES;
-constexpr int kFanoutStages = BA_FANOUT_STAGES;
 // Workgroups the fan-out planner aims for (prefix-chunk jobs plus suffix jobs).
 #ifndef BA_FANOUT_TARGET_WG
 #define BA_FANOUT_TARGET_WG 512
