@@ -189,6 +189,7 @@ def bench_fanout(torch, ba, H, w, steps, warmup):
     log(f"fanout: {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
     return {"workload": w.name, "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
             "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": w.bytes(),
+            "traffic_attention_kernel": traffic_record("fanout_kernel_fanout_decode"),
             "timing": "median over steps, HIP events around the call, 1 GiB read between calls evicts the caches"}
 
 
@@ -260,6 +261,19 @@ def bench_merge_scaled(torch, ba, steps, warmup, n_parts=32, rows=131072, D=128)
             "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes}
 
 
+def copy_calibration(torch, steps):
+    """A plain device copy of 1 GiB, repeated: the known-size reference that scales
+    the HBM FETCH_SIZE / WRITE_SIZE counters of the attention kernels."""
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"workload": "device copy of 1 GiB (torch copy_)", "bytes_read_per_copy": n * 4,
+            "bytes_written_per_copy": n * 4, "copies": steps}
+
+
 def cpu_baseline(w, q, k, v, budget_s):
     """The oracle, as it stands, on a bounded sample of query tokens of the headline workload."""
     from threadpoolctl import threadpool_info
@@ -294,7 +308,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="all",
-                    choices=["all", "causal_prefill", "ring_share", "fanout", "shard_merge", "merge_scaled"])
+                    choices=["all", "causal_prefill", "ring_share", "fanout", "shard_merge", "merge_scaled",
+                             "copy_calibration"])
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -324,6 +339,8 @@ def main():
         secondary["shard_merge"] = bench_shard_merge(torch, ba, H, wl.SHARD_MERGE, args.steps, args.warmup)
     if only == "merge_scaled":
         secondary["merge_scaled"] = bench_merge_scaled(torch, ba, args.steps, args.warmup)
+    if only == "copy_calibration":
+        secondary["copy_calibration"] = copy_calibration(torch, args.steps)
     if only not in ("all", "causal_prefill"):
         print(json.dumps({"metric": METRIC, "partial": only, "secondary": secondary}), flush=True)
         return
