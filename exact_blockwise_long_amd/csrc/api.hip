@@ -478,21 +478,36 @@ struct FanoutPlan {
   int row_tiles = 0;   // 128-row tiles of one KV head's rows (n_branches * G)
   int chunk_len = 0;
   int n_chunks = 0;    // prefix chunks
+  int bpj = 1;         // branches per suffix job
   int suffix_jobs = 0;
   int slots = 0;       // workspace partial slots
   int suffix_slot = -1;
   int n_jobs = 0;
 };
 
-// Prefix chunks are sized so that prefix-chunk jobs plus suffix jobs come to
-// about kFanoutTargetWorkgroups: enough to cover every compute unit and hide
-// HBM latency while keeping the partial states (one per chunk and row) small.
+// The launch is sized to about kFanoutTargetWorkgroups jobs that each move
+// about the same number of K/V bytes, so no compute unit idles while others
+// still stream: every job of the decode is bandwidth bound, and a job's time
+// is its bytes over its share of HBM.  A suffix job walks bpj branches' private
+// suffixes of one KV head one after another; a prefix job walks one chunk of
+// the shared prefix for one row tile of a KV head.
 FanoutPlan plan_fanout(const ba_fanout* f) {
   FanoutPlan fp;
   const int G = f->n_q_heads / f->n_kv_heads;
   fp.row_tiles = (int)(((int64_t)f->n_branches * G + ba::kTileRows - 1) / ba::kTileRows);
   const int xs = fp.row_tiles * f->n_kv_heads;
-  fp.suffix_jobs = f->suffix_len > 0 ? f->n_branches * f->n_kv_heads : 0;
+  // Keys each job should walk: all keys read (the prefix once per row tile)
+  // over the target job count.
+  const int64_t keys_total = (int64_t)f->n_kv_heads *
+                             ((int64_t)f->prefix_len * fp.row_tiles + (int64_t)f->n_branches * f->suffix_len);
+  const int64_t per_job = keys_total / ba::kFanoutTargetWorkgroups > 1 ? keys_total / ba::kFanoutTargetWorkgroups : 1;
+  if (f->suffix_len > 0) {
+    int64_t bpj = (per_job + f->suffix_len / 2) / f->suffix_len;
+    if (bpj > f->n_branches) bpj = f->n_branches;
+    if (bpj < 1) bpj = 1;
+    fp.bpj = (int)bpj;
+    fp.suffix_jobs = f->n_kv_heads * (int)((f->n_branches + fp.bpj - 1) / fp.bpj);
+  }
   if (f->prefix_len > 0) {
     int64_t want = (ba::kFanoutTargetWorkgroups - fp.suffix_jobs) / xs;
     if (want < 1) want = 1;
@@ -569,6 +584,7 @@ ba_status fanout_prefix_decode(const ba_fanout* f, const void* q, const void* pr
   a.sv = suffix_v;
   a.S = f->suffix_len;
   a.suffix_slot = fp.suffix_slot;
+  a.bpj = fp.bpj;
   a.ws_m = wm;
   a.ws_l = wl;
   a.ws_o = wo;

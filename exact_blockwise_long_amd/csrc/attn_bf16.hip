@@ -237,15 +237,18 @@ __device__ inline void tile_compute(const lds_char* stage, int lane, const bf16x
   // Positions are relative to the tile's first query: key kk sits at krel + kk,
   // the lane's query rows at qrel[qb].
   if (need_mask) {
+    // Key kk is visible to query column qb iff kk < lim[qb]; with kk = 16*kb + 4*lg + i
+    // that is 16*kb + i < lim[qb] - 4*lg, one compare per score against a constant.
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int qb = 0; qb < 2; ++qb) {
+      const int lim = causal ? min(n_valid, qrel[qb] - krel + 1) : n_valid;
+      const int t = lim - 4 * lg;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kk = 16 * kb + 4 * lg + i;
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          if (kk >= n_valid || (causal && krel + kk > qrel[qb])) s[kb][qb][i] = -INFINITY;
-      }
+        for (int i = 0; i < 4; ++i)
+          if (16 * kb + i >= t) s[kb][qb][i] = -INFINITY;
+    }
   }
 
   bf16x8 pf[2][2];  // [key chunk of 32][qb]
@@ -588,8 +591,8 @@ __global__ __launch_bounds__(kThreads, 2) void split_kernel(SplitArgs a) {
 // Runtime Architecture" s.3.2-3.4): jobs [0, n_prefix_jobs) are (row tile,
 // KV head, prefix chunk) -- every branch's rows of a KV head against one chunk
 // of the shared prefix, written to slot `chunk`; the remaining jobs are
-// (branch, KV head) -- that branch's rows against its private suffix, written
-// to slot `suffix_slot`.
+// (branch group, KV head) -- each branch's rows against its private suffix in
+// turn, written to slot `suffix_slot`.
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void fanout_kernel(FanoutArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[2 * Cfg<D>::STAGEB];
@@ -599,29 +602,29 @@ __global__ __launch_bounds__(kThreads, 2) void fanout_kernel(FanoutArgs a) {
   const int xs = a.row_tiles * Hkv;
   const int n_prefix_jobs = xs * a.n_chunks;
   const int id = blockIdx.x;
-  int f0, f1, g;
-  int64_t slot;
-  Seg sg;
   if (id < n_prefix_jobs) {
     const int x = id % xs;
     const int chunk = id / xs;
-    g = x % Hkv;
-    f0 = (x / Hkv) * kTileRows;
-    f1 = min(f0 + kTileRows, total);
+    const int g = x % Hkv;
+    const int f0 = (x / Hkv) * kTileRows;
+    const int f1 = min(f0 + kTileRows, total);
     const int k_off = chunk * a.chunk_len;
-    sg = a.prefix;
+    Seg sg = a.prefix;
     sg.k = (const uint16_t*)sg.k + (int64_t)k_off * sg.ks_t;
     sg.v = (const uint16_t*)sg.v + (int64_t)k_off * sg.vs_t;
     sg.pos0 = k_off;
     sg.n = min(a.chunk_len, a.prefix.n - k_off);
-    slot = chunk;
-  } else {
-    const int j = id - n_prefix_jobs;
-    const int b = j / Hkv;
-    const int64_t tok = (int64_t)Hkv * D;
-    g = j % Hkv;
-    f0 = b * G;
-    f1 = f0 + G;
+    partial_job<D>(a.qs, f0, f1, g, sg, a.ws_m, a.ws_l, a.ws_o, (int64_t)chunk * a.R, (lds_char*)lds);
+    return;
+  }
+  const int j = id - n_prefix_jobs;
+  const int g = j % Hkv;
+  const int b0 = (j / Hkv) * a.bpj;
+  const int b1 = min(b0 + a.bpj, a.qs.q_len);
+  const int64_t tok = (int64_t)Hkv * D;
+  for (int b = b0; b < b1; ++b) {
+    if (b > b0) __syncthreads();  // every wave is done with the previous branch's LDS tiles
+    Seg sg;
     sg.k = (const uint16_t*)a.sk + (int64_t)b * a.S * tok;
     sg.v = (const uint16_t*)a.sv + (int64_t)b * a.S * tok;
     sg.ks_t = tok;
@@ -631,9 +634,9 @@ __global__ __launch_bounds__(kThreads, 2) void fanout_kernel(FanoutArgs a) {
     sg.pos0 = 0;
     sg.n = a.S;
     sg.pad_ = 0;
-    slot = a.suffix_slot;
+    partial_job<D>(a.qs, b * G, b * G + G, g, sg, a.ws_m, a.ws_l, a.ws_o, (int64_t)a.suffix_slot * a.R,
+                   (lds_char*)lds);
   }
-  partial_job<D>(a.qs, f0, f1, g, sg, a.ws_m, a.ws_l, a.ws_o, slot * a.R, (lds_char*)lds);
 }
 
 }  // namespace

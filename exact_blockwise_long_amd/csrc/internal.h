@@ -70,8 +70,9 @@ struct SplitArgs {
 // Fan-out decode: one launch of prefix-chunk jobs and branch-suffix jobs.
 // Prefix job (row tile, KV head g, chunk c): flat rows of the tile against
 // prefix keys [c * chunk_len, ...), written to workspace slot c.  Suffix job
-// (branch b, KV head g): flat rows [b*G, b*G + G) against branch b's suffix
-// (suffix k/v are [n_branches, S, Hkv, D]), written to slot suffix_slot.
+// (branch group, KV head g): for each branch b of the group (bpj consecutive
+// branches), flat rows [b*G, b*G + G) against branch b's suffix (suffix k/v
+// are [n_branches, S, Hkv, D]), written to slot suffix_slot.
 struct FanoutArgs {
   QSide qs;          // q_len = n_branches, non-causal
   Seg prefix;        // the whole shared prefix
@@ -82,6 +83,7 @@ struct FanoutArgs {
   const void* sv;
   int32_t S;
   int32_t suffix_slot;
+  int32_t bpj;       // branches per suffix job
   float* ws_m;
   float* ws_l;
   float* ws_o;

@@ -308,10 +308,12 @@ def test_shard_states_then_merge():
 
 # ---------------------------------------------------------------- fan-out decode
 
-@pytest.mark.parametrize("P,S", [(1000, 37), (0, 70), (333, 0), (4096, 512)])
-def test_fanout_small(P, S):
-    nb, Hq, Hkv, D = 3, 8, 2, 128
-    announce(f"fanout nb={nb} Hq={Hq} Hkv={Hkv} P={P} S={S} seed 71")
+# The last case plans two branches per suffix job with a ragged last group
+# (131 branches) and two row tiles per KV head (G = 1).
+@pytest.mark.parametrize("nb,Hq,Hkv,D,P,S", [(3, 8, 2, 128, 1000, 37), (3, 8, 2, 128, 0, 70), (3, 8, 2, 128, 333, 0),
+                                             (3, 8, 2, 128, 4096, 512), (131, 8, 8, 64, 100, 40)])
+def test_fanout_small(nb, Hq, Hkv, D, P, S):
+    announce(f"fanout nb={nb} Hq={Hq} Hkv={Hkv} D={D} P={P} S={S} seed 71")
     g = synth.rng(71)
     q = synth.normal(g, (nb, Hq, D), 0.5, "bf16")
     pk = synth.normal(g, (P, Hkv, D), 0.5, "bf16")
