@@ -519,7 +519,8 @@ __global__ __launch_bounds__(kThreads, 2) void walk_kernel(WalkArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[2 * Cfg<D>::STAGEB];
   const int Hkv = a.qs.Hkv;
   const int g = blockIdx.x % Hkv;          // consecutive workgroups land on different XCDs;
-  const int tile = blockIdx.x / Hkv;       // with Hkv = 8 each XCD serves one KV head
+  const int n_tiles = (a.qs.q_len * a.qs.G + kTileRows - 1) / kTileRows;
+  const int tile = n_tiles - 1 - (int)(blockIdx.x / Hkv);  // causal: longest rows first
   const int total = a.qs.q_len * a.qs.G;
   const int f0 = tile * kTileRows;
   const int f1 = min(f0 + kTileRows, total);
