@@ -321,6 +321,58 @@ def bench_merge_scaled(torch, ba, steps, warmup, n_parts=32, rows=131072, D=128)
             "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes}
 
 
+def bench_layouts(torch, ba, H, w, reps):
+    """Load-balanced causal shares ("RingAttention and Context Parallelism", section 5):
+    every device of an n-device causal ring emulated on this GPU, each (device, step)
+    timed with HIP events.  The ring waits for its slowest device at every step, so the
+    critical path is the sum over steps of the slowest device's time; efficiency is the
+    busy time over n times that path."""
+    from exact_blockwise_long_amd import layouts as L
+    log(f"inputs: {w.name}")
+    q, k, v = w.make_inputs()
+    qd, kd, vd = H.to_device(q), H.to_device(k), H.to_device(v)
+    del q, k, v
+    n = w.n_devices
+    res = {"workload": w.name, "n_devices": n, "algorithmic_flops": w.flops(), "layouts": {}}
+    for layout in L.LAYOUTS:
+        calls = []
+        for dev in range(n):
+            c = []
+            L.run_device(ba, torch, layout, qd, kd, vd, n, dev, n_kv_heads=w.n_kv_heads, calls_out=c)
+            calls.append(c)
+        torch.cuda.synchronize()
+        times = np.zeros((reps, n, n))
+        for r in range(reps):
+            ev = []
+            for dev in range(n):
+                for t in range(n):
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for tt, fn in calls[dev]:
+                        if tt == t:
+                            fn()
+                    e1.record()
+                    ev.append((dev, t, e0, e1))
+            torch.cuda.synchronize()
+            for dev, t, e0, e1 in ev:
+                times[r, dev, t] = e0.elapsed_time(e1)
+        tm = np.median(times, axis=0)            # [device, step] ms
+        crit = float(tm.max(axis=0).sum())
+        busy = float(tm.sum())
+        per_dev = tm.sum(axis=1)
+        tf = w.flops() / n / crit / 1e9
+        res["layouts"][layout] = {
+            "critical_path_ms": round(crit, 3), "busy_ms": round(busy, 3),
+            "efficiency": round(busy / (n * crit), 4),
+            "TFLOP/s_per_device": round(tf, 1),
+            "device_ms_min_max": [round(float(per_dev.min()), 3), round(float(per_dev.max()), 3)]}
+        log(f"layout {layout}: critical path {crit:.2f} ms, efficiency {busy / (n * crit):.3f}, "
+            f"{tf:.0f} TFLOP/s per device, device totals {per_dev.min():.2f}..{per_dev.max():.2f} ms")
+    res["timing"] = f"median of {reps} replays; HIP events around each (device, step) group of fwd_block calls"
+    return res
+
+
 def copy_calibration(torch, steps):
     """A plain device copy of 1 GiB, repeated: the known-size reference that scales
     the HBM FETCH_SIZE / WRITE_SIZE counters of the attention kernels."""
@@ -369,7 +421,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="all",
                     choices=["all", "causal_prefill", "ring_share", "fanout", "shard_merge", "merge_scaled",
-                             "copy_calibration"])
+                             "layouts", "copy_calibration"])
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -400,6 +452,8 @@ def main():
         secondary["shard_merge"] = bench_shard_merge(torch, ba, H, wl.SHARD_MERGE, args.steps, args.warmup)
     if only == "merge_scaled":
         secondary["merge_scaled"] = bench_merge_scaled(torch, ba, args.steps, args.warmup)
+    if only == "layouts":
+        secondary["causal_ring_layouts"] = bench_layouts(torch, ba, H, wl.CAUSAL_RING_LAYOUTS, max(1, args.steps // 10))
     if only == "copy_calibration":
         secondary["copy_calibration"] = copy_calibration(torch, args.steps)
     if only not in ("all", "causal_prefill"):
@@ -445,6 +499,7 @@ def main():
         secondary["shard_merge"] = bench_shard_merge(torch, ba, H, wl.SHARD_MERGE, args.steps, args.warmup)
         secondary["merge_scaled"] = bench_merge_scaled(torch, ba, args.steps, args.warmup)
         secondary["ring_share"] = bench_ring_share(torch, ba, H, wl.RING_SHARE, 2, 1)
+        secondary["causal_ring_layouts"] = bench_layouts(torch, ba, H, wl.CAUSAL_RING_LAYOUTS, 2)
     if secondary:
         line["secondary"] = secondary
     if not args.no_cpu:

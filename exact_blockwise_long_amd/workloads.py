@@ -225,4 +225,40 @@ SHARD_MERGE = ShardMergeWorkload(
     name="shard_merge_1m: bf16 D128, 8 branches x 8 heads of one KV group, 1048576 keys in 32 shards, logits ~ +-30",
     n_branches=8, n_q_heads=8, head_dim=128, kv_len=1048576, n_shards=32, seed=5)
 
+@dataclass
+class CausalRingWorkload:
+    """A whole causal sequence sharded over n emulated ring devices in one of
+    the layouts of "RingAttention and Context Parallelism", section 5; every
+    device's ring steps run on the one GPU."""
+
+    name: str
+    seq_len: int
+    n_devices: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    seed: int
+    scale_qkv: float = 0.5
+
+    def pairs(self) -> int:
+        """Causal (query token, key) pairs of the whole sequence, per query head."""
+        return self.seq_len * (self.seq_len + 1) // 2
+
+    def flops(self) -> float:
+        return 4.0 * self.head_dim * self.n_q_heads * self.pairs()
+
+    def make_inputs(self):
+        """(q, k, v) synth.Tensors over the whole sequence: q [S, Hq, D]; k, v [S, Hkv, D]."""
+        g = synth.rng(self.seed)
+        q = synth.normal(g, (self.seq_len, self.n_q_heads, self.head_dim), self.scale_qkv, "bf16")
+        k = synth.normal(g, (self.seq_len, self.n_kv_heads, self.head_dim), self.scale_qkv, "bf16")
+        v = synth.normal(g, (self.seq_len, self.n_kv_heads, self.head_dim), self.scale_qkv, "bf16")
+        return q, k, v
+
+
+CAUSAL_RING_LAYOUTS = CausalRingWorkload(
+    name="causal_ring_32k_8dev: bf16 GQA 64/8 D128, 32768 tokens over 8 emulated devices "
+         "(contiguous / zigzag / striped shards)",
+    seq_len=32768, n_devices=8, n_q_heads=64, n_kv_heads=8, head_dim=128, seed=6)
+
 ALL = [TINY_EXACT, CAUSAL_PREFILL, RING_SHARE, FANOUT_DECODE, SHARD_MERGE]

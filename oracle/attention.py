@@ -285,6 +285,44 @@ def emulate_ring(q_blocks, kv_blocks, scale, causal=False, block_len=None):
     return [finalize(*s) for s in states]
 
 
+# ---------------------------------------------------------------- load-balanced causal shares
+# [RAC] section 5, "Causal Masking and Load Balancing: Striped vs. Zigzag Ring
+# Attention": which tokens device k of n holds.  Each function returns the
+# absolute token indices in the order the device stores them.
+
+def contiguous_tokens(seq_len: int, n: int, k: int) -> np.ndarray:
+    """Naive sequential partitioning: device k holds tokens [k*B, (k+1)*B), B = seq_len / n."""
+    b = seq_len // n
+    return np.arange(k * b, (k + 1) * b)
+
+
+def striped_tokens(seq_len: int, n: int, k: int) -> np.ndarray:
+    """Striped sharding: device k holds every token i with i mod n == k."""
+    return np.array([i for i in range(seq_len) if i % n == k], dtype=np.int64)
+
+
+def zigzag_tokens(seq_len: int, n: int, k: int) -> np.ndarray:
+    """Zigzag sharding: the sequence is cut into 2n equal chunks c_0 .. c_{2n-1};
+    device k holds c_k, then c_{2n-1-k}."""
+    c = seq_len // (2 * n)
+    first = k
+    second = 2 * n - 1 - k
+    return np.concatenate([np.arange(first * c, (first + 1) * c), np.arange(second * c, (second + 1) * c)])
+
+
+def visible_pairs(q_pos, k_pos) -> int:
+    """Number of (query, key) pairs the causal rule keeps: #{(i, j) : k_pos[j] <= q_pos[i]}."""
+    return int(causal_visible(np.asarray(q_pos), np.asarray(k_pos)).sum())
+
+
+def ring_step_pairs(owner, seq_len: int, n: int, k: int, t: int) -> int:
+    """Causal pairs device k computes at ring step t: its query tokens against
+    the K/V tokens of device (k - t) mod n, which it holds at that step
+    ([RAC] section 3 ring schedule; section 5 causal rule)."""
+    src = (k - t) % n
+    return visible_pairs(owner(seq_len, n, k), owner(seq_len, n, src))
+
+
 def fanout_decode(q, prefix_k, prefix_v, suffix_k, suffix_v, scale):
     """Shared-prefix fan-out decode, by definition.
 

@@ -322,6 +322,90 @@ def pin_finalize_empty():
     _close(lse[1], 0.5 + math.log(2.0), 1e-15, 0, "finalize lse")
 
 
+# ---------------------------------------------------------------- load-balanced causal shares
+# [RAC] section 5 (Striped vs. Zigzag Ring Attention).
+
+def pin_zigzag_printed_allocation():
+    """Zigzag ownership equals the page's printed 4-GPU allocation (GPU k holds c_k and c_{2N-1-k})."""
+    g = json.load(open(os.path.join(GOLDEN, "zigzag_allocation_printed.json")))
+    n, c = g["n_devices"], 5
+    S = 2 * n * c
+    for k, chunks in g["chunks_per_device"].items():
+        want = np.concatenate([np.arange(ci * c, (ci + 1) * c) for ci in chunks])
+        got = ora.zigzag_tokens(S, n, int(k))
+        assert np.array_equal(got, want), ("zigzag", k, got, want)
+
+
+def pin_layouts_partition():
+    """Every layout hands each token to exactly one device, S / n tokens each."""
+    for owner in (ora.contiguous_tokens, ora.striped_tokens, ora.zigzag_tokens):
+        for n in (1, 2, 4, 8):
+            S = 16 * n
+            parts = [np.asarray(owner(S, n, k)) for k in range(n)]
+            assert all(len(p) == S // n for p in parts), owner.__name__
+            assert np.array_equal(np.sort(np.concatenate(parts)), np.arange(S)), owner.__name__
+
+
+def pin_layout_pair_counts():
+    """Closed forms of the causal pairs per device and ring step, from the layouts' definitions:
+    contiguous B^2 / B(B+1)/2 / 0 for a block before / at / after the device's own; zigzag
+    2C^2 + C at step 0 and 2C^2 after (equal on every device); striped B(B+1)/2 when the
+    source device index is <= k, else B(B-1)/2.  The totals are the causal triangle S(S+1)/2."""
+    for n in (2, 4, 8):
+        B = 12
+        S, C = n * B, B // 2
+        tot = {}
+        for k in range(n):
+            for t in range(n):
+                src = (k - t) % n
+                cont = ora.ring_step_pairs(ora.contiguous_tokens, S, n, k, t)
+                assert cont == (B * B if src < k else B * (B + 1) // 2 if src == k else 0), ("cont", n, k, t)
+                zz = ora.ring_step_pairs(ora.zigzag_tokens, S, n, k, t)
+                assert zz == (2 * C * C + C if t == 0 else 2 * C * C), ("zigzag", n, k, t)
+                st = ora.ring_step_pairs(ora.striped_tokens, S, n, k, t)
+                assert st == (B * (B + 1) // 2 if src <= k else B * (B - 1) // 2), ("striped", n, k, t)
+                for name, v in (("c", cont), ("z", zz), ("s", st)):
+                    tot[name] = tot.get(name, 0) + v
+        assert all(v == S * (S + 1) // 2 for v in tot.values()), tot
+
+
+def pin_zigzag_ring_exact():
+    """Walking the zigzag ring with the recurrence reproduces plain causal attention
+    (the page's exact causal equivalence)."""
+    rng = _rng(31)
+    n, c, Hq, Hkv, D = 3, 7, 4, 2, 8
+    S = 2 * n * c
+    q = rng.standard_normal((S, Hq, D))
+    k = rng.standard_normal((S, Hkv, D))
+    v = rng.standard_normal((S, Hkv, D))
+    scale = 1.0 / math.sqrt(D)
+    a_ref, _, _, lse_ref = brute_free_attend(q, k, v, scale)
+    for dev in range(n):
+        mine = ora.zigzag_tokens(S, n, dev)
+        st = ora.init_state(len(mine), Hq, D)
+        for t in range(n):
+            src = ora.zigzag_tokens(S, n, (dev - t) % n)
+            st = ora.online_step(st, q[mine], k[src], v[src], scale, mine, src, causal=True)
+        a, lse = ora.finalize(*st)
+        _close(a, a_ref[mine], 0, 1e-12, "zigzag A")
+        _close(lse, lse_ref[mine], 0, 1e-12, "zigzag lse")
+
+
+def brute_free_attend(q, k, v, scale):
+    """Causal attention written out with scipy's softmax (not the oracle's own state code)."""
+    S, Hq, D = q.shape
+    G = Hq // k.shape[1]
+    a = np.zeros_like(q)
+    lse = np.zeros((S, Hq))
+    for h in range(Hq):
+        g = h // G
+        z = scale * (q[:, h, :] @ k[:, g, :].T)
+        z = np.where(np.tril(np.ones((S, S), dtype=bool)), z, -np.inf)
+        a[:, h, :] = scipy.special.softmax(z, axis=1) @ v[:, g, :]
+        lse[:, h] = scipy.special.logsumexp(z, axis=1)
+    return a, None, None, lse
+
+
 ALL_PINS = [
     pin_brute_force_tiny,
     pin_scipy_softmax_logsumexp,
@@ -336,4 +420,8 @@ ALL_PINS = [
     pin_ring_emulation,
     pin_fanout_decode,
     pin_finalize_empty,
+    pin_zigzag_printed_allocation,
+    pin_layouts_partition,
+    pin_layout_pair_counts,
+    pin_zigzag_ring_exact,
 ]

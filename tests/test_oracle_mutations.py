@@ -85,7 +85,24 @@ def _ring_wrong_direction(k, n):
     return [(k + t) % n for t in range(n)]
 
 
+def _zigzag_mirror_off_by_one(seq_len, n, k):
+    c = seq_len // (2 * n)
+    second = (2 * n - k) % (2 * n)
+    return np.concatenate([np.arange(k * c, (k + 1) * c), np.arange(second * c, (second + 1) * c)])
+
+
+def _striped_shifted(seq_len, n, k):
+    return np.array([i for i in range(seq_len) if i % n == (k + 1) % n], dtype=np.int64)
+
+
+def _pairs_strict(q_pos, k_pos):
+    return int((np.asarray(k_pos)[None, :] < np.asarray(q_pos)[:, None]).sum())
+
+
 MUTATIONS = {
+    "zigzag mirror chunk off by one": ("zigzag_tokens", _zigzag_mirror_off_by_one),
+    "striped residue shifted": ("striped_tokens", _striped_shifted),
+    "pair count excludes the diagonal": ("visible_pairs", _pairs_strict),
     "dropped scale": ("scaled_logits", _no_scale),
     "diagonal excluded from causal mask": ("causal_visible", _strict_causal),
     "causal mask reversed": ("causal_visible", _reversed_causal),
