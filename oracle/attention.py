@@ -347,6 +347,35 @@ def fanout_decode(q, prefix_k, prefix_v, suffix_k, suffix_v, scale):
     return a, lse
 
 
+def fanout_prefill(q, prefix_k, prefix_v, suffix_k, suffix_v, scale):
+    """Shared-prefix fan-out over several new tokens per branch, by definition.
+
+    q [nb, T, Hq, D] holds the T newest tokens of each branch; suffix_k/v
+    [nb, S, Hkv, D] are the branch's private tokens, whose last T are those new
+    tokens ([AHBM] 3.1 context structure, 3.2 "20 new tokens per sub-agent",
+    3.6 prefill of the private suffixes).  Branch b's context is the shared
+    prefix followed by its own suffix; positions run 0 .. P + S - 1 in that
+    order, the new token i of the branch sits at P + S - T + i, and the causal
+    rule applies ([RAC] section 5).  Returns (A [nb, T, Hq, D], LSE [nb, T, Hq]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    nb, T = q.shape[:2]
+    P = np.asarray(prefix_k).shape[0]
+    S = np.asarray(suffix_k).shape[1]
+    a = np.empty(q.shape)
+    lse = np.empty(q.shape[:3])
+    for b in range(nb):
+        keys = np.concatenate([np.asarray(prefix_k, dtype=np.float64).reshape(P, *np.asarray(suffix_k).shape[2:]),
+                               np.asarray(suffix_k[b], dtype=np.float64)], axis=0)
+        vals = np.concatenate([np.asarray(prefix_v, dtype=np.float64).reshape(P, *np.asarray(suffix_v).shape[2:]),
+                               np.asarray(suffix_v[b], dtype=np.float64)], axis=0)
+        q_pos = P + S - T + np.arange(T)
+        ab, _, _, lb = attend(q[b], keys, vals, scale, q_pos, np.arange(P + S), causal=True)
+        a[b] = ab
+        lse[b] = lb
+    return a, lse
+
+
 def fanout_state_rows(q, k, v, scale):
     """Partial state of fan-out rows against one KV range (no mask).
 

@@ -315,6 +315,36 @@ def pin_fanout_decode():
         _close(lse[b], LSE[0], 1e-13, 0, "fanout brute lse")
 
 
+def pin_fanout_prefill():
+    """Fan-out prefill: T = 1 is the decode; each new token equals a one-token
+    decode over the suffix cut just after it (pins the causal offset); brute force."""
+    g = _rng(93)
+    nb, T, Hq, Hkv, D, P, S = 2, 3, 4, 2, 8, 9, 5
+    q = g.standard_normal((nb, T, Hq, D))
+    pk = g.standard_normal((P, Hkv, D))
+    pv = g.standard_normal((P, Hkv, D))
+    sk = g.standard_normal((nb, S, Hkv, D))
+    sv = g.standard_normal((nb, S, Hkv, D))
+    s = 1.0 / math.sqrt(D)
+    a, lse = ora.fanout_prefill(q, pk, pv, sk, sv, s)
+    a1, lse1 = ora.fanout_prefill(q[:, -1:], pk, pv, sk, sv, s)
+    ad, lsed = ora.fanout_decode(q[:, -1], pk, pv, sk, sv, s)
+    _close(a1[:, 0], ad, 1e-13, 1e-14, "prefill T=1 vs decode")
+    _close(lse1[:, 0], lsed, 1e-13, 0, "prefill T=1 vs decode lse")
+    for i in range(T):
+        cut = S - T + i + 1
+        ai, lsei = ora.fanout_decode(q[:, i], pk, pv, sk[:, :cut], sv[:, :cut], s)
+        _close(a[:, i], ai, 1e-13, 1e-14, f"prefill token {i}")
+        _close(lse[:, i], lsei, 1e-13, 0, f"prefill token {i} lse")
+    for b in range(nb):
+        keys = np.concatenate([pk, sk[b]])
+        vals = np.concatenate([pv, sv[b]])
+        q_pos = [P + S - T + i for i in range(T)]
+        A, _, _, LSE = brute.attend(q[b].tolist(), keys.tolist(), vals.tolist(), s, q_pos, list(range(P + S)), True)
+        _close(a[b], A, 1e-13, 1e-14, "prefill brute")
+        _close(lse[b], LSE, 1e-13, 0, "prefill brute lse")
+
+
 def pin_finalize_empty():
     a, lse = ora.finalize(np.array([-np.inf, 0.5]), np.array([0.0, 2.0]), np.array([[0.0, 0.0], [1.0, -3.0]]))
     assert np.all(a[0] == 0) and np.isneginf(lse[0])
@@ -419,6 +449,7 @@ ALL_PINS = [
     pin_ring_simulator_worked_example,
     pin_ring_emulation,
     pin_fanout_decode,
+    pin_fanout_prefill,
     pin_finalize_empty,
     pin_zigzag_printed_allocation,
     pin_layouts_partition,

@@ -99,7 +99,27 @@ def _pairs_strict(q_pos, k_pos):
     return int((np.asarray(k_pos)[None, :] < np.asarray(q_pos)[:, None]).sum())
 
 
+_orig_fanout_prefill = ora.fanout_prefill
+
+
+def _prefill_offset_by_one(q, prefix_k, prefix_v, suffix_k, suffix_v, scale):
+    # the new tokens placed one position early: each misses its own key
+    q = np.asarray(q, dtype=np.float64)
+    nb, T = q.shape[:2]
+    P = np.asarray(prefix_k).shape[0]
+    S = np.asarray(suffix_k).shape[1]
+    a = np.empty(q.shape)
+    lse = np.empty(q.shape[:3])
+    for b in range(nb):
+        keys = np.concatenate([prefix_k, suffix_k[b]])
+        vals = np.concatenate([prefix_v, suffix_v[b]])
+        ab, _, _, lb = ora.attend(q[b], keys, vals, scale, P + S - T - 1 + np.arange(T), np.arange(P + S), True)
+        a[b], lse[b] = ab, lb
+    return a, lse
+
+
 MUTATIONS = {
+    "prefill new tokens one position early": ("fanout_prefill", _prefill_offset_by_one),
     "zigzag mirror chunk off by one": ("zigzag_tokens", _zigzag_mirror_off_by_one),
     "striped residue shifted": ("striped_tokens", _striped_shifted),
     "pair count excludes the diagonal": ("visible_pairs", _pairs_strict),
