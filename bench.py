@@ -321,6 +321,53 @@ def bench_merge_scaled(torch, ba, steps, warmup, n_parts=32, rows=131072, D=128)
             "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes}
 
 
+def bench_fanout_prefill(torch, ba, H, w, steps, warmup):
+    """Fan-out prefill of the private suffixes: every branch's new query rows of a
+    KV head batched against each prefix chunk (one call), against the same work
+    issued one branch at a time (the prefix then streams once per branch)."""
+    log(f"inputs: {w.name}")
+    ins = w.make_inputs()
+    q, pk, pv, sk, sv = [H.to_device(t) for t in ins]
+    del ins
+    nb, T, Hq, D = q.shape
+    out = torch.empty(nb, T, Hq, D, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(nb, T, Hq, dtype=torch.float32, device="cuda")
+    ws = torch.empty(ba.fanout_prefill_workspace_bytes(nb, T, Hq, w.n_kv_heads, D, w.prefix_len, w.suffix_len),
+                     dtype=torch.uint8, device="cuda")
+    ws1 = torch.empty(ba.fanout_prefill_workspace_bytes(1, T, Hq, w.n_kv_heads, D, w.prefix_len, w.suffix_len),
+                      dtype=torch.uint8, device="cuda")
+    flush = flush_buffer(torch)
+
+    def batched():
+        ba.fanout_prefix_prefill(q, pk, pv, sk, sv, workspace=ws, out=out, lse=lse)
+
+    def per_branch():
+        for b in range(nb):
+            ba.fanout_prefix_prefill(q[b:b + 1], pk, pv, sk[b:b + 1], sv[b:b + 1], workspace=ws1,
+                                     out=out[b:b + 1], lse=lse[b:b + 1])
+
+    res = {"workload": w.name, "algorithmic_flops": w.flops(), "algorithmic_bytes": w.bytes()}
+    for name, fn in (("batched", batched), ("per_branch", per_branch)):
+        for _ in range(warmup):
+            fn()
+        timer = Timer(torch)
+        for _ in range(steps):
+            flush()
+            e0 = timer.start()
+            fn()
+            timer.stop(e0)
+        torch.cuda.synchronize()
+        ms = timer.median_ms()
+        tf = w.flops() / ms / 1e9
+        res[name] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1),
+                     "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "GB/s": round(w.bytes() / ms / 1e6, 1)}
+        log(f"fanout prefill {name}: {ms * 1e3:.1f} us, {tf:.0f} TFLOP/s, {w.bytes() / ms / 1e6:.0f} GB/s")
+    res["batching_speedup"] = round(res["per_branch"]["us"] / res["batched"]["us"], 3)
+    res["timing"] = "median over steps, HIP events around the call(s), 1 GiB read between calls evicts the caches"
+    return res
+
+
 def bench_layouts(torch, ba, H, w, reps):
     """Load-balanced causal shares ("RingAttention and Context Parallelism", section 5):
     every device of an n-device causal ring emulated on this GPU, each (device, step)
@@ -421,7 +468,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="all",
                     choices=["all", "causal_prefill", "ring_share", "fanout", "shard_merge", "merge_scaled",
-                             "layouts", "copy_calibration"])
+                             "layouts", "fanout_prefill", "copy_calibration"])
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -452,6 +499,8 @@ def main():
         secondary["shard_merge"] = bench_shard_merge(torch, ba, H, wl.SHARD_MERGE, args.steps, args.warmup)
     if only == "merge_scaled":
         secondary["merge_scaled"] = bench_merge_scaled(torch, ba, args.steps, args.warmup)
+    if only == "fanout_prefill":
+        secondary["fanout_prefill"] = bench_fanout_prefill(torch, ba, H, wl.FANOUT_PREFILL, args.steps, args.warmup)
     if only == "layouts":
         secondary["causal_ring_layouts"] = bench_layouts(torch, ba, H, wl.CAUSAL_RING_LAYOUTS, max(1, args.steps // 10))
     if only == "copy_calibration":
@@ -496,6 +545,7 @@ def main():
             line["roofline"]["clock"] = clk
     if not args.no_secondary and only == "all":
         secondary["fanout_decode"] = bench_fanout(torch, ba, H, wl.FANOUT_DECODE, args.steps, args.warmup)
+        secondary["fanout_prefill"] = bench_fanout_prefill(torch, ba, H, wl.FANOUT_PREFILL, args.steps, args.warmup)
         secondary["shard_merge"] = bench_shard_merge(torch, ba, H, wl.SHARD_MERGE, args.steps, args.warmup)
         secondary["merge_scaled"] = bench_merge_scaled(torch, ba, args.steps, args.warmup)
         secondary["ring_share"] = bench_ring_share(torch, ba, H, wl.RING_SHARE, 2, 1)

@@ -63,10 +63,19 @@ class Fanout(ctypes.Structure):
     ]
 
 
+class FanoutPrefill(ctypes.Structure):
+    _fields_ = [
+        ("n_branches", ctypes.c_int32), ("n_new", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("prefix_len", ctypes.c_int32),
+        ("suffix_len", ctypes.c_int32), ("scale", ctypes.c_float),
+    ]
+
+
 EXPORTS = [
     "blockattn_fwd_block", "blockattn_fwd_workspace_bytes", "blockattn_shard_states",
     "blockattn_shard_workspace_bytes", "blockattn_merge_states", "blockattn_finalize",
-    "fanout_prefix_decode", "fanout_workspace_bytes", "blockattn_status_str",
+    "fanout_prefix_decode", "fanout_workspace_bytes", "fanout_prefix_prefill",
+    "fanout_prefill_workspace_bytes", "blockattn_status_str",
     "blockattn_last_error", "blockattn_abi_version",
 ]
 
@@ -110,6 +119,10 @@ def load():
     lib.fanout_prefix_decode.restype = i32
     lib.fanout_workspace_bytes.argtypes = [P(Fanout)]
     lib.fanout_workspace_bytes.restype = sz
+    lib.fanout_prefix_prefill.argtypes = [P(FanoutPrefill), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.fanout_prefix_prefill.restype = i32
+    lib.fanout_prefill_workspace_bytes.argtypes = [P(FanoutPrefill)]
+    lib.fanout_prefill_workspace_bytes.restype = sz
     lib.blockattn_status_str.argtypes = [i32]
     lib.blockattn_status_str.restype = ctypes.c_char_p
     lib.blockattn_last_error.argtypes = []
@@ -285,3 +298,37 @@ def fanout_prefix_decode(q, prefix_k, prefix_v, suffix_k, suffix_v, scale: float
 def fanout_workspace_bytes(n_branches, n_q_heads, n_kv_heads, head_dim, prefix_len, suffix_len) -> int:
     f = Fanout(n_branches, n_q_heads, n_kv_heads, head_dim, prefix_len, suffix_len, 0.0)
     return load().fanout_workspace_bytes(ctypes.byref(f))
+
+
+def fanout_prefix_prefill(q, prefix_k, prefix_v, suffix_k, suffix_v, scale: float = 0.0,
+                          workspace: Optional[torch.Tensor] = None, want_lse: bool = True,
+                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, stream=None):
+    """fanout_prefix_prefill: q [nb, T, Hq, D] (each branch's T newest tokens); prefix [P, Hkv, D];
+    suffix [nb, S, Hkv, D] whose last T tokens are the new ones (all contiguous bf16).
+    Returns out [nb, T, Hq, D] bf16 and lse [nb, T, Hq]."""
+    lib = load()
+    nb, T, Hq, D = q.shape
+    Hkv = prefix_k.shape[1] if prefix_k is not None else suffix_k.shape[2]
+    P = prefix_k.shape[0] if prefix_k is not None else 0
+    S = suffix_k.shape[1] if suffix_k is not None else 0
+    for name, t in (("q", q), ("prefix_k", prefix_k), ("prefix_v", prefix_v), ("suffix_k", suffix_k),
+                    ("suffix_v", suffix_v)):
+        if t is not None and (not t.is_contiguous() or t.dtype != torch.bfloat16):
+            raise ValueError(f"{name} must be contiguous bf16")
+    f = FanoutPrefill(nb, T, Hq, Hkv, D, P, S, scale)
+    need = lib.fanout_prefill_workspace_bytes(ctypes.byref(f))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if out is None:
+        out = torch.empty(nb, T, Hq, D, dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty(nb, T, Hq, dtype=torch.float32, device=q.device)
+    _check(lib.fanout_prefix_prefill(ctypes.byref(f), _ptr(q), _ptr(prefix_k), _ptr(prefix_v), _ptr(suffix_k),
+                                     _ptr(suffix_v), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+                                     _stream(stream)), "fanout_prefix_prefill")
+    return out, lse
+
+
+def fanout_prefill_workspace_bytes(nb, T, Hq, Hkv, D, P, S) -> int:
+    return load().fanout_prefill_workspace_bytes(ctypes.byref(FanoutPrefill(nb, T, Hq, Hkv, D, P, S, 0.0)))

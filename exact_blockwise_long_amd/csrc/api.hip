@@ -464,87 +464,112 @@ ba_status blockattn_finalize(ba_state s, int64_t rows, int32_t head_dim, void* o
 
 namespace {
 
-ba_status check_fanout(const ba_fanout* f) {
-  if (!f) return fail(BA_ERR_NULL, "fanout descriptor is NULL");
-  if (f->head_dim != 64 && f->head_dim != 128) return fail(BA_ERR_SHAPE, "head_dim %d", f->head_dim);
-  if (f->n_q_heads <= 0 || f->n_kv_heads <= 0 || f->n_q_heads % f->n_kv_heads != 0)
-    return fail(BA_ERR_SHAPE, "bad head counts %d / %d", f->n_q_heads, f->n_kv_heads);
-  if (f->n_branches < 0 || f->prefix_len < 0 || f->suffix_len < 0) return fail(BA_ERR_SHAPE, "negative size");
-  if (f->n_branches > 0 && f->prefix_len + f->suffix_len == 0) return fail(BA_ERR_SHAPE, "no keys to attend to");
+// Fan-out shapes shared by decode (one new token per branch) and prefill
+// (the last T tokens of every branch's private suffix).
+struct FanoutShape {
+  int nb = 0, T = 1, Hq = 0, Hkv = 0, D = 0, P = 0, S = 0;
+  float scale = 0.f;
+};
+
+ba_status check_fanout_shape(const FanoutShape& f) {
+  if (f.D != 64 && f.D != 128) return fail(BA_ERR_SHAPE, "head_dim %d", f.D);
+  if (f.Hq <= 0 || f.Hkv <= 0 || f.Hq % f.Hkv != 0)
+    return fail(BA_ERR_SHAPE, "bad head counts %d / %d", f.Hq, f.Hkv);
+  if (f.nb < 0 || f.P < 0 || f.S < 0) return fail(BA_ERR_SHAPE, "negative size");
+  if (f.nb > 0 && f.P + f.S == 0) return fail(BA_ERR_SHAPE, "no keys to attend to");
+  if ((int64_t)f.nb * f.T * f.Hq > ((int64_t)1 << 31) / 2) return fail(BA_ERR_SHAPE, "too many query rows");
   return BA_OK;
 }
 
+ba_status check_fanout(const ba_fanout* f) {
+  if (!f) return fail(BA_ERR_NULL, "fanout descriptor is NULL");
+  FanoutShape s;
+  s.nb = f->n_branches;
+  s.Hq = f->n_q_heads;
+  s.Hkv = f->n_kv_heads;
+  s.D = f->head_dim;
+  s.P = f->prefix_len;
+  s.S = f->suffix_len;
+  return check_fanout_shape(s);
+}
+
 struct FanoutPlan {
-  int row_tiles = 0;   // 128-row tiles of one KV head's rows (n_branches * G)
+  int row_tiles = 0;   // 128-row tiles of one KV head's rows (n_branches * T * G)
   int chunk_len = 0;
   int n_chunks = 0;    // prefix chunks
-  int bpj = 1;         // branches per suffix job
+  int srt = 1;         // 128-row tiles of one branch's rows (T * G)
+  int bpj = 1;         // branches per suffix job (when a branch's rows fit one tile)
   int suffix_jobs = 0;
   int slots = 0;       // workspace partial slots
   int suffix_slot = -1;
   int n_jobs = 0;
 };
 
-// The launch is sized to about kFanoutTargetWorkgroups jobs that each move
-// about the same number of K/V bytes, so no compute unit idles while others
-// still stream: every job of the decode is bandwidth bound, and a job's time
-// is its bytes over its share of HBM.  A suffix job walks bpj branches' private
-// suffixes of one KV head one after another; a prefix job walks one chunk of
-// the shared prefix for one row tile of a KV head.
-FanoutPlan plan_fanout(const ba_fanout* f) {
+// The launch is sized to about kFanoutTargetWorkgroups jobs that each walk
+// about the same number of (row tile, key) pairs, so no compute unit idles
+// while others still work: a job's time is its K/V bytes over its share of
+// HBM for a decode and its tile-key pairs over its share of the matrix cores
+// for a prefill, both proportional to the keys a row tile walks.  Suffix jobs
+// far shorter than that are not counted against the target.  A suffix job
+// walks bpj branches' private suffixes of one KV head one after another (or
+// one row tile of one branch when a branch has more than one); a prefix job
+// walks one chunk of the shared prefix for one row tile of a KV head.
+FanoutPlan plan_fanout(const FanoutShape& f) {
   FanoutPlan fp;
-  const int G = f->n_q_heads / f->n_kv_heads;
-  fp.row_tiles = (int)(((int64_t)f->n_branches * G + ba::kTileRows - 1) / ba::kTileRows);
-  const int xs = fp.row_tiles * f->n_kv_heads;
-  // Keys each job should walk: all keys read (the prefix once per row tile)
-  // over the target job count.
-  const int64_t keys_total = (int64_t)f->n_kv_heads *
-                             ((int64_t)f->prefix_len * fp.row_tiles + (int64_t)f->n_branches * f->suffix_len);
+  const int G = f.Hq / f.Hkv;
+  const int64_t rows = (int64_t)f.nb * f.T * G;
+  fp.row_tiles = (int)((rows + ba::kTileRows - 1) / ba::kTileRows);
+  fp.srt = (int)(((int64_t)f.T * G + ba::kTileRows - 1) / ba::kTileRows);
+  const int xs = fp.row_tiles * f.Hkv;
+  const int64_t keys_total =
+      (int64_t)f.Hkv * ((int64_t)f.P * fp.row_tiles + (int64_t)f.nb * fp.srt * f.S);
   const int64_t per_job = keys_total / ba::kFanoutTargetWorkgroups > 1 ? keys_total / ba::kFanoutTargetWorkgroups : 1;
-  if (f->suffix_len > 0) {
-    int64_t bpj = (per_job + f->suffix_len / 2) / f->suffix_len;
-    if (bpj > f->n_branches) bpj = f->n_branches;
-    if (bpj < 1) bpj = 1;
-    fp.bpj = (int)bpj;
-    fp.suffix_jobs = f->n_kv_heads * (int)((f->n_branches + fp.bpj - 1) / fp.bpj);
+  if (f.S > 0) {
+    if (fp.srt == 1) {
+      int64_t bpj = (per_job + f.S / 2) / f.S;
+      if (bpj > f.nb) bpj = f.nb;
+      if (bpj < 1) bpj = 1;
+      fp.bpj = (int)bpj;
+      fp.suffix_jobs = f.Hkv * (int)((f.nb + fp.bpj - 1) / fp.bpj);
+    } else {
+      fp.suffix_jobs = f.Hkv * f.nb * fp.srt;
+    }
   }
-  if (f->prefix_len > 0) {
-    int64_t want = (ba::kFanoutTargetWorkgroups - fp.suffix_jobs) / xs;
+  if (f.P > 0) {
+    // Suffix jobs much shorter than the average job (many new tokens per
+    // branch against a short private suffix) run in the gaps the prefix jobs
+    // leave; only comparable ones take prefix jobs' places in the launch.
+    const int64_t suffix_job_keys = fp.srt == 1 ? (int64_t)fp.bpj * f.S : (int64_t)f.S;
+    const bool suffix_small = f.S > 0 && 2 * suffix_job_keys < per_job;
+    int64_t want = (ba::kFanoutTargetWorkgroups - (suffix_small ? 0 : fp.suffix_jobs)) / xs;
     if (want < 1) want = 1;
-    int64_t cl = (f->prefix_len + want - 1) / want;
+    int64_t cl = (f.P + want - 1) / want;
     cl = (cl + 63) / 64 * 64;
     if (cl < 256) cl = 256;
     fp.chunk_len = (int)cl;
-    fp.n_chunks = (int)((f->prefix_len + cl - 1) / cl);
+    fp.n_chunks = (int)((f.P + cl - 1) / cl);
   }
   fp.slots = fp.n_chunks;
-  if (f->suffix_len > 0) fp.suffix_slot = fp.slots++;
+  if (f.S > 0) fp.suffix_slot = fp.slots++;
   fp.n_jobs = xs * fp.n_chunks + fp.suffix_jobs;
   return fp;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t fanout_workspace_bytes(const ba_fanout* f) {
-  if (check_fanout(f) != BA_OK || f->n_branches == 0) return 0;
-  FanoutPlan fp = plan_fanout(f);
-  return partial_bytes(fp.slots, (int64_t)f->n_branches * f->n_q_heads, f->head_dim);
+size_t fanout_bytes(const FanoutShape& f) {
+  const FanoutPlan fp = plan_fanout(f);
+  return partial_bytes(fp.slots, (int64_t)f.nb * f.T * f.Hq, f.D);
 }
 
-ba_status fanout_prefix_decode(const ba_fanout* f, const void* q, const void* prefix_k, const void* prefix_v,
-                               const void* suffix_k, const void* suffix_v, void* out, float* lse, void* workspace,
-                               size_t workspace_bytes, hipStream_t stream) {
-  ba_status st = check_fanout(f);
-  if (st) return st;
-  if (f->n_branches == 0) return ok();
+ba_status fanout_run(const FanoutShape& f, const void* q, const void* prefix_k, const void* prefix_v,
+                     const void* suffix_k, const void* suffix_v, void* out, float* lse, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  if (f.nb == 0) return ok();
   if (!q || !out) return fail(BA_ERR_NULL, "q or out is NULL");
-  if (f->prefix_len > 0 && (!prefix_k || !prefix_v)) return fail(BA_ERR_NULL, "prefix k/v is NULL");
-  if (f->suffix_len > 0 && (!suffix_k || !suffix_v)) return fail(BA_ERR_NULL, "suffix k/v is NULL");
-  const int D = f->head_dim;
-  const int64_t R = (int64_t)f->n_branches * f->n_q_heads;
-  FanoutPlan fp = plan_fanout(f);
+  if (f.P > 0 && (!prefix_k || !prefix_v)) return fail(BA_ERR_NULL, "prefix k/v is NULL");
+  if (f.S > 0 && (!suffix_k || !suffix_v)) return fail(BA_ERR_NULL, "suffix k/v is NULL");
+  const int D = f.D;
+  const int64_t R = (int64_t)f.nb * f.T * f.Hq;
+  const FanoutPlan fp = plan_fanout(f);
   const size_t need = partial_bytes(fp.slots, R, D);
   if (!workspace || workspace_bytes < need)
     return fail(BA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
@@ -552,17 +577,18 @@ ba_status fanout_prefix_decode(const ba_fanout* f, const void* q, const void* pr
   float *wm, *wl, *wo;
   partial_ptrs(workspace, fp.slots, R, &wm, &wl, &wo);
 
+  // The query rows of all branches as one block of nb * T tokens.
   ba_problem p;
   memset(&p, 0, sizeof(p));
-  p.n_q_heads = f->n_q_heads;
-  p.n_kv_heads = f->n_kv_heads;
+  p.n_q_heads = f.Hq;
+  p.n_kv_heads = f.Hkv;
   p.head_dim = D;
-  p.q_len = f->n_branches;
+  p.q_len = f.nb * f.T;
   p.q_pos0 = 0;
-  p.q_stride_token = (int64_t)f->n_q_heads * D;
+  p.q_stride_token = (int64_t)f.Hq * D;
   p.q_stride_head = D;
   p.dtype = BA_BF16;
-  p.scale = f->scale;
+  p.scale = f.scale;
   p.causal = 0;
   const ba::QSide qs = make_qside(&p, q);
 
@@ -572,9 +598,9 @@ ba_status fanout_prefix_decode(const ba_fanout* f, const void* q, const void* pr
   ba_kv_block b;
   b.k = prefix_k;
   b.v = prefix_v;
-  b.len = f->prefix_len;
+  b.len = f.P;
   b.pos0 = 0;
-  b.k_stride_token = b.v_stride_token = (int64_t)f->n_kv_heads * D;
+  b.k_stride_token = b.v_stride_token = (int64_t)f.Hkv * D;
   b.k_stride_head = b.v_stride_head = D;
   a.prefix = make_seg(b);
   a.row_tiles = fp.row_tiles;
@@ -582,8 +608,10 @@ ba_status fanout_prefix_decode(const ba_fanout* f, const void* q, const void* pr
   a.n_chunks = fp.n_chunks;
   a.sk = suffix_k;
   a.sv = suffix_v;
-  a.S = f->suffix_len;
+  a.S = f.S;
+  a.T = f.T;
   a.suffix_slot = fp.suffix_slot;
+  a.srt = fp.srt;
   a.bpj = fp.bpj;
   a.ws_m = wm;
   a.ws_l = wl;
@@ -604,6 +632,67 @@ ba_status fanout_prefix_decode(const ba_fanout* f, const void* q, const void* pr
   mg.fin_out = (uint16_t*)out;
   mg.fin_lse = lse;
   return hip_status(ba::launch_merge_groups(mg, D, stream), "fanout merge launch");
+}
+
+FanoutShape decode_shape(const ba_fanout* f) {
+  FanoutShape s;
+  s.nb = f->n_branches;
+  s.T = 1;
+  s.Hq = f->n_q_heads;
+  s.Hkv = f->n_kv_heads;
+  s.D = f->head_dim;
+  s.P = f->prefix_len;
+  s.S = f->suffix_len;
+  s.scale = f->scale;
+  return s;
+}
+
+ba_status prefill_shape(const ba_fanout_prefill* f, FanoutShape* s) {
+  if (!f) return fail(BA_ERR_NULL, "fanout prefill descriptor is NULL");
+  s->nb = f->n_branches;
+  s->T = f->n_new;
+  s->Hq = f->n_q_heads;
+  s->Hkv = f->n_kv_heads;
+  s->D = f->head_dim;
+  s->P = f->prefix_len;
+  s->S = f->suffix_len;
+  s->scale = f->scale;
+  if (f->n_new < 1 || f->n_new > f->suffix_len)
+    return fail(BA_ERR_SHAPE, "n_new %d outside 1..suffix_len (%d)", f->n_new, f->suffix_len);
+  return check_fanout_shape(*s);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fanout_workspace_bytes(const ba_fanout* f) {
+  if (check_fanout(f) != BA_OK || f->n_branches == 0) return 0;
+  return fanout_bytes(decode_shape(f));
+}
+
+ba_status fanout_prefix_decode(const ba_fanout* f, const void* q, const void* prefix_k, const void* prefix_v,
+                               const void* suffix_k, const void* suffix_v, void* out, float* lse, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  ba_status st = check_fanout(f);
+  if (st) return st;
+  return fanout_run(decode_shape(f), q, prefix_k, prefix_v, suffix_k, suffix_v, out, lse, workspace,
+                    workspace_bytes, stream);
+}
+
+size_t fanout_prefill_workspace_bytes(const ba_fanout_prefill* f) {
+  FanoutShape s;
+  if (prefill_shape(f, &s) != BA_OK || s.nb == 0) return 0;
+  return fanout_bytes(s);
+}
+
+ba_status fanout_prefix_prefill(const ba_fanout_prefill* f, const void* q, const void* prefix_k,
+                                const void* prefix_v, const void* suffix_k, const void* suffix_v, void* out,
+                                float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  FanoutShape s;
+  ba_status st = prefill_shape(f, &s);
+  if (st) return st;
+  return fanout_run(s, q, prefix_k, prefix_v, suffix_k, suffix_v, out, lse, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -588,12 +588,13 @@ __global__ __launch_bounds__(kThreads, 2) void split_kernel(SplitArgs a) {
   partial_job<D>(a.qs, f0, f1, g, cs, a.ws_m, a.ws_l, a.ws_o, (int64_t)chunk * a.R, (lds_char*)lds);
 }
 
-// Shared-prefix fan-out decode, one launch for both job kinds ("AHBM Agentic
-// Runtime Architecture" s.3.2-3.4): jobs [0, n_prefix_jobs) are (row tile,
+// Shared-prefix fan-out (decode, or prefill of the private suffixes), one
+// launch for both job kinds ("AHBM Agentic Runtime Architecture" s.3.2-3.4,
+// s.3.6): jobs [0, n_prefix_jobs) are (row tile,
 // KV head, prefix chunk) -- every branch's rows of a KV head against one chunk
 // of the shared prefix, written to slot `chunk`; the remaining jobs are
-// (branch group, KV head) -- each branch's rows against its private suffix in
-// turn, written to slot `suffix_slot`.
+// (branch group or branch row tile, KV head) -- each branch's rows against its
+// private suffix under the causal rule, written to slot `suffix_slot`.
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void fanout_kernel(FanoutArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[2 * Cfg<D>::STAGEB];
@@ -620,8 +621,18 @@ __global__ __launch_bounds__(kThreads, 2) void fanout_kernel(FanoutArgs a) {
   }
   const int j = id - n_prefix_jobs;
   const int g = j % Hkv;
-  const int b0 = (j / Hkv) * a.bpj;
-  const int b1 = min(b0 + a.bpj, a.qs.q_len);
+  const int u = j / Hkv;
+  const int TG = a.T * G;
+  int b0, b1, rt;
+  if (a.srt == 1) {
+    b0 = u * a.bpj;
+    b1 = min(b0 + a.bpj, a.qs.q_len / a.T);
+    rt = 0;
+  } else {
+    b0 = u / a.srt;
+    b1 = b0 + 1;
+    rt = u % a.srt;
+  }
   const int64_t tok = (int64_t)Hkv * D;
   for (int b = b0; b < b1; ++b) {
     if (b > b0) __syncthreads();  // every wave is done with the previous branch's LDS tiles
@@ -635,8 +646,14 @@ __global__ __launch_bounds__(kThreads, 2) void fanout_kernel(FanoutArgs a) {
     sg.pos0 = 0;
     sg.n = a.S;
     sg.pad_ = 0;
-    partial_job<D>(a.qs, b * G, b * G + G, g, sg, a.ws_m, a.ws_l, a.ws_o, (int64_t)a.suffix_slot * a.R,
-                   (lds_char*)lds);
+    // Suffix positions: key j at j, branch b's new token i (query token b*T + i)
+    // at S - T + i.
+    QSide qs = a.qs;
+    qs.causal = 1;
+    qs.q_pos0 = (int64_t)(a.S - a.T) - (int64_t)b * a.T;
+    const int f0 = b * TG + rt * kTileRows;
+    const int f1 = min(f0 + kTileRows, (b + 1) * TG);
+    partial_job<D>(qs, f0, f1, g, sg, a.ws_m, a.ws_l, a.ws_o, (int64_t)a.suffix_slot * a.R, (lds_char*)lds);
   }
 }
 

@@ -67,12 +67,16 @@ struct SplitArgs {
   Seg seg[kMaxSeg];
 };
 
-// Fan-out decode: one launch of prefix-chunk jobs and branch-suffix jobs.
+// Fan-out over the last T tokens of each branch (T = 1: decode): one launch
+// of prefix-chunk jobs and branch-suffix jobs.  The query rows are one block
+// of n_branches * T tokens (qs.q_len), branch b's tokens being b*T .. b*T+T-1.
 // Prefix job (row tile, KV head g, chunk c): flat rows of the tile against
-// prefix keys [c * chunk_len, ...), written to workspace slot c.  Suffix job
-// (branch group, KV head g): for each branch b of the group (bpj consecutive
-// branches), flat rows [b*G, b*G + G) against branch b's suffix (suffix k/v
-// are [n_branches, S, Hkv, D]), written to slot suffix_slot.
+// prefix keys [c * chunk_len, ...), no mask, written to workspace slot c.
+// Suffix job for KV head g: with srt == 1, each branch b of a group of bpj
+// consecutive branches; otherwise one 128-row tile rt of one branch b -- the
+// branch's flat rows [b*T*G, (b+1)*T*G) (tile rt of them) against its own
+// suffix (suffix k/v are [n_branches, S, Hkv, D]), causal with new token i at
+// suffix position S - T + i, written to slot suffix_slot.
 struct FanoutArgs {
   QSide qs;          // q_len = n_branches, non-causal
   Seg prefix;        // the whole shared prefix
@@ -82,8 +86,10 @@ struct FanoutArgs {
   const void* sk;
   const void* sv;
   int32_t S;
+  int32_t T;         // new tokens per branch
   int32_t suffix_slot;
-  int32_t bpj;       // branches per suffix job
+  int32_t srt;       // 128-row tiles of one branch's rows
+  int32_t bpj;       // branches per suffix job (srt == 1)
   float* ws_m;
   float* ws_l;
   float* ws_o;

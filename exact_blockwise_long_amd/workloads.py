@@ -226,6 +226,49 @@ SHARD_MERGE = ShardMergeWorkload(
     n_branches=8, n_q_heads=8, head_dim=128, kv_len=1048576, n_shards=32, seed=5)
 
 @dataclass
+class FanoutPrefillWorkload:
+    """Shared-prefix fan-out over the newest T tokens of every branch (prefill
+    of the private suffixes): each new token sees the prefix and its branch's
+    suffix up to itself."""
+
+    name: str
+    n_branches: int
+    n_new: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    prefix_len: int
+    suffix_len: int
+    seed: int
+    scale_qkv: float = 0.5
+
+    def pairs(self) -> int:
+        """Visible (query token, key) pairs, per query head."""
+        T, P, S = self.n_new, self.prefix_len, self.suffix_len
+        per_branch = sum(P + S - T + i + 1 for i in range(T))
+        return self.n_branches * per_branch
+
+    def flops(self) -> float:
+        return 4.0 * self.head_dim * self.n_q_heads * self.pairs()
+
+    def bytes(self) -> int:
+        kv_tok = 2 * self.n_kv_heads * self.head_dim * 2
+        q = self.n_branches * self.n_new * self.n_q_heads * self.head_dim * 2
+        return self.prefix_len * kv_tok + self.n_branches * self.suffix_len * kv_tok + 2 * q
+
+    def make_inputs(self):
+        """(q [nb, T, Hq, D], prefix_k, prefix_v [P, Hkv, D], suffix_k, suffix_v [nb, S, Hkv, D])."""
+        g = synth.rng(self.seed)
+        nb, T, Hq, Hkv, D = self.n_branches, self.n_new, self.n_q_heads, self.n_kv_heads, self.head_dim
+        q = synth.normal(g, (nb, T, Hq, D), self.scale_qkv, "bf16")
+        pk = synth.normal(g, (self.prefix_len, Hkv, D), self.scale_qkv, "bf16")
+        pv = synth.normal(g, (self.prefix_len, Hkv, D), self.scale_qkv, "bf16")
+        sk = synth.normal(g, (nb, self.suffix_len, Hkv, D), self.scale_qkv, "bf16")
+        sv = synth.normal(g, (nb, self.suffix_len, Hkv, D), self.scale_qkv, "bf16")
+        return q, pk, pv, sk, sv
+
+
+@dataclass
 class CausalRingWorkload:
     """A whole causal sequence sharded over n emulated ring devices in one of
     the layouts of "RingAttention and Context Parallelism", section 5; every
@@ -255,6 +298,10 @@ class CausalRingWorkload:
         v = synth.normal(g, (self.seq_len, self.n_kv_heads, self.head_dim), self.scale_qkv, "bf16")
         return q, k, v
 
+
+FANOUT_PREFILL = FanoutPrefillWorkload(
+    name="fanout_prefill_64k: bf16 GQA 64/8 D128, prefix 65536, 8 branches x 20 new tokens, 512-token private suffixes",
+    n_branches=8, n_new=20, n_q_heads=64, n_kv_heads=8, head_dim=128, prefix_len=65536, suffix_len=512, seed=7)
 
 CAUSAL_RING_LAYOUTS = CausalRingWorkload(
     name="causal_ring_32k_8dev: bf16 GQA 64/8 D128, 32768 tokens over 8 emulated devices "

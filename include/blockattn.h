@@ -228,6 +228,47 @@ ba_status fanout_prefix_decode(const ba_fanout* f, const void* q,
 
 size_t fanout_workspace_bytes(const ba_fanout* f);
 
+/* Shared-prefix fan-out over several new tokens per branch: prefill of the
+ * branches' private suffixes ([AHBM] s.2.5, s.3.1-3.2 and s.3.6: 8 sub-agents
+ * x 20 new tokens give a combined query matrix of 160 rows per query head).
+ *
+ * q [n_branches, n_new, n_q_heads, head_dim] bf16 holds each branch's n_new
+ * newest tokens; prefix_k/v [prefix_len, n_kv_heads, head_dim] bf16 is the
+ * shared prefix, read once for all branches; suffix_k/v [n_branches,
+ * suffix_len, n_kv_heads, head_dim] bf16 holds each branch's private tokens,
+ * whose last n_new are the new ones (1 <= n_new <= suffix_len).  All
+ * contiguous.  Branch b's context is the prefix then its own suffix, at
+ * positions 0 .. prefix_len + suffix_len - 1; new token i sits at
+ * prefix_len + suffix_len - n_new + i and sees every key up to and including
+ * its own position (the causal rule of [RAC] s.5).  Every branch's rows that
+ * share a KV head are batched against each prefix chunk; each branch's suffix
+ * gives its own causal partial; partials merge by log-sum-exp per row.
+ * Writes out [n_branches, n_new, n_q_heads, head_dim] bf16 and, if lse is not
+ * NULL, lse [n_branches, n_new, n_q_heads] fp32.  With n_new = 1 this is
+ * fanout_prefix_decode.  Needs fanout_prefill_workspace_bytes() bytes of
+ * workspace (device memory, 16-byte aligned).  Errors: BA_ERR_NULL,
+ * BA_ERR_SHAPE (bad head counts or head_dim, n_new outside 1..suffix_len,
+ * negative lengths), BA_ERR_WORKSPACE. */
+typedef struct {
+  int32_t n_branches;  /* branches                                              */
+  int32_t n_new;       /* new query tokens per branch (the suffix's last n_new) */
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;    /* 64 or 128                                             */
+  int32_t prefix_len;  /* shared prefix keys (>= 0)                             */
+  int32_t suffix_len;  /* private keys per branch, incl. the new tokens         */
+  float scale;         /* <= 0 selects 1/sqrt(head_dim)                         */
+} ba_fanout_prefill;
+
+ba_status fanout_prefix_prefill(const ba_fanout_prefill* f, const void* q,
+                                const void* prefix_k, const void* prefix_v,
+                                const void* suffix_k, const void* suffix_v,
+                                void* out, float* lse,
+                                void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+size_t fanout_prefill_workspace_bytes(const ba_fanout_prefill* f);
+
 /* Static description of a status code; never NULL. */
 const char* blockattn_status_str(int32_t status);
 

@@ -171,6 +171,32 @@ def test_fanout_validation(lib):
     assert call(ba.Fanout(0, 8, 2, 128, 100, 10, 0.0)) == 0   # no branches: no-op
 
 
+def test_fanout_prefill_validation(lib):
+    def call(f, ws=None, ws_bytes=0, **ptrs):
+        a = dict(q=FAKE, pk=FAKE, pv=FAKE, sk=FAKE, sv=FAKE, out=FAKE)
+        a.update(ptrs)
+        return lib.fanout_prefix_prefill(ctypes.byref(f), a["q"], a["pk"], a["pv"], a["sk"], a["sv"], a["out"],
+                                         None, ws, ws_bytes, None)
+    P = ba.FanoutPrefill
+    assert call(P(4, 20, 8, 3, 128, 100, 64, 0.0)) == 2          # heads
+    assert call(P(4, 0, 8, 2, 128, 100, 64, 0.0)) == 2           # n_new < 1
+    assert call(P(4, 65, 8, 2, 128, 100, 64, 0.0)) == 2          # n_new > suffix_len
+    assert call(P(4, 20, 8, 2, 96, 100, 64, 0.0)) == 2           # head_dim
+    assert call(P(4, 20, 8, 2, 128, 100, 64, 0.0), q=None) == 1
+    assert call(P(4, 20, 8, 2, 128, 100, 64, 0.0), sv=None) == 1
+    assert lib.fanout_prefix_prefill(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 1
+    f = P(8, 20, 64, 8, 128, 65536, 512, 0.0)
+    need = lib.fanout_prefill_workspace_bytes(ctypes.byref(f))
+    assert need > 0 and need % 256 == 0
+    assert call(f) == 5
+    assert call(f, ws=FAKE, ws_bytes=need - 16) == 5
+    assert call(P(0, 20, 8, 2, 128, 100, 64, 0.0)) == 0           # no branches: no-op
+    # one new token per branch needs exactly the decode's workspace
+    dec = lib.fanout_workspace_bytes(ctypes.byref(ba.Fanout(16, 64, 8, 128, 65536, 512, 0.0)))
+    pre = lib.fanout_prefill_workspace_bytes(ctypes.byref(P(16, 1, 64, 8, 128, 65536, 512, 0.0)))
+    assert dec == pre
+
+
 def test_workspace_sizes_are_deterministic(lib):
     f = ba.Fanout(16, 64, 8, 128, 65536, 512, 0.0)
     a = lib.fanout_workspace_bytes(ctypes.byref(f))

@@ -119,3 +119,17 @@ def test_shard_merge_full_size_all_rows():
     H.assert_close(H.host(merged[0]).reshape(m_ref.shape), m_ref, H.BF16_M * max(1.0, logits_span / 4), "shard m")
     print(f"    all {w.rows} rows, max |m| {logits_span:.1f}: max/mean abs err {stats[0]:.2e}/{stats[1]:.2e}",
           flush=True)
+
+
+def test_fanout_prefill_full_size_all_rows():
+    w = wl.FANOUT_PREFILL
+    announce(w.name)
+    ins = w.make_inputs()
+    dev = [H.to_device(t) for t in ins]
+    out, lse = ba.fanout_prefix_prefill(*dev)
+    torch.cuda.synchronize()
+    a_ref, lse_ref = ora.fanout_prefill(*[t.f64() for t in ins], 1.0 / np.sqrt(w.head_dim))
+    stats = H.assert_bf16_out(H.host(out), a_ref, w.name)
+    H.assert_close(H.host(lse), lse_ref, H.BF16_LSE, "fanout prefill lse")
+    print(f"    all {w.n_branches * w.n_new * w.n_q_heads} rows: max/mean abs err {stats[0]:.2e}/{stats[1]:.2e}",
+          flush=True)

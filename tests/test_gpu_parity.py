@@ -326,3 +326,43 @@ def test_fanout_small(nb, Hq, Hkv, D, P, S):
     a_ref, lse_ref = ora.fanout_decode(q.f64(), pk.f64(), pv.f64(), sk.f64(), sv.f64(), 1.0 / np.sqrt(D))
     H.assert_bf16_out(H.host(out), a_ref, "fanout")
     H.assert_close(H.host(lse), lse_ref, H.BF16_LSE, "fanout lse")
+
+
+# ---------------------------------------------------------------- fan-out prefill
+
+# (nb, T, Hq, Hkv, D, P, S): several new tokens per branch, causal in the suffix.
+# 2 x 20 x 8 rows: 160 rows per KV head, two row tiles per branch; T = S: no
+# older private tokens; P = 0: no prefix; the last case groups branches per job.
+@pytest.mark.parametrize("nb,T,Hq,Hkv,D,P,S", [(3, 5, 8, 2, 128, 1000, 37), (2, 20, 64, 8, 128, 700, 90),
+                                               (4, 7, 8, 2, 64, 300, 7), (3, 9, 8, 2, 128, 0, 70),
+                                               (42, 2, 4, 4, 64, 2000, 3)])
+def test_fanout_prefill(nb, T, Hq, Hkv, D, P, S):
+    announce(f"fanout prefill nb={nb} T={T} Hq={Hq} Hkv={Hkv} D={D} P={P} S={S} seed 72")
+    g = synth.rng(72)
+    q = synth.normal(g, (nb, T, Hq, D), 0.5, "bf16")
+    pk = synth.normal(g, (P, Hkv, D), 0.5, "bf16")
+    pv = synth.normal(g, (P, Hkv, D), 0.5, "bf16")
+    sk = synth.normal(g, (nb, S, Hkv, D), 0.5, "bf16")
+    sv = synth.normal(g, (nb, S, Hkv, D), 0.5, "bf16")
+    dev = [H.to_device(t) if t.storage.size else None for t in (q, pk, pv, sk, sv)]
+    out, lse = ba.fanout_prefix_prefill(*dev)
+    torch.cuda.synchronize()
+    a_ref, lse_ref = ora.fanout_prefill(q.f64(), pk.f64(), pv.f64(), sk.f64(), sv.f64(), 1.0 / np.sqrt(D))
+    H.assert_bf16_out(H.host(out), a_ref, "fanout prefill")
+    H.assert_close(H.host(lse), lse_ref, H.BF16_LSE, "fanout prefill lse")
+
+
+def test_fanout_prefill_one_token_is_the_decode():
+    nb, Hq, Hkv, D, P, S = 5, 8, 2, 128, 900, 33
+    announce(f"fanout prefill T=1 vs decode nb={nb} P={P} S={S} seed 74")
+    g = synth.rng(74)
+    q = synth.normal(g, (nb, 1, Hq, D), 0.5, "bf16")
+    pk = synth.normal(g, (P, Hkv, D), 0.5, "bf16")
+    pv = synth.normal(g, (P, Hkv, D), 0.5, "bf16")
+    sk = synth.normal(g, (nb, S, Hkv, D), 0.5, "bf16")
+    sv = synth.normal(g, (nb, S, Hkv, D), 0.5, "bf16")
+    qd, pkd, pvd, skd, svd = [H.to_device(t) for t in (q, pk, pv, sk, sv)]
+    o1, l1 = ba.fanout_prefix_prefill(qd, pkd, pvd, skd, svd)
+    o2, l2 = ba.fanout_prefix_decode(qd[:, 0].contiguous(), pkd, pvd, skd, svd)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[:, 0], o2) and torch.equal(l1[:, 0], l2)
