@@ -285,6 +285,90 @@ def emulate_ring(q_blocks, kv_blocks, scale, causal=False, block_len=None):
     return [finalize(*s) for s in states]
 
 
+# ---------------------------------------------------------------- backward pass
+# [RAC] section 7, "Memory and Backward Pass Complexity": the forward keeps Q
+# and the log-sum-exp L = m + ln l; the backward recomputes each block's
+# scores from them, accumulates dQ locally and dK, dV per visiting block.
+# The gradients themselves are those of the attention definition of section 1
+# (A = softmax(scale * Q K^T + M) V), by the chain rule.
+
+def attention_grads(q, k, v, d_out, scale, q_pos=None, k_pos=None, causal=False, key_subset=None):
+    """Gradients of sum(A * d_out) with A the exact attention of ``attend``.
+
+    With p = softmax(z) over row i's visible keys and z = scale * q . k:
+      dV_j  = sum_i p_ij dO_i;   dp_ij = dO_i . V_j;
+      dz_ij = p_ij (dp_ij - sum_j' p_ij' dp_ij');
+      dQ_i  = scale * sum_j dz_ij K_j;   dK_j = scale * sum_i dz_ij Q_i,
+    summed over the query heads that read a KV head.  With ``key_subset`` the
+    probabilities are still those of the whole key set (the row's final
+    softmax) and only the listed keys' terms are returned: dK and dV of the
+    other keys are zero and dQ is the listed keys' share -- the contribution
+    one visiting block makes in a blockwise backward.  Returns (dQ [T, Hq, D],
+    dK [L, Hkv, D], dV [L, Hkv, Dv]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    d_out = np.asarray(d_out, dtype=np.float64)
+    T, Hq, D = q.shape
+    L, Hkv, _ = k.shape
+    q_pos = np.arange(T, dtype=np.int64) if q_pos is None else np.asarray(q_pos, dtype=np.int64)
+    k_pos = np.arange(L, dtype=np.int64) if k_pos is None else np.asarray(k_pos, dtype=np.int64)
+    keep = np.ones(L, dtype=bool)
+    if key_subset is not None:
+        keep[:] = False
+        keep[np.asarray(key_subset, dtype=np.int64)] = True
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for h in range(Hq):
+        g = kv_head_of(h, Hq, Hkv)
+        z = scaled_logits(q[:, h, :], k[:, g, :], scale)
+        vis = causal_visible(q_pos, k_pos) if causal else np.ones((T, L), dtype=bool)
+        z = np.where(vis, z, NEG_INF)
+        zmax = z.max(axis=1, keepdims=True)
+        zmax = np.where(np.isneginf(zmax), 0.0, zmax)
+        w = np.where(vis, np.exp(z - zmax), 0.0)
+        den = w.sum(axis=1, keepdims=True)
+        p = np.divide(w, den, out=np.zeros_like(w), where=den > 0)
+        dp = d_out[:, h, :] @ v[:, g, :].T
+        dz = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+        pk = np.where(keep[None, :], p, 0.0)
+        dzk = np.where(keep[None, :], dz, 0.0)
+        dv[:, g, :] += pk.T @ d_out[:, h, :]
+        dq[:, h, :] = scale * (dzk @ k[:, g, :])
+        dk[:, g, :] += scale * (dzk.T @ q[:, h, :])
+    return dq, dk, dv
+
+
+def backward_ring(q_blocks, kv_blocks, d_out_blocks, scale, causal=False, block_len=None):
+    """Blockwise backward over an emulated ring ([RAC] section 7): device i keeps
+    Q_i, dO_i and its forward's log-sum-exp; the K/V blocks (with their dK, dV
+    buffers) visit in reverse ring order; each visit adds the block's terms to
+    the device's dQ and to the visiting block's dK and dV.  Returns
+    (dQ per device, dK per block, dV per block)."""
+    n = len(q_blocks)
+    if block_len is None:
+        block_len = np.asarray(q_blocks[0]).shape[0]
+    k_all = np.concatenate([np.asarray(kv[0], dtype=np.float64) for kv in kv_blocks])
+    v_all = np.concatenate([np.asarray(kv[1], dtype=np.float64) for kv in kv_blocks])
+    k_pos = np.arange(k_all.shape[0])
+    dqs = [np.zeros(np.asarray(qb).shape) for qb in q_blocks]
+    dks = [np.zeros(np.asarray(kv[0]).shape) for kv in kv_blocks]
+    dvs = [np.zeros(np.asarray(kv[1]).shape) for kv in kv_blocks]
+    for i in range(n):
+        q_pos = i * block_len + np.arange(np.asarray(q_blocks[i]).shape[0])
+        for t in reversed(range(n)):       # the forward's visits, last first
+            b = (i - t) % n
+            sub = np.arange(b * block_len, (b + 1) * block_len)
+            dq, dk, dv = attention_grads(q_blocks[i], k_all, v_all, d_out_blocks[i], scale, q_pos, k_pos,
+                                         causal, key_subset=sub)
+            dqs[i] += dq
+            dks[b] += dk[sub]
+            dvs[b] += dv[sub]
+    return dqs, dks, dvs
+
+
 # ---------------------------------------------------------------- load-balanced causal shares
 # [RAC] section 5, "Causal Masking and Load Balancing: Striped vs. Zigzag Ring
 # Attention": which tokens device k of n holds.  Each function returns the

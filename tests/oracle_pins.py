@@ -345,6 +345,94 @@ def pin_fanout_prefill():
         _close(lse[b], LSE, 1e-13, 0, "prefill brute lse")
 
 
+def _loss_and_grads_fd(q, k, v, d_out, scale, q_pos, k_pos, causal, eps=1e-6):
+    """Central finite differences of sum(A * d_out) -- independent of any gradient formula."""
+    def loss(q_, k_, v_):
+        a, _, _, _ = ora.attend(q_, k_, v_, scale, q_pos, k_pos, causal)
+        return float((a * d_out).sum())
+    grads = []
+    for which in range(3):
+        base = [q.copy(), k.copy(), v.copy()]
+        x = base[which]
+        gx = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            old = x[idx]
+            x[idx] = old + eps
+            lp = loss(*base)
+            x[idx] = old - eps
+            lm = loss(*base)
+            x[idx] = old
+            gx[idx] = (lp - lm) / (2 * eps)
+        grads.append(gx)
+    return grads
+
+
+def pin_attention_grads_finite_differences():
+    """dQ, dK, dV against central finite differences of the forward, GQA, causal and not."""
+    g = _rng(95)
+    T, L, Hq, Hkv, D = 4, 5, 4, 2, 3
+    q = g.standard_normal((T, Hq, D))
+    k = g.standard_normal((L, Hkv, D))
+    v = g.standard_normal((L, Hkv, D))
+    d_out = g.standard_normal((T, Hq, D))
+    s = 0.7
+    for causal in (False, True):
+        q_pos = np.arange(T) + 1
+        k_pos = np.arange(L)
+        dq, dk, dv = ora.attention_grads(q, k, v, d_out, s, q_pos, k_pos, causal)
+        fq, fk, fv = _loss_and_grads_fd(q, k, v, d_out, s, q_pos, k_pos, causal)
+        _close(dq, fq, 1e-6, 1e-8, "dQ vs finite differences")
+        _close(dk, fk, 1e-6, 1e-8, "dK vs finite differences")
+        _close(dv, fv, 1e-6, 1e-8, "dV vs finite differences")
+
+
+def pin_attention_grads_autograd():
+    """dQ, dK, dV against torch autograd (float64, CPU) of a plain masked softmax attention."""
+    import torch
+    g = _rng(96)
+    T, L, Hq, Hkv, D = 6, 9, 4, 2, 5
+    q = g.standard_normal((T, Hq, D))
+    k = g.standard_normal((L, Hkv, D))
+    v = g.standard_normal((L, Hkv, D))
+    d_out = g.standard_normal((T, Hq, D))
+    s = 1.0 / math.sqrt(D)
+    q_pos = np.arange(T) + 3
+    k_pos = np.arange(L)
+    dq, dk, dv = ora.attention_grads(q, k, v, d_out, s, q_pos, k_pos, True)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    G = Hq // Hkv
+    kk = tk.repeat_interleave(G, dim=1)
+    vv = tv.repeat_interleave(G, dim=1)
+    z = torch.einsum("thd,lhd->htl", tq, kk) * s
+    mask = torch.tensor(k_pos[None, :] <= q_pos[:, None])
+    z = z.masked_fill(~mask[None], float("-inf"))
+    a = torch.einsum("htl,lhd->thd", torch.softmax(z, dim=-1), vv)
+    (a * torch.tensor(d_out)).sum().backward()
+    _close(dq, tq.grad.numpy(), 1e-12, 1e-13, "dQ vs autograd")
+    _close(dk, tk.grad.numpy(), 1e-12, 1e-13, "dK vs autograd")
+    _close(dv, tv.grad.numpy(), 1e-12, 1e-13, "dV vs autograd")
+
+
+def pin_backward_ring_is_full_gradient():
+    """Reverse-ring blockwise backward (per-block terms with the row's final
+    softmax) sums to the gradient of plain causal attention."""
+    g = _rng(97)
+    n, B, Hq, Hkv, D = 3, 4, 4, 2, 6
+    S = n * B
+    q = g.standard_normal((S, Hq, D))
+    k = g.standard_normal((S, Hkv, D))
+    v = g.standard_normal((S, Hkv, D))
+    d_out = g.standard_normal((S, Hq, D))
+    s = 1.0 / math.sqrt(D)
+    dq, dk, dv = ora.attention_grads(q, k, v, d_out, s, np.arange(S), np.arange(S), True)
+    blocks = [slice(i * B, (i + 1) * B) for i in range(n)]
+    dqs, dks, dvs = ora.backward_ring([q[b] for b in blocks], [(k[b], v[b]) for b in blocks],
+                                      [d_out[b] for b in blocks], s, causal=True, block_len=B)
+    _close(np.concatenate(dqs), dq, 1e-12, 1e-13, "ring dQ")
+    _close(np.concatenate(dks), dk, 1e-12, 1e-13, "ring dK")
+    _close(np.concatenate(dvs), dv, 1e-12, 1e-13, "ring dV")
+
+
 def pin_finalize_empty():
     a, lse = ora.finalize(np.array([-np.inf, 0.5]), np.array([0.0, 2.0]), np.array([[0.0, 0.0], [1.0, -3.0]]))
     assert np.all(a[0] == 0) and np.isneginf(lse[0])
@@ -450,6 +538,9 @@ ALL_PINS = [
     pin_ring_emulation,
     pin_fanout_decode,
     pin_fanout_prefill,
+    pin_attention_grads_finite_differences,
+    pin_attention_grads_autograd,
+    pin_backward_ring_is_full_gradient,
     pin_finalize_empty,
     pin_zigzag_printed_allocation,
     pin_layouts_partition,

@@ -118,7 +118,47 @@ def _prefill_offset_by_one(q, prefix_k, prefix_v, suffix_k, suffix_v, scale):
     return a, lse
 
 
+_orig_grads = ora.attention_grads
+
+
+def _grads_without_delta(q, k, v, d_out, scale, q_pos=None, k_pos=None, causal=False, key_subset=None):
+    # dz = p * dp: the row term sum_j p_ij dp_ij of the softmax Jacobian dropped
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    d_out = np.asarray(d_out, dtype=np.float64)
+    T, Hq, D = q.shape
+    L, Hkv, _ = k.shape
+    q_pos = np.arange(T) if q_pos is None else np.asarray(q_pos)
+    k_pos = np.arange(L) if k_pos is None else np.asarray(k_pos)
+    keep = np.ones(L, dtype=bool)
+    if key_subset is not None:
+        keep[:] = False
+        keep[np.asarray(key_subset)] = True
+    dq, dk, dv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        z = scale * (q[:, h] @ k[:, g].T)
+        vis = (k_pos[None, :] <= q_pos[:, None]) if causal else np.ones((T, L), dtype=bool)
+        z = np.where(vis, z, -np.inf)
+        w = np.where(vis, np.exp(z - z.max(axis=1, keepdims=True)), 0.0)
+        p = w / w.sum(axis=1, keepdims=True)
+        dz = p * (d_out[:, h] @ v[:, g].T)
+        pk, dzk = np.where(keep[None], p, 0.0), np.where(keep[None], dz, 0.0)
+        dv[:, g] += pk.T @ d_out[:, h]
+        dq[:, h] = scale * (dzk @ k[:, g])
+        dk[:, g] += scale * (dzk.T @ q[:, h])
+    return dq, dk, dv
+
+
+def _grads_dk_unscaled(q, k, v, d_out, scale, q_pos=None, k_pos=None, causal=False, key_subset=None):
+    dq, dk, dv = _orig_grads(q, k, v, d_out, scale, q_pos, k_pos, causal, key_subset)
+    return dq, dk / scale, dv
+
+
 MUTATIONS = {
+    "softmax Jacobian row term dropped": ("attention_grads", _grads_without_delta),
+    "dK missing the scale": ("attention_grads", _grads_dk_unscaled),
     "prefill new tokens one position early": ("fanout_prefill", _prefill_offset_by_one),
     "zigzag mirror chunk off by one": ("zigzag_tokens", _zigzag_mirror_off_by_one),
     "striped residue shifted": ("striped_tokens", _striped_shifted),
