@@ -75,7 +75,7 @@ EXPORTS = [
     "blockattn_fwd_block", "blockattn_fwd_workspace_bytes", "blockattn_shard_states",
     "blockattn_shard_workspace_bytes", "blockattn_merge_states", "blockattn_finalize",
     "fanout_prefix_decode", "fanout_workspace_bytes", "fanout_prefix_prefill",
-    "fanout_prefill_workspace_bytes", "blockattn_status_str",
+    "fanout_prefill_workspace_bytes", "blockattn_bwd_delta", "blockattn_bwd_block", "blockattn_status_str",
     "blockattn_last_error", "blockattn_abi_version",
 ]
 
@@ -119,6 +119,11 @@ def load():
     lib.fanout_prefix_decode.restype = i32
     lib.fanout_workspace_bytes.argtypes = [P(Fanout)]
     lib.fanout_workspace_bytes.restype = sz
+    lib.blockattn_bwd_delta.argtypes = [i64, i32, vp, i32, i64, vp, i64, vp, vp]
+    lib.blockattn_bwd_delta.restype = i32
+    lib.blockattn_bwd_block.argtypes = [P(Problem), vp, vp, vp, vp, P(KVBlock), i32, P(i32), i32, vp,
+                                        P(ctypes.c_void_p), P(ctypes.c_void_p), vp]
+    lib.blockattn_bwd_block.restype = i32
     lib.fanout_prefix_prefill.argtypes = [P(FanoutPrefill), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.fanout_prefix_prefill.restype = i32
     lib.fanout_prefill_workspace_bytes.argtypes = [P(FanoutPrefill)]
@@ -332,3 +337,57 @@ def fanout_prefix_prefill(q, prefix_k, prefix_v, suffix_k, suffix_v, scale: floa
 
 def fanout_prefill_workspace_bytes(nb, T, Hq, Hkv, D, P, S) -> int:
     return load().fanout_prefill_workspace_bytes(ctypes.byref(FanoutPrefill(nb, T, Hq, Hkv, D, P, S, 0.0)))
+
+
+def bwd_delta(out: torch.Tensor, dout: torch.Tensor, delta: Optional[torch.Tensor] = None, stream=None):
+    """blockattn_bwd_delta: delta[r] = sum_d dout[r, d] * out[r, d] over rows in state-row order.
+
+    out: the forward's output ([rows, D] or [T, Hq, D], bf16 or fp32, rows contiguous);
+    dout: bf16 of the same shape."""
+    lib = load()
+    D = out.shape[-1]
+    o2 = out.reshape(-1, D)
+    g2 = dout.reshape(-1, D)
+    if o2.stride(1) != 1 or g2.stride(1) != 1 or dout.dtype != torch.bfloat16:
+        raise ValueError("out and dout need a contiguous last axis; dout must be bf16")
+    rows = o2.shape[0]
+    if delta is None:
+        delta = torch.empty(rows, dtype=torch.float32, device=out.device)
+    code = BA_BF16 if out.dtype == torch.bfloat16 else BA_F32
+    _check(lib.blockattn_bwd_delta(rows, D, _ptr(o2), code, o2.stride(0), _ptr(g2), g2.stride(0), _ptr(delta),
+                                   _stream(stream)), "blockattn_bwd_delta")
+    return delta
+
+
+def bwd_block(q: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor, delta: torch.Tensor,
+              blocks: Sequence[Tuple[torch.Tensor, torch.Tensor, int]], order: Optional[Sequence[int]],
+              dq: torch.Tensor, dkv: Sequence[Tuple[torch.Tensor, torch.Tensor]], *, n_kv_heads: int,
+              q_pos0: int = 0, causal: bool = False, scale: float = 0.0, stream=None):
+    """blockattn_bwd_block: accumulate dq [T*Hq, D] and each visited block's (dk, dv) [len, Hkv, D]
+    (all fp32) over the visits of one forward call.  dout has q's shape and strides (bf16)."""
+    lib = load()
+    if dout.shape != q.shape or dout.stride() != q.stride() or dout.dtype != torch.bfloat16:
+        raise ValueError("dout must be bf16 with q's shape and strides")
+    p = make_problem(q, n_kv_heads, q_pos0, causal, scale, 0)
+    arr = make_blocks(blocks)
+    n_visit = len(order) if order is not None else len(blocks)
+    order_arr = (ctypes.c_int32 * max(1, n_visit))(*(order or []))
+    dks = (ctypes.c_void_p * max(1, len(blocks)))(*[t[0].data_ptr() for t in dkv])
+    dvs = (ctypes.c_void_p * max(1, len(blocks)))(*[t[1].data_ptr() for t in dkv])
+    T, Hq, D = q.shape
+    if dq.dtype != torch.float32 or not dq.is_contiguous() or dq.numel() != T * Hq * D:
+        raise ValueError("dq must be contiguous fp32 with q_len * n_q_heads * head_dim elements")
+    if lse.numel() != T * Hq or delta.numel() != T * Hq:
+        raise ValueError("lse and delta need one fp32 entry per (token, query head)")
+    if len(dkv) != len(blocks):
+        raise ValueError("one (dk, dv) pair per block")
+    for (kb, _, _), (dk, dv) in zip(blocks, dkv):
+        want = (kb.shape[0], n_kv_heads, D)
+        if dk.dtype != torch.float32 or dv.dtype != torch.float32 or not dk.is_contiguous() or not dv.is_contiguous():
+            raise ValueError("dk and dv must be contiguous fp32")
+        if tuple(dk.shape) != want or tuple(dv.shape) != want:
+            raise ValueError(f"dk and dv of a block of {kb.shape[0]} keys must have shape {want}")
+    _check(lib.blockattn_bwd_block(ctypes.byref(p), _ptr(q), _ptr(dout), _ptr(lse), _ptr(delta), arr, len(blocks),
+                                   order_arr if order is not None else None, n_visit, _ptr(dq), dks, dvs,
+                                   _stream(stream)), "blockattn_bwd_block")
+    return dq, dkv

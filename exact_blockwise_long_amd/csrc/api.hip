@@ -331,6 +331,85 @@ ba_status blockattn_fwd_block(const ba_problem* p, const void* q, const ba_kv_bl
   return hip_status(ba::launch_merge_groups(mg, D, stream), "fwd_block merge launch");
 }
 
+ba_status blockattn_bwd_delta(int64_t rows, int32_t head_dim, const void* out, int32_t out_dtype,
+                              int64_t out_row_stride, const void* dout, int64_t dout_row_stride, float* delta,
+                              hipStream_t stream) {
+  if (head_dim != 64 && head_dim != 128) return fail(BA_ERR_SHAPE, "head_dim %d", head_dim);
+  if (rows < 0) return fail(BA_ERR_SHAPE, "rows %lld < 0", (long long)rows);
+  if (out_dtype != BA_BF16 && out_dtype != BA_F32) return fail(BA_ERR_UNSUPPORTED, "out dtype %d", out_dtype);
+  if (rows == 0) return ok();
+  if (!out || !dout || !delta) return fail(BA_ERR_NULL, "out, dout or delta is NULL");
+  if (out_row_stride < head_dim || dout_row_stride < head_dim)
+    return fail(BA_ERR_SHAPE, "row strides must be >= head_dim");
+  if (out_row_stride % 8 != 0 || dout_row_stride % 8 != 0)
+    return fail(BA_ERR_SHAPE, "row strides must be multiples of 8 elements");
+  if (((uintptr_t)out % 16) != 0 || ((uintptr_t)dout % 16) != 0) return fail(BA_ERR_SHAPE, "out/dout not 16-byte aligned");
+  ba::DeltaArgs a;
+  memset(&a, 0, sizeof(a));
+  a.rows = rows;
+  a.out = out;
+  a.out_bf16 = out_dtype == BA_BF16 ? 1 : 0;
+  a.out_stride = out_row_stride;
+  a.dout = dout;
+  a.dout_stride = dout_row_stride;
+  a.delta = delta;
+  return hip_status(ba::launch_delta(a, head_dim, stream), "bwd_delta launch");
+}
+
+ba_status blockattn_bwd_block(const ba_problem* p, const void* q, const void* dout, const float* lse,
+                              const float* delta, const ba_kv_block* blocks, int32_t n_blocks, const int32_t* order,
+                              int32_t n_visit, float* dq, float* const* dk, float* const* dv, hipStream_t stream) {
+  ba_status st = check_problem(p, q);
+  if (st) return st;
+  if (p->dtype != BA_BF16) return fail(BA_ERR_UNSUPPORTED, "the backward pass is bf16 only");
+  if (n_blocks < 0) return fail(BA_ERR_SHAPE, "n_blocks %d < 0", n_blocks);
+  if (n_visit > 0 && !blocks) return fail(BA_ERR_NULL, "blocks is NULL");
+  Visits v;
+  st = resolve_order(n_blocks, order, n_visit, v);
+  if (st) return st;
+  for (int j : v.idx) {
+    st = check_block(blocks[j], j, p->dtype);
+    if (st) return st;
+  }
+  if (p->q_len == 0 || v.idx.empty()) return ok();
+  if (!dout || !lse || !delta || !dq) return fail(BA_ERR_NULL, "dout, lse, delta or dq is NULL");
+  if (((uintptr_t)dout % 16) != 0 || ((uintptr_t)dq % 16) != 0) return fail(BA_ERR_SHAPE, "dout/dq not 16-byte aligned");
+  if (!dk || !dv) return fail(BA_ERR_NULL, "dk or dv pointer array is NULL");
+  const int D = p->head_dim;
+  const int64_t R = (int64_t)p->q_len * p->n_q_heads;
+  const int64_t q_extent =
+      ((int64_t)(p->q_len - 1) * p->q_stride_token + (int64_t)(p->n_q_heads - 1) * p->q_stride_head + D) * 2;
+  if (q_extent > (int64_t)UINT32_MAX || R * 4 > (int64_t)UINT32_MAX)
+    return fail(BA_ERR_SHAPE, "the backward pass addresses q, dout, lse and delta with 32-bit offsets");
+  ba::BwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.qs = make_qside(p, q);
+  a.dout = dout;
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.scale = a.qs.c / ba::kLog2e;
+  a.q_bytes = (uint32_t)q_extent;
+  a.rows_bytes = (uint32_t)(R * 4);
+  a.n_seg = 0;
+  int tiles = 0;
+  for (int j : v.idx) {
+    if (usable_keys(p, blocks[j]) == 0) continue;   // causal future or empty: no gradient terms
+    if (!dk[j] || !dv[j]) return fail(BA_ERR_NULL, "dk or dv of visited block %d is NULL", j);
+    if (((uintptr_t)dk[j] % 16) != 0 || ((uintptr_t)dv[j] % 16) != 0)
+      return fail(BA_ERR_SHAPE, "dk/dv of block %d not 16-byte aligned", j);
+    a.seg[a.n_seg] = make_seg(blocks[j]);
+    a.dk[a.n_seg] = dk[j];
+    a.dv[a.n_seg] = dv[j];
+    a.tile_begin[a.n_seg] = tiles;
+    tiles += (int)((blocks[j].len + 63) / 64);
+    ++a.n_seg;
+  }
+  a.tile_begin[a.n_seg] = tiles;
+  if (a.n_seg == 0) return ok();
+  return hip_status(ba::launch_bwd_bf16(a, tiles, D, stream), "bwd_block launch");
+}
+
 size_t blockattn_shard_workspace_bytes(const ba_problem* p, const ba_kv_block* blocks, int32_t n_blocks) {
   if (check_problem(p, (const void*)256) != BA_OK || !blocks || n_blocks <= 0 || n_blocks > BLOCKATTN_MAX_VISITS)
     return 0;

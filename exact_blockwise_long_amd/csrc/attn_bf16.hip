@@ -33,100 +33,10 @@
 //    the O rescale is skipped for the whole wave in almost every tile.  The
 //    true running max is tracked alongside and the state is renormalised to it
 //    when written, so the stored (m, l, O) is exactly the recurrence's.
-#include "internal.h"
+#include "bf16_tiles.h"
 
 namespace ba {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
-
-constexpr int kThreads = 256;
-constexpr int kTileKeys = 64;
-constexpr float kTau = 8.0f;   // lazy-rescale headroom, log2 units
-
-template <int D>
-struct Cfg {
-  static constexpr int ROWB = D * 2;                  // bytes per K or V row in LDS
-  static constexpr int CPR = D / 8;                   // 16-byte chunks per row
-  static constexpr int TILEB = kTileKeys * ROWB;      // bytes of one K (or V) tile
-  static constexpr int STAGEB = 2 * TILEB;            // K tile then V tile
-  static constexpr int RPI = 64 / CPR;                // rows per wave-wide 1 KiB load
-  static constexpr int LPW = kTileKeys / RPI / 4;     // loads per wave per tile (each of K and V)
-  static constexpr int DC = D / 32;                   // 32-wide d chunks (QK^T K-dim steps)
-  static constexpr int DB = D / 16;                   // 16-wide d blocks of O^T
-};
-
-// Chunk swizzles (XOR on the 16-byte chunk index within a row).
-template <int D>
-__device__ inline int swz_k(int row) { return D == 128 ? (row & 15) : (row & 7); }
-template <int D>
-__device__ inline int swz_v(int row) { return D == 128 ? ((row & 7) << 1) : ((row & 3) << 1); }
-
-// Reductions over the 4 lanes that share lane % 16 (one query column).
-//
-// v_permlane16_swap(a, b) returns (a with its odd 16-lane rows replaced by
-// b's even rows, b with its even rows replaced by a's odd rows); with a = b = x
-// the two results hold x and its lane ^ 16 partner, so combining them is one
-// butterfly step, and v_permlane32_swap likewise pairs lane ^ 32 (checked on
-// the hardware).  Registers only, no LDS crossbar.  (The two results are
-// copied to scalars before the bit casts: a bit cast applied directly to an
-// element of the returned vector reads element 0 with this compiler.)
-struct PairF {
-  float a, b;
-};
-__device__ inline PairF swap16(float x) {
-  const unsigned u = __builtin_bit_cast(unsigned, x);
-  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  const unsigned r0 = r[0], r1 = r[1];
-  return PairF{__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1)};
-}
-__device__ inline PairF swap32(float x) {
-  const unsigned u = __builtin_bit_cast(unsigned, x);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  const unsigned r0 = r[0], r1 = r[1];
-  return PairF{__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1)};
-}
-__device__ inline float xor16_pair_max(float x) { const PairF p = swap16(x); return fmaxf(p.a, p.b); }
-__device__ inline float xor32_pair_max(float x) { const PairF p = swap32(x); return fmaxf(p.a, p.b); }
-__device__ inline float xor16_pair_sum(float x) { const PairF p = swap16(x); return p.a + p.b; }
-__device__ inline float xor32_pair_sum(float x) { const PairF p = swap32(x); return p.a + p.b; }
-__device__ inline float wave_max_cols(float x) { return xor32_pair_max(xor16_pair_max(x)); }
-__device__ inline float wave_sum_cols(float x) { return xor32_pair_sum(xor16_pair_sum(x)); }
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-// Two floats to a packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32).
-__device__ inline bf16x2 pack_bf16x2(float a, float b) { return __builtin_convertvector(f32x2{a, b}, bf16x2); }
-
-// One 16-byte-per-lane buffer load straight into LDS (buffer_load_dwordx4 ...
-// lds): lane i's bytes land at dst + 16 * i.  The host compilation pass never
-// runs device code but rejects this builtin in some template contexts, so the
-// call is compiled for the device only.
-__device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t dst, uint32_t voff, uint32_t soff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(size_t)dst, 16, voff, soff, 0, 0);
-#endif
-}
-
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// Per-workgroup description of the query rows.
-struct RowCtx {
-  int f0, f1;              // flat row range [f0, f1) of this tile
-  int g;                   // KV head
-  int64_t qpos_min, qpos_max;
-};
 
 // Per-lane registers of the running state for the wave's 2 column blocks.
 template <int D>
@@ -136,73 +46,6 @@ struct Acc {
   float mt[2];             // true running max (base 2)
   float lp[2];             // per-lane partial of the denominator, relative to m2
 };
-
-// A key range as the kernels see it: buffer resources over K and V of one KV
-// head, the byte stride between keys, the absolute position of key 0 and the
-// number of keys.  Reads past the range return zeros (buffer range check).
-struct KVSrc {
-  __amdgpu_buffer_rsrc_t k, v;
-  uint32_t kst, vst;       // bytes between consecutive keys
-  int64_t pos0;
-  int n;
-};
-
-template <int D>
-__device__ inline KVSrc make_src(const Seg& s, int g) {
-  KVSrc r;
-  const char* kb = (const char*)s.k + (int64_t)g * s.ks_h * 2;
-  const char* vb = (const char*)s.v + (int64_t)g * s.vs_h * 2;
-  r.kst = (uint32_t)(s.ks_t * 2);
-  r.vst = (uint32_t)(s.vs_t * 2);
-  r.k = make_rsrc(kb, s.n > 0 ? (uint32_t)((s.n - 1) * (int64_t)r.kst + D * 2) : 0u);
-  r.v = make_rsrc(vb, s.n > 0 ? (uint32_t)((s.n - 1) * (int64_t)r.vst + D * 2) : 0u);
-  r.pos0 = s.pos0;
-  r.n = s.n;
-  return r;
-}
-
-// Per-lane byte offsets, within a tile, of the 16-byte chunks this lane moves:
-// wave-wide load j carries RPI whole rows; lane (row r, chunk position p)
-// fetches the global chunk p ^ swizzle(r), which is where the operand reads
-// look for it.  They depend only on the key strides, so they are computed once
-// per segment.
-template <int D>
-struct LaneOffs {
-  uint32_t k[Cfg<D>::LPW];
-  uint32_t v[Cfg<D>::LPW];
-};
-
-template <int D>
-__device__ inline LaneOffs<D> lane_offsets(const KVSrc& src, int wave, int lane) {
-  using C = Cfg<D>;
-  LaneOffs<D> o;
-  const int rsub = lane / C::CPR;
-  const int p = lane % C::CPR;
-#pragma unroll
-  for (int j = 0; j < C::LPW; ++j) {
-    const int row = (wave * C::LPW + j) * C::RPI + rsub;
-    o.k[j] = (uint32_t)row * src.kst + (uint32_t)((p ^ swz_k<D>(row)) * 16);
-    o.v[j] = (uint32_t)row * src.vst + (uint32_t)((p ^ swz_v<D>(row)) * 16);
-  }
-  return o;
-}
-
-// Issue the HBM -> LDS loads of the 64-key tile starting at key k0 of `src`.
-// Keys past the end of the range read as zeros (buffer range check); their
-// scores are masked, so their P is exactly 0.
-// `stage` is the LDS byte address of the stage.
-template <int D>
-__device__ inline void issue_tile(const KVSrc& src, const LaneOffs<D>& offs, int k0, uint32_t stage, int wave) {
-  using C = Cfg<D>;
-  const uint32_t soff_k = (uint32_t)k0 * src.kst;
-  const uint32_t soff_v = (uint32_t)k0 * src.vst;
-#pragma unroll
-  for (int j = 0; j < C::LPW; ++j) {
-    const uint32_t rbase = (uint32_t)((wave * C::LPW + j) * C::RPI);
-    lds_dma16(src.k, stage + rbase * C::ROWB, offs.k[j], soff_k);
-    lds_dma16(src.v, stage + C::TILEB + rbase * C::ROWB, offs.v[j], soff_v);
-  }
-}
 
 // One 64-key tile for one wave: S^T = K Q^T, online-softmax update, O^T += V^T P^T.
 template <int D>
@@ -323,41 +166,6 @@ __device__ inline void tile_compute(const lds_char* stage, int lane, const bf16x
   }
 }
 
-// Number of keys of segment `s` that some row of the tile can see.
-__device__ inline int seg_effective(const Seg& s, const QSide& qs, const RowCtx& rc) {
-  if (!qs.causal) return s.n;
-  int64_t lim = rc.qpos_max - s.pos0 + 1;
-  if (lim <= 0) return 0;
-  return (int)min((int64_t)s.n, lim);
-}
-
-// The per-lane row bookkeeping shared by every kernel.  Cheap to recompute,
-// so the kernels rebuild it after the key loop instead of keeping it live.
-struct LaneRows {
-  int qrel[2];       // query position minus the tile's first query position
-  int64_t srow[2];   // state row t*Hq + h
-  bool valid[2];
-  const uint16_t* qptr[2];
-};
-
-__device__ inline LaneRows lane_rows(const QSide& qs, const RowCtx& rc, int wave, int lane) {
-  LaneRows lr;
-  const int t0 = rc.f0 / qs.G;
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    int f = rc.f0 + wave * 32 + qb * 16 + (lane & 15);
-    lr.valid[qb] = f < rc.f1;
-    int fc = min(f, rc.f1 - 1);
-    int t = fc / qs.G;
-    int j = fc - t * qs.G;
-    int h = rc.g * qs.G + j;
-    lr.qrel[qb] = t - t0;
-    lr.srow[qb] = (int64_t)t * qs.Hq + h;
-    lr.qptr[qb] = (const uint16_t*)qs.q + (int64_t)t * qs.qs_t + (int64_t)h * qs.qs_h;
-  }
-  return lr;
-}
-
 template <int D>
 __device__ inline void load_q(const LaneRows& lr, int lane, bf16x8 (&qf)[2][Cfg<D>::DC]) {
 #pragma unroll
@@ -418,102 +226,6 @@ __device__ inline void store_acc(Acc<D>& acc, const LaneRows& lr, int lane, floa
   }
 }
 
-__device__ inline void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// The key-tile loop over a list of segments, double-buffered through LDS: the
-// next tile loads while the current one is multiplied.  One barrier per tile:
-// after it, every wave's loads of the tile about to be used have landed and
-// every wave is done with the stage the next load overwrites.  The loop is
-// unrolled by two so each stage's LDS offsets are compile-time constants.
-// Segment bookkeeping (visible key count, buffer resources, per-lane offsets)
-// runs only when a cursor crosses into another segment.
-template <int D, class GetSeg>
-__device__ inline void run_segments(const QSide& qs, const RowCtx& rc, const LaneRows& lr, int n_seg,
-                                    GetSeg get_seg, const bf16x8 (&qf)[2][Cfg<D>::DC], Acc<D>& acc,
-                                    lds_char* lds, bool wave_active) {
-  using C = Cfg<D>;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-
-  // First segment at or after s with a key some row of the tile can see.
-  auto next_nonempty = [&](int s, int& n_eff) {
-    for (; s < n_seg; ++s) {
-      n_eff = seg_effective(get_seg(s), qs, rc);
-      if (n_eff > 0) return s;
-    }
-    n_eff = 0;
-    return n_seg;
-  };
-
-  // issue cursor
-  int is_n = 0;
-  int is = next_nonempty(0, is_n);
-  if (is >= n_seg) return;
-  int ik = 0;
-  KVSrc isrc = make_src<D>(get_seg(is), rc.g);
-  LaneOffs<D> ilo = lane_offsets<D>(isrc, wave, lane);
-  // compute cursor
-  int cs = is, ck = 0, cn = is_n;
-  int64_t cpos0 = get_seg(cs).pos0;
-
-  const uint32_t lds_addr = (uint32_t)(size_t)lds;
-  auto issue_next = [&](int stage_off) {
-    issue_tile<D>(isrc, ilo, ik, lds_addr + (uint32_t)stage_off, wave);
-    ik += kTileKeys;
-    if (ik >= is_n) {
-      is = next_nonempty(is + 1, is_n);
-      ik = 0;
-      if (is < n_seg) {
-        isrc = make_src<D>(get_seg(is), rc.g);
-        ilo = lane_offsets<D>(isrc, wave, lane);
-      }
-    }
-  };
-
-  // One tile: wait for it, let the next one start loading, multiply.
-  auto step = [&](int cur_off, int nxt_off) {
-    wait_all_loads();
-    __syncthreads();
-    if (is < n_seg) issue_next(nxt_off);
-    if (wave_active) {
-      const int n_valid = min(kTileKeys, cn - ck);
-      const int64_t kpos0 = cpos0 + ck;
-      const bool need_mask = (n_valid < kTileKeys) || (qs.causal && kpos0 + kTileKeys - 1 > rc.qpos_min);
-      // Visited keys satisfy kpos0 <= qpos_max, so the offset fits easily in 32 bits
-      // whenever a mask is needed; far-past tiles are clamped (never masked).
-      const int64_t krel64 = kpos0 - rc.qpos_min;
-      const int krel = (int)max((int64_t)-(1 << 30), min((int64_t)(1 << 30), krel64));
-      tile_compute<D>(lds + cur_off, lane, qf, acc, qs.c, need_mask, qs.causal != 0, n_valid, krel, lr.qrel);
-    }
-    ck += kTileKeys;
-    if (ck >= cn) {
-      cs = next_nonempty(cs + 1, cn);
-      ck = 0;
-      if (cs < n_seg) cpos0 = get_seg(cs).pos0;
-    }
-  };
-
-  issue_next(0);
-  while (true) {
-    step(0, C::STAGEB);
-    if (cs >= n_seg) break;
-    step(C::STAGEB, 0);
-    if (cs >= n_seg) break;
-  }
-  // Leave no load in flight into LDS that a later phase might reuse.
-  wait_all_loads();
-}
-
-__device__ inline RowCtx make_rowctx(const QSide& qs, int f0, int f1, int g) {
-  RowCtx rc;
-  rc.f0 = f0;
-  rc.f1 = f1;
-  rc.g = g;
-  rc.qpos_min = qs.q_pos0 + f0 / qs.G;
-  rc.qpos_max = qs.q_pos0 + (f1 - 1) / qs.G;
-  return rc;
-}
-
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void walk_kernel(WalkArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[2 * Cfg<D>::STAGEB];
@@ -538,8 +250,13 @@ __global__ __launch_bounds__(kThreads, 2) void walk_kernel(WalkArgs a) {
   else
     load_acc<D>(acc, lr, lane, a.m, a.l, a.o);
 
-  run_segments<D>(a.qs, rc, lr, a.n_seg, [&](int i) -> const Seg& { return a.seg[i]; }, qf, acc,
-                     (lds_char*)lds, wave_active);
+  const QSide& qs = a.qs;
+  run_segments<D>(
+      qs, rc, a.n_seg, [&](int i) -> const Seg& { return a.seg[i]; },
+      [&](const lds_char* stage, bool need_mask, int n_valid, int krel) {
+        tile_compute<D>(stage, lane, qf, acc, qs.c, need_mask, qs.causal != 0, n_valid, krel, lr.qrel);
+      },
+      (lds_char*)lds, wave_active);
   store_acc<D>(acc, lane_rows(a.qs, rc, wave, lane), lane, a.m, a.l, a.o, 0);
 }
 
@@ -570,7 +287,12 @@ __device__ inline void partial_job(const QSide& qs, int f0, int f1, int g, const
   load_q<D>(lr, lane, qf);
   Acc<D> acc;
   init_acc<D>(acc);
-  run_segments<D>(qs, rc, lr, 1, [&](int) -> const Seg& { return sg; }, qf, acc, lds, wave_active);
+  run_segments<D>(
+      qs, rc, 1, [&](int) -> const Seg& { return sg; },
+      [&](const lds_char* stage, bool need_mask, int n_valid, int krel) {
+        tile_compute<D>(stage, lane, qf, acc, qs.c, need_mask, qs.causal != 0, n_valid, krel, lr.qrel);
+      },
+      lds, wave_active);
   store_acc<D>(acc, lane_rows(qs, rc, wave, lane), lane, ws_m, ws_l, ws_o, row_base);
 }
 

@@ -1,0 +1,487 @@
+// Backward pass of the blockwise attention for gfx950 (bf16 inputs, fp32
+// gradients).
+//
+// "RingAttention and Context Parallelism" (llms.blog), section 7: the forward
+// keeps Q and the per-row log-sum-exp L = m + ln l; the backward visits the K/V
+// blocks again, recomputes each block's scores from Q and L, accumulates dQ for
+// the stationary query block and dK, dV for the visiting block.  With
+// P = exp(s - L) (the row's final softmax over every visited key):
+//   dV += P^T dO,  dP = dO V^T,  dS = P * (dP - D) with D = rowsum(dO * A),
+//   dQ += scale dS K,  dK += scale dS^T Q
+// (the chain rule of the attention definition of its section 1).
+//
+// Two kernels, no atomics, so results do not depend on scheduling:
+//  * dq_kernel walks key tiles for a tile of 128 query rows, exactly like the
+//    forward walk (the same LDS tile pipeline): S^T = K Q^T and dP^T = V dO^T
+//    with Q and dO in registers, then dQ^T += K^T dS^T with K^T read from the
+//    row-major K tile by ds_read_b64_tr_b16.
+//  * dkdv_kernel owns 64 keys of one visited block (16 per wave, their K and V
+//    in registers) and walks tiles of 64 query rows staged in LDS:
+//    S = Q K^T and dP = dO V^T put keys along the accumulator columns, so P and
+//    dS come out in the B-operand layout of dV^T += dO^T P and dK^T += Q^T dS,
+//    whose A operands are transposing reads of the dO and Q tiles.
+#include "bf16_tiles.h"
+
+namespace ba {
+namespace {
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// One 4-byte-per-lane buffer load straight into LDS: lane i's word lands at dst + 4 * i.
+__device__ inline void lds_dma4(__amdgpu_buffer_rsrc_t rsrc, uint32_t dst, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(size_t)dst, 4, voff, soff, 0, 0);
+#endif
+}
+
+// The log-sum-exp of a row in base 2, with rows that saw no key (L = -inf)
+// mapped to +inf so that exp2(s * c - L2) is 0 for them.
+__device__ inline float lse2(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }
+
+// ---------------------------------------------------------------- D = rowsum(dO * A)
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void delta_kernel(DeltaArgs a) {
+  constexpr int TPR = D / 8;                 // threads per row, 8 elements each
+  constexpr int RPB = kThreads / TPR;
+  const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int c8 = threadIdx.x % TPR;
+  float s = 0.f;
+  if (r < a.rows) {
+    const bf16x8 g = *(const bf16x8*)((const uint16_t*)a.dout + r * a.dout_stride + 8 * c8);
+    if (a.out_bf16) {
+      const bf16x8 o = *(const bf16x8*)((const uint16_t*)a.out + r * a.out_stride + 8 * c8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s = __builtin_fmaf((float)g[i], (float)o[i], s);
+    } else {
+      const float* o = (const float*)a.out + r * a.out_stride + 8 * c8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s = __builtin_fmaf((float)g[i], o[i], s);
+    }
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, TPR);
+  if (r < a.rows && c8 == 0) a.delta[r] = s;
+}
+
+// ---------------------------------------------------------------- dQ
+
+// One 64-key tile for one wave's 32 rows: dQ^T += K^T dS^T, one 32-key chunk
+// at a time (its scores, dS and products finish before the next chunk's start,
+// which keeps the live scores to one chunk).
+template <int D>
+__device__ inline void dq_tile(const lds_char* stage, int lane, const bf16x8 (&qf)[2][Cfg<D>::DC],
+                               const bf16x8 (&gf)[2][Cfg<D>::DC], f32x4 (&dq)[Cfg<D>::DB][2],
+                               const float (&l2)[2], const float (&dl)[2], float c, bool need_mask, bool causal,
+                               int n_valid, int krel, const int (&qrel)[2]) {
+  using C = Cfg<D>;
+  const lds_char* kl = stage;
+  const lds_char* vl = stage + C::TILEB;
+  const int lr = lane & 15;
+  const int lg = lane >> 4;
+#pragma unroll
+  for (int ch = 0; ch < 2; ++ch) {
+    // s[h][qb][i], dp[h][qb][i]: key 32*ch + 16*h + 4*lg + i against query column qb.
+    f32x4 s[2][2], dp[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        s[h][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dp[h][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int dc = 0; dc < C::DC; ++dc) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = 32 * ch + 16 * h + lr;
+        const bf16x8 kf = *(const lds_bf16x8*)(kl + row * C::ROWB + (((4 * dc + lg) ^ swz_k<D>(row)) * 16));
+        const bf16x8 vf = *(const lds_bf16x8*)(vl + row * C::ROWB + (((4 * dc + lg) ^ swz_v<D>(row)) * 16));
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          s[h][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][dc], s[h][qb], 0, 0, 0);
+          dp[h][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, gf[qb][dc], dp[h][qb], 0, 0, 0);
+        }
+      }
+    }
+    if (need_mask) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int lim = causal ? min(n_valid, qrel[qb] - krel + 1) : n_valid;
+        const int t = lim - 4 * lg;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (32 * ch + 16 * h + i >= t) s[h][qb][i] = -INFINITY;
+      }
+    }
+    // dS^T = P^T * (dP^T - D), rounded to bf16 in the B-operand layout of the
+    // product below (k-slot 8*lg + i: key 32*ch + 4*lg + i for i < 4,
+    // 32*ch + 16 + 4*lg + i - 4 otherwise).
+    bf16x8 df[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float d[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[h][qb][i], c, -l2[qb]));
+          d[h][i] = p * (dp[h][qb][i] - dl[qb]);
+        }
+      bf16x2 w[4];
+      w[0] = pack_bf16x2(d[0][0], d[0][1]);
+      w[1] = pack_bf16x2(d[0][2], d[0][3]);
+      w[2] = pack_bf16x2(d[1][0], d[1][1]);
+      w[3] = pack_bf16x2(d[1][2], d[1][3]);
+      df[qb] = __builtin_bit_cast(bf16x8, w);
+    }
+    // dQ^T[d][q] += sum_key K^T[d][key] dS^T[key][q]: K^T straight from the
+    // row-major K tile by transposing reads (the forward's V^T read on K).
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const int row0 = 32 * ch + 4 * lg + (lr >> 2);
+      const int row1 = row0 + 16;
+      const int cidx = 2 * db + ((lr & 3) >> 1);
+      const int half = (lr & 1) * 8;
+      const lds_char* a0 = kl + row0 * C::ROWB + ((cidx ^ swz_k<D>(row0)) * 16) + half;
+      const lds_char* a1 = kl + row1 * C::ROWB + ((cidx ^ swz_k<D>(row1)) * 16) + half;
+      const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a0);
+      const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a1);
+      const s16x8 xx = s16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      const bf16x8 kt = __builtin_bit_cast(bf16x8, xx);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        dq[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, df[qb], dq[db][qb], 0, 0, 0);
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
+  using C = Cfg<D>;
+  __shared__ __attribute__((aligned(16))) char lds[2 * C::STAGEB];
+  const QSide& qs = a.qs;
+  const int Hkv = qs.Hkv;
+  const int g = blockIdx.x % Hkv;
+  const int n_tiles = (qs.q_len * qs.G + kTileRows - 1) / kTileRows;
+  const int tile = n_tiles - 1 - (int)(blockIdx.x / Hkv);  // causal: longest rows first
+  const int total = qs.q_len * qs.G;
+  const int f0 = tile * kTileRows;
+  const int f1 = min(f0 + kTileRows, total);
+  const RowCtx rc = make_rowctx(qs, f0, f1, g);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const LaneRows lr = lane_rows(qs, rc, wave, lane);
+  const bool wave_active = f0 + wave * 32 < f1;
+
+  bf16x8 qf[2][C::DC], gf[2][C::DC];
+  float l2[2], dl[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int64_t off = lr.qptr[qb] - (const uint16_t*)qs.q;
+    const uint16_t* gp = (const uint16_t*)a.dout + off;
+#pragma unroll
+    for (int dc = 0; dc < C::DC; ++dc) {
+      qf[qb][dc] = *(const bf16x8*)(lr.qptr[qb] + 32 * dc + 8 * (lane >> 4));
+      gf[qb][dc] = *(const bf16x8*)(gp + 32 * dc + 8 * (lane >> 4));
+    }
+    l2[qb] = lse2(a.lse[lr.srow[qb]]);
+    dl[qb] = a.delta[lr.srow[qb]];
+  }
+  f32x4 dq[C::DB][2];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) dq[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  run_segments<D>(
+      qs, rc, a.n_seg, [&](int i) -> const Seg& { return a.seg[i]; },
+      [&](const lds_char* stage, bool need_mask, int n_valid, int krel) {
+        dq_tile<D>(stage, lane, qf, gf, dq, l2, dl, qs.c, need_mask, qs.causal != 0, n_valid, krel, lr.qrel);
+      },
+      (lds_char*)lds, wave_active);
+
+  // dq[r, 16*db + 4*lg + i] += scale * dQ^T.
+  const LaneRows lw = lane_rows(qs, rc, wave, lane);
+  const int lg = lane >> 4;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    if (!lw.valid[qb] || !wave_active) continue;
+    float* dst = a.dq + lw.srow[qb] * D + 4 * lg;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      f32x4 v = *(f32x4*)(dst + 16 * db);
+      v += dq[db][qb] * a.scale;
+      *(f32x4*)(dst + 16 * db) = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dK, dV
+
+constexpr int kRowTile = 64;   // query rows per LDS stage of the dK/dV kernel
+
+template <int D>
+struct BwdCfg {
+  static constexpr int ROWB = D * 2;
+  static constexpr int CPR = D / 8;
+  static constexpr int TILEB = kRowTile * ROWB;        // one Q (or dO) tile
+  static constexpr int STAGEB = 2 * TILEB + 2 * kRowTile * 4;  // Q, dO, L2, D
+  static constexpr int RPI = 64 / CPR;                 // rows per wave-wide 1 KiB load
+  static constexpr int LPW = kRowTile / RPI / 4;       // loads per wave per tile
+  static constexpr int DC = D / 32;
+  static constexpr int DB = D / 16;
+};
+
+// Issues the loads of query-row tile f0 .. f0 + 63 (flat rows of KV head g)
+// into the stage at `stage`: Q and dO rows (swizzled as K tiles are), then the
+// rows' log-sum-exp and D.  Rows past the last are loaded as the last row; the
+// caller masks them.
+template <int D>
+__device__ inline void issue_rows(const BwdArgs& a, __amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rg,
+                                  __amdgpu_buffer_rsrc_t rl, __amdgpu_buffer_rsrc_t rd, int f0, int g,
+                                  uint32_t stage, int wave, int lane) {
+  using C = BwdCfg<D>;
+  const QSide& qs = a.qs;
+  const int total = qs.q_len * qs.G;
+  const int rsub = lane / C::CPR;
+  const int p = lane % C::CPR;
+#pragma unroll
+  for (int j = 0; j < C::LPW; ++j) {
+    const int row = (wave * C::LPW + j) * C::RPI + rsub;
+    const int f = min(f0 + row, total - 1);
+    const int t = f / qs.G;
+    const int h = g * qs.G + (f - t * qs.G);
+    const uint32_t off = (uint32_t)(((int64_t)t * qs.qs_t + (int64_t)h * qs.qs_h) * 2) + (uint32_t)((p ^ swz_k<D>(row)) * 16);
+    const uint32_t dst = stage + (uint32_t)((wave * C::LPW + j) * C::RPI) * C::ROWB;
+    lds_dma16(rq, dst, off, 0);
+    lds_dma16(rg, dst + C::TILEB, off, 0);
+  }
+  if (wave < 2) {
+    const int f = min(f0 + lane, total - 1);
+    const int t = f / qs.G;
+    const int h = g * qs.G + (f - t * qs.G);
+    const uint32_t off = (uint32_t)(((int64_t)t * qs.Hq + h) * 4);
+    lds_dma4(wave == 0 ? rl : rd, stage + 2 * C::TILEB + (uint32_t)(wave * kRowTile * 4), off, 0);
+  }
+}
+
+// One tile of 64 query rows for one wave's 16 keys.
+template <int D>
+__device__ inline void dkdv_tile(const lds_char* stage, int lane, const bf16x8 (&kf)[BwdCfg<D>::DC],
+                                 const bf16x8 (&vf)[BwdCfg<D>::DC], f32x4 (&dk)[BwdCfg<D>::DB],
+                                 f32x4 (&dv)[BwdCfg<D>::DB], float c, bool need_mask, const QSide& qs, int f0,
+                                 int total, int key_idx, int n_keys, int64_t kpos) {
+  using C = BwdCfg<D>;
+  const lds_char* ql = stage;
+  const lds_char* gl = stage + C::TILEB;
+  const float* l2s = (const float*)(stage + 2 * C::TILEB);
+  const float* dls = l2s + kRowTile;
+  const int lr = lane & 15;
+  const int lg = lane >> 4;
+
+  // s[rb][i], dp[rb][i]: query row 16*rb + 4*lg + i of the tile against key lr.
+  f32x4 s[4], dp[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    s[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dp[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int dc = 0; dc < C::DC; ++dc) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int row = 16 * rb + lr;
+      const int off = row * C::ROWB + (((4 * dc + lg) ^ swz_k<D>(row)) * 16);
+      const bf16x8 qa = *(const lds_bf16x8*)(ql + off);
+      const bf16x8 ga = *(const lds_bf16x8*)(gl + off);
+      s[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[dc], s[rb], 0, 0, 0);
+      dp[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga, vf[dc], dp[rb], 0, 0, 0);
+    }
+  }
+  float p[4][4], d[4][4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const f32x4 l2 = *(const __attribute__((address_space(3))) f32x4*)(l2s + 16 * rb + 4 * lg);
+    const f32x4 dl = *(const __attribute__((address_space(3))) f32x4*)(dls + 16 * rb + 4 * lg);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float l2i = l2[i] == -INFINITY ? INFINITY : l2[i] * kLog2e;
+      p[rb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][i], c, -l2i));
+      d[rb][i] = p[rb][i] * (dp[rb][i] - dl[i]);
+    }
+  }
+  if (need_mask) {
+    // Key key_idx at absolute position kpos against flat row f0 + r.
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int f = f0 + 16 * rb + 4 * lg + i;
+        bool vis = key_idx < n_keys && f < total;
+        if (qs.causal) vis = vis && kpos <= qs.q_pos0 + f / qs.G;
+        if (!vis) {
+          p[rb][i] = 0.f;
+          d[rb][i] = 0.f;
+        }
+      }
+  }
+  // P and dS in the B-operand layout of the products over query rows: k-slot
+  // 8*lg + i of row chunk ch is row 32*ch + 4*lg + i (i < 4) or
+  // 32*ch + 16 + 4*lg + i - 4.
+  bf16x8 pf[2], df[2];
+#pragma unroll
+  for (int ch = 0; ch < 2; ++ch) {
+    bf16x2 w[4], x[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      w[2 * h] = pack_bf16x2(p[2 * ch + h][0], p[2 * ch + h][1]);
+      w[2 * h + 1] = pack_bf16x2(p[2 * ch + h][2], p[2 * ch + h][3]);
+      x[2 * h] = pack_bf16x2(d[2 * ch + h][0], d[2 * ch + h][1]);
+      x[2 * h + 1] = pack_bf16x2(d[2 * ch + h][2], d[2 * ch + h][3]);
+    }
+    pf[ch] = __builtin_bit_cast(bf16x8, w);
+    df[ch] = __builtin_bit_cast(bf16x8, x);
+  }
+  // dV^T[d][key] += sum_row dO^T[d][row] P[row][key];  dK^T += Q^T dS, with the
+  // transposed operands read from the row-major dO and Q tiles.
+#pragma unroll
+  for (int ch = 0; ch < 2; ++ch) {
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const int row0 = 32 * ch + 4 * lg + (lr >> 2);
+      const int row1 = row0 + 16;
+      const int cidx = 2 * db + ((lr & 3) >> 1);
+      const int half = (lr & 1) * 8;
+      const int o0 = row0 * C::ROWB + ((cidx ^ swz_k<D>(row0)) * 16) + half;
+      const int o1 = row1 * C::ROWB + ((cidx ^ swz_k<D>(row1)) * 16) + half;
+      const s16x4 g0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(gl + o0));
+      const s16x4 g1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(gl + o1));
+      const s16x4 q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(ql + o0));
+      const s16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(ql + o1));
+      const bf16x8 gt = __builtin_bit_cast(bf16x8, s16x8{g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]});
+      const bf16x8 qt = __builtin_bit_cast(bf16x8, s16x8{q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]});
+      dv[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gt, pf[ch], dv[db], 0, 0, 0);
+      dk[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt, df[ch], dk[db], 0, 0, 0);
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdArgs a) {
+  using C = BwdCfg<D>;
+  __shared__ __attribute__((aligned(16))) char lds[2 * C::STAGEB];
+  const QSide& qs = a.qs;
+  const int Hkv = qs.Hkv;
+  const int g = blockIdx.x % Hkv;
+  const int tile = blockIdx.x / Hkv;
+  int si = 0;
+  while (si + 1 < a.n_seg && a.tile_begin[si + 1] <= tile) ++si;
+  const Seg& sg = a.seg[si];
+  const int k0 = (tile - a.tile_begin[si]) * kTileKeys;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int key_idx = k0 + 16 * wave + (lane & 15);   // this lane's key (column of S)
+  const int n_keys = sg.n;
+  const int64_t kpos = sg.pos0 + key_idx;
+  const int total = qs.q_len * qs.G;
+
+  // The wave's 16 keys as B operands: key 16*wave + lane%16, d = 32*dc + 8*(lane/16) .. +7.
+  bf16x8 kf[C::DC], vf[C::DC];
+  {
+    const int kk = min(key_idx, n_keys - 1);
+    const uint16_t* kp = (const uint16_t*)sg.k + (int64_t)kk * sg.ks_t + (int64_t)g * sg.ks_h + 8 * (lane >> 4);
+    const uint16_t* vp = (const uint16_t*)sg.v + (int64_t)kk * sg.vs_t + (int64_t)g * sg.vs_h + 8 * (lane >> 4);
+#pragma unroll
+    for (int dc = 0; dc < C::DC; ++dc) {
+      kf[dc] = *(const bf16x8*)(kp + 32 * dc);
+      vf[dc] = *(const bf16x8*)(vp + 32 * dc);
+    }
+  }
+  f32x4 dk[C::DB], dv[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+    dk[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dv[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Query-row tiles that can see a key of this tile: with the causal rule,
+  // rows from the first token at or after the tile's first key position.
+  const int64_t kpos_min = sg.pos0 + k0;
+  const int64_t kpos_max = sg.pos0 + min(k0 + kTileKeys, n_keys) - 1;
+  int64_t r_begin = 0;
+  if (qs.causal) r_begin = max((int64_t)0, (kpos_min - qs.q_pos0) * qs.G);
+  const int t_end = (total + kRowTile - 1) / kRowTile;
+  const int t_begin = r_begin >= total ? t_end : (int)(r_begin / kRowTile);
+
+  if (t_begin < t_end) {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qs.q, a.q_bytes);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.dout, a.q_bytes);
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse, a.rows_bytes);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.delta, a.rows_bytes);
+    const uint32_t lds_addr = (uint32_t)(size_t)(lds_char*)lds;
+    issue_rows<D>(a, rq, rg, rl, rd, t_begin * kRowTile, g, lds_addr, wave, lane);
+    for (int t = t_begin; t < t_end; ++t) {
+      const int cur = (t - t_begin) & 1;
+      wait_all_loads();
+      __syncthreads();
+      if (t + 1 < t_end)
+        issue_rows<D>(a, rq, rg, rl, rd, (t + 1) * kRowTile, g, lds_addr + (uint32_t)((cur ^ 1) * C::STAGEB),
+                      wave, lane);
+      const int f0 = t * kRowTile;
+      // Rows of the tile span positions q_pos0 + f0/G .. q_pos0 + (f0 + 63)/G.
+      const int64_t qpos_min = qs.q_pos0 + f0 / qs.G;
+      const bool need_mask = (k0 + kTileKeys > n_keys) || (f0 + kRowTile > total) ||
+                             (qs.causal && kpos_max > qpos_min);
+      dkdv_tile<D>((const lds_char*)lds + cur * C::STAGEB, lane, kf, vf, dk, dv, qs.c, need_mask, qs, f0, total,
+                   key_idx, n_keys, kpos);
+    }
+    wait_all_loads();
+  }
+
+  // dk[key, g, 16*db + 4*(lane/16) + i] += scale * dK^T; dv likewise, unscaled.
+  if (key_idx < n_keys && t_begin < t_end) {
+    const int64_t base = ((int64_t)key_idx * Hkv + g) * D + 4 * (lane >> 4);
+    float* dkp = a.dk[si] + base;
+    float* dvp = a.dv[si] + base;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      f32x4 x = *(f32x4*)(dkp + 16 * db);
+      x += dk[db] * a.scale;
+      *(f32x4*)(dkp + 16 * db) = x;
+      f32x4 y = *(f32x4*)(dvp + 16 * db);
+      y += dv[db];
+      *(f32x4*)(dvp + 16 * db) = y;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_delta(const DeltaArgs& a, int D, hipStream_t s) {
+  const int rpb = kThreads / (D / 8);
+  dim3 grid((unsigned)((a.rows + rpb - 1) / rpb));
+  if (D == 128)
+    hipLaunchKernelGGL(delta_kernel<128>, grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(delta_kernel<64>, grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, int n_key_tiles, int D, hipStream_t s) {
+  const int tiles = (a.qs.q_len * a.qs.G + kTileRows - 1) / kTileRows;
+  dim3 grid_q(tiles * a.qs.Hkv);
+  dim3 grid_k(n_key_tiles * a.qs.Hkv);
+  if (D == 128) {
+    hipLaunchKernelGGL(dq_kernel<128>, grid_q, dim3(kThreads), 0, s, a);
+    if (n_key_tiles > 0) hipLaunchKernelGGL(dkdv_kernel<128>, grid_k, dim3(kThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(dq_kernel<64>, grid_q, dim3(kThreads), 0, s, a);
+    if (n_key_tiles > 0) hipLaunchKernelGGL(dkdv_kernel<64>, grid_k, dim3(kThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ba

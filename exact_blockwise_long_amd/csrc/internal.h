@@ -136,6 +136,38 @@ struct FinalizeArgs {
   float* lse;
 };
 
+// Backward of one call's visits: dq (fp32, state-row order [rows, D]) and the
+// visited blocks' dk, dv (fp32 [n, Hkv, D] each) accumulate.  dout uses Q's
+// strides; lse (natural log) and delta are per state row.  The dK/dV kernel's
+// grid covers tile_begin[n_seg] 64-key tiles: tiles [tile_begin[s],
+// tile_begin[s+1]) are segment s's.
+struct BwdArgs {
+  QSide qs;
+  const void* dout;
+  const float* lse;
+  const float* delta;
+  float* dq;
+  float scale;
+  uint32_t q_bytes;      // bytes from q (and dout) to the end of its last row
+  uint32_t rows_bytes;   // bytes of lse and delta
+  int32_t n_seg;
+  int32_t tile_begin[kMaxSeg + 1];
+  Seg seg[kMaxSeg];
+  float* dk[kMaxSeg];
+  float* dv[kMaxSeg];
+};
+
+// delta[r] = sum_d dout[r * dout_stride + d] * out[r * out_stride + d].
+struct DeltaArgs {
+  int64_t rows;
+  const void* out;
+  int32_t out_bf16;
+  int64_t out_stride;
+  const void* dout;
+  int64_t dout_stride;
+  float* delta;
+};
+
 // Rows per workgroup tile of the bf16 attention kernels.
 constexpr int kTileRows = 128;
 
@@ -152,5 +184,7 @@ hipError_t launch_walk_f32(const WalkArgs& a, int D, hipStream_t s);
 hipError_t launch_merge_groups(const MergeGroupArgs& a, int D, hipStream_t s);
 hipError_t launch_merge_ptrs(const MergePtrArgs& a, int D, hipStream_t s);
 hipError_t launch_finalize(const FinalizeArgs& a, int D, hipStream_t s);
+hipError_t launch_delta(const DeltaArgs& a, int D, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdArgs& a, int n_key_tiles, int D, hipStream_t s);
 
 }  // namespace ba

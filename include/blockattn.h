@@ -275,6 +275,50 @@ const char* blockattn_status_str(int32_t status);
 /* Message of the last failed check on the calling thread ("" if none). */
 const char* blockattn_last_error(void);
 
+/* Backward pass, first step: delta[r] = sum_d dout[r, d] * out[r, d] (the row
+ * term of the softmax Jacobian, [RAC] s.7 backward box with the chain rule of
+ * s.1).  out is the forward's finalised output (bf16 or fp32 as out_dtype),
+ * dout the gradient of the loss with respect to it (bf16); rows in state-row
+ * order (token * n_q_heads + head), row strides in elements.  Errors:
+ * BA_ERR_NULL, BA_ERR_SHAPE (head_dim, strides < head_dim or not multiples of
+ * 8, misaligned), BA_ERR_UNSUPPORTED (out_dtype). */
+ba_status blockattn_bwd_delta(int64_t rows, int32_t head_dim, const void* out, int32_t out_dtype,
+                              int64_t out_row_stride, const void* dout, int64_t dout_row_stride,
+                              float* delta, hipStream_t stream);
+
+/* Backward pass over the K/V blocks one forward call visited ([RAC] s.7:
+ * recompute each block's scores from the stored Q and log-sum-exp, accumulate
+ * dQ for the stationary query block and dK, dV for the visiting block).
+ *
+ * p, q, blocks, n_blocks, order and n_visit are those of the forward; dout
+ * ([q_len, n_q_heads, head_dim] bf16 with q's strides) is the gradient of the
+ * loss with respect to the finalised output; lse [q_len * n_q_heads] is the
+ * forward's final log-sum-exp (blockattn_finalize, natural log; -inf for a
+ * row that saw no key) and delta the output of blockattn_bwd_delta, both in
+ * state-row order.  With P = exp(scale q.k - lse) over the row's visible keys:
+ *   dq[r, :] += scale * sum_j P_rj (dP_rj - delta_r) k_j,  dP_rj = dout_r . v_j;
+ *   dk_b[j, g, :] += scale * sum_r P_rj (dP_rj - delta_r) q_r;
+ *   dv_b[j, g, :] += sum_r P_rj dout_r,
+ * summed over the query heads r of KV head g.  dq is fp32 [q_len * n_q_heads,
+ * head_dim] (state-row order); dk and dv are HOST arrays of n_blocks device
+ * pointers, entry b pointing at fp32 [blocks[b].len, n_kv_heads, head_dim]
+ * (contiguous) for every visited block; all accumulate (+=), so one call per
+ * ring step (reverse order or any order) builds the full gradients.  Blocks no
+ * query of the block can see are skipped.  The dk/dv buffers of different
+ * blocks of one call are updated concurrently and must not overlap; calls that
+ * share buffers must be ordered (one stream).  The caller owns every buffer;
+ * nothing is kept after the call returns.  Results do not depend on scheduling
+ * (no atomics).  bf16 only; q, dout, lse and delta must each span less than
+ * 4 GiB.  Errors: as blockattn_fwd_block, plus
+ * BA_ERR_NULL (dout, lse, delta, dq, or a visited block's dk/dv) and
+ * BA_ERR_UNSUPPORTED (fp32 problems). */
+ba_status blockattn_bwd_block(const ba_problem* p, const void* q, const void* dout,
+                              const float* lse, const float* delta,
+                              const ba_kv_block* blocks, int32_t n_blocks,
+                              const int32_t* order, int32_t n_visit,
+                              float* dq, float* const* dk, float* const* dv,
+                              hipStream_t stream);
+
 /* BLOCKATTN_ABI_VERSION of the loaded library. */
 int32_t blockattn_abi_version(void);
 

@@ -202,3 +202,52 @@ def test_workspace_sizes_are_deterministic(lib):
     a = lib.fanout_workspace_bytes(ctypes.byref(f))
     b = lib.fanout_workspace_bytes(ctypes.byref(f))
     assert a == b and a % 256 == 0
+
+
+def _bwd(lib, p=None, q=FAKE, dout=FAKE, lse=FAKE, delta=FAKE, blocks=None, n_blocks=2, order=None, n_visit=2,
+         dq=FAKE, dk=(FAKE, FAKE), dv=(FAKE, FAKE), dk_arr=True):
+    p = _problem() if p is None else p
+    blocks = _blocks(n_blocks) if blocks is None else blocks
+    o = None if order is None else (ctypes.c_int32 * len(order))(*order)
+    dka = (ctypes.c_void_p * len(dk))(*dk) if dk_arr else None
+    dva = (ctypes.c_void_p * len(dv))(*dv)
+    return lib.blockattn_bwd_block(ctypes.byref(p), q, dout, lse, delta, blocks, n_blocks, o, n_visit, dq, dka, dva,
+                                   None)
+
+
+def test_bwd_block_validation(lib):
+    assert lib.blockattn_bwd_block(None, FAKE, FAKE, FAKE, FAKE, _blocks(1), 1, None, 1, FAKE, None, None, None) == 1
+    assert _bwd(lib, p=_problem(dtype=ba.BA_F32)) == 3           # bf16 only
+    assert _bwd(lib, p=_problem(head_dim=96)) == 2
+    assert _bwd(lib, order=[0, 0]) == 4
+    assert _bwd(lib, dout=None) == 1
+    assert _bwd(lib, lse=None) == 1
+    assert _bwd(lib, delta=None) == 1
+    assert _bwd(lib, dq=None) == 1
+    assert _bwd(lib, dout=FAKE + 2) == 2
+    assert _bwd(lib, dq=FAKE + 4) == 2
+    assert _bwd(lib, dk_arr=False) == 1
+    assert _bwd(lib, dk=(FAKE, None)) == 1
+    assert _bwd(lib, dv=(FAKE + 4, FAKE)) == 2
+    assert _bwd(lib, p=_problem(q_stride_token=1 << 28)) == 2   # beyond 32-bit offsets
+    # nothing to do: no rows, no visits, or every visited key in the causal future
+    assert _bwd(lib, p=_problem(q_len=0)) == 0
+    assert _bwd(lib, order=[], n_visit=0) == 0
+    future = _blocks(2)
+    for i in range(2):
+        future[i].pos0 = 1000 + 64 * i
+    assert _bwd(lib, p=_problem(causal=1), blocks=future, dk=(None, None), dv=(None, None)) == 0
+
+
+def test_bwd_delta_validation(lib):
+    def call(rows=16, D=128, out=FAKE, dtype=ba.BA_BF16, os_=128, dout=FAKE, gs=128, delta=FAKE):
+        return lib.blockattn_bwd_delta(rows, D, out, dtype, os_, dout, gs, delta, None)
+    assert call(D=96) == 2
+    assert call(rows=-1) == 2
+    assert call(dtype=7) == 3
+    assert call(rows=0) == 0
+    assert call(out=None) == 1
+    assert call(delta=None) == 1
+    assert call(os_=64) == 2
+    assert call(gs=132) == 2
+    assert call(dout=FAKE + 8) == 2

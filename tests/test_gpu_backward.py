@@ -1,0 +1,162 @@
+"""GPU parity of the blockwise backward (through the C ABI) against the CPU
+fp64 oracle's attention gradients.
+
+The forward runs on the GPU (fwd_block + finalize), its bf16 output and
+log-sum-exp feed bwd_delta and bwd_block, and dQ, dK, dV are compared with
+the oracle's exact gradients of the same bf16 inputs.  Every case prints its
+name, shape and seed before it touches the GPU.
+
+Tolerance (a reading: no gradient tolerance is fixed for the method).  The
+kernels round P and dS to bf16 for the matrix cores and read the forward's
+bf16 output for D = rowsum(dO * A); each of those is a relative 2^-9
+perturbation of a term of a sum of hundreds of terms with random signs.  The
+errors are judged against the gradient's own scale: the largest error at most
+2e-2 of the largest reference magnitude, the mean error at most 5e-3 of the
+mean reference magnitude.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from exact_blockwise_long_amd import blockattn as ba
+from exact_blockwise_long_amd import synth
+from oracle import attention as ora
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+MAX_REL, MEAN_REL = 2e-2, 5e-3
+
+
+def announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ba.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def check_grad(got, ref, what):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
+    assert np.all(np.isfinite(got)), f"{what}: non-finite gradient"
+    err = np.abs(got - ref)
+    scale_max = float(np.abs(ref).max()) if ref.size else 0.0
+    scale_mean = float(np.abs(ref).mean()) if ref.size else 0.0
+    mx = float(err.max()) / max(scale_max, 1e-30) if err.size else 0.0
+    mn = float(err.mean()) / max(scale_mean, 1e-30) if err.size else 0.0
+    print(f"    {what}: max err / max|ref| {mx:.2e}, mean err / mean|ref| {mn:.2e} "
+          f"(max|ref| {scale_max:.3e})", flush=True)
+    assert mx <= MAX_REL and mn <= MEAN_REL, f"{what}: relative errors {mx:.3e} / {mn:.3e}"
+
+
+def make_case(seed, T, Hq, Hkv, D, lens):
+    g = synth.rng(seed)
+    L = sum(lens)
+    q = synth.normal(g, (T, Hq, D), 0.5, "bf16")
+    k = synth.normal(g, (L, Hkv, D), 0.5, "bf16")
+    v = synth.normal(g, (L, Hkv, D), 0.5, "bf16")
+    do = synth.normal(g, (T, Hq, D), 0.5, "bf16")
+    return q, k, v, do
+
+
+def device_blocks(kd, vd, lens):
+    blocks, off = [], 0
+    for n in lens:
+        blocks.append((kd[off:off + n], vd[off:off + n], off))
+        off += n
+    return blocks
+
+
+def gpu_grads(q, k, v, do, lens, order, *, Hkv, q_pos0, causal, per_visit):
+    """Forward on the GPU, then the backward over the same visits (reversed
+    and one call per visit when ``per_visit``, as a ring's backward runs)."""
+    T, Hq, D = q.shape
+    qd, kd, vd, dod = (H.to_device(x) for x in (q, k, v, do))
+    blocks = device_blocks(kd, vd, lens)
+    st = ba.new_state(T * Hq, D)
+    ba.fwd_block(qd, blocks, order, st, reset=True, n_kv_heads=Hkv, q_pos0=q_pos0, causal=causal, split_mode=1)
+    out, lse = ba.finalize(st)
+    delta = ba.bwd_delta(out, dod)
+    dq = torch.zeros(T * Hq, D, dtype=torch.float32, device="cuda")
+    dkv = [(torch.zeros(n, Hkv, D, dtype=torch.float32, device="cuda"),
+            torch.zeros(n, Hkv, D, dtype=torch.float32, device="cuda")) for n in lens]
+    if per_visit:
+        for j in reversed(order):
+            ba.bwd_block(qd, dod, lse, delta, blocks, [j], dq, dkv, n_kv_heads=Hkv, q_pos0=q_pos0, causal=causal)
+    else:
+        ba.bwd_block(qd, dod, lse, delta, blocks, order, dq, dkv, n_kv_heads=Hkv, q_pos0=q_pos0, causal=causal)
+    torch.cuda.synchronize()
+    dk = torch.cat([x[0] for x in dkv], 0)
+    dv = torch.cat([x[1] for x in dkv], 0)
+    return H.host(dq).reshape(T, Hq, D), H.host(dk), H.host(dv)
+
+
+def oracle_grads(q, k, v, do, q_pos0, causal):
+    T, _, D = q.shape
+    L = k.shape[0]
+    return ora.attention_grads(q.f64(), k.f64(), v.f64(), do.f64(), 1.0 / np.sqrt(D), q_pos0 + np.arange(T),
+                               np.arange(L), causal)
+
+
+CASES = [
+    # (seed, T, Hq, Hkv, D, lens, order, q_pos0, causal): several row and key
+    # tiles, ragged tails, GQA, causal diagonals inside tiles, fully future keys.
+    (41, 300, 8, 2, 128, [200, 77, 129, 64], [2, 0, 3, 1], 350, True),
+    (42, 300, 8, 2, 128, [200, 77, 129, 64], [3, 2, 1, 0], 0, False),
+    (43, 130, 4, 4, 64, [65, 128, 31], [1, 2, 0], 150, True),
+    (44, 17, 16, 1, 128, [513, 1000], [1, 0], 1400, True),
+]
+
+
+@pytest.mark.parametrize("per_visit", [False, True], ids=["one_call", "per_visit"])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"seed{c[0]}")
+def test_backward_matches_oracle(case, per_visit):
+    seed, T, Hq, Hkv, D, lens, order, q_pos0, causal = case
+    announce(f"bwd seed {seed} T={T} Hq={Hq} Hkv={Hkv} D={D} lens={lens} order={order} q_pos0={q_pos0} "
+             f"causal={causal} per_visit={per_visit}")
+    q, k, v, do = make_case(seed, T, Hq, Hkv, D, lens)
+    dq, dk, dv = gpu_grads(q, k, v, do, lens, order, Hkv=Hkv, q_pos0=q_pos0, causal=causal, per_visit=per_visit)
+    rq, rk, rv = oracle_grads(q, k, v, do, q_pos0, causal)
+    check_grad(dq, rq, f"seed{seed} dQ")
+    check_grad(dk, rk, f"seed{seed} dK")
+    check_grad(dv, rv, f"seed{seed} dV")
+    if causal:
+        # keys after every query's position receive no gradient at all
+        L = k.shape[0]
+        dead = np.arange(L) > q_pos0 + T - 1
+        if dead.any():
+            assert not dk[dead].any() and not dv[dead].any(), "gradient on keys no query sees"
+
+
+def test_backward_deterministic():
+    seed, T, Hq, Hkv, D, lens, order, q_pos0, causal = CASES[0]
+    announce(f"bwd determinism seed {seed}")
+    q, k, v, do = make_case(seed, T, Hq, Hkv, D, lens)
+    a = gpu_grads(q, k, v, do, lens, order, Hkv=Hkv, q_pos0=q_pos0, causal=causal, per_visit=False)
+    b = gpu_grads(q, k, v, do, lens, order, Hkv=Hkv, q_pos0=q_pos0, causal=causal, per_visit=False)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+def test_delta_is_rowsum_of_dout_times_out(out_dtype):
+    rows, D, seed = 1000, 128, 45
+    announce(f"bwd_delta rows={rows} D={D} out={out_dtype} seed {seed}")
+    g = synth.rng(seed)
+    out = synth.normal(g, (rows, D), 1.0, out_dtype)
+    do = synth.normal(g, (rows, D), 1.0, "bf16")
+    got = H.host(ba.bwd_delta(H.to_device(out), H.to_device(do)))
+    terms = out.f64() * do.f64()
+    ref = terms.sum(axis=1)
+    bound = 1e-5 * np.abs(terms).sum(axis=1)
+    assert np.all(np.abs(got - ref) <= bound), f"worst {np.max(np.abs(got - ref) / bound):.3e} of the bound"
