@@ -117,6 +117,60 @@ def bench_prefill(torch, ba, H, w, steps, warmup):
     return dict(q=q, k=k, v=v, ms_step=ms_step, kernel_ms=kernel_ms, flops=flops, step=step)
 
 
+def bench_backward(torch, ba, H, w, steps, warmup):
+    """Backward of the prefill workload: clear the fp32 accumulators, bwd_delta,
+    then one bwd_block call over the forward's visits (the dQ walk and the
+    dK/dV kernel).  Algorithmic work is five products per visible pair (scores
+    recomputed once, dP, dV, dK, dQ: 2.5x the forward's); the kernels
+    recompute scores and dP on both sides, seven products."""
+    log(f"inputs: {w.name} (backward)")
+    q, k, v = w.make_inputs()
+    do = w.make_dout()
+    qd, kd, vd, dod = H.to_device(q), H.to_device(k), H.to_device(v), H.to_device(do)
+    del q, k, v, do
+    L = w.block_len
+    blocks = [(kd[b * L:(b + 1) * L], vd[b * L:(b + 1) * L], b * L) for b in range(w.n_blocks)]
+    st = ba.new_state(w.rows, w.head_dim)
+    ba.fwd_block(qd, blocks, w.order, st, reset=True, n_kv_heads=w.n_kv_heads, q_pos0=w.q_pos0, causal=w.causal)
+    out, lse = ba.finalize(st)
+    del st
+    delta = torch.empty(w.rows, dtype=torch.float32, device="cuda")
+    dq = torch.empty(w.rows, w.head_dim, dtype=torch.float32, device="cuda")
+    dkv = [(torch.empty(L, w.n_kv_heads, w.head_dim, dtype=torch.float32, device="cuda"),
+            torch.empty(L, w.n_kv_heads, w.head_dim, dtype=torch.float32, device="cuda")) for _ in blocks]
+
+    def step(timer=None):
+        dq.zero_()
+        for a, b in dkv:
+            a.zero_()
+            b.zero_()
+        ba.bwd_delta(out, dod, delta)
+        e0 = timer.start() if timer else None
+        ba.bwd_block(qd, dod, lse, delta, blocks, w.order, dq, dkv, n_kv_heads=w.n_kv_heads, q_pos0=w.q_pos0,
+                     causal=w.causal)
+        if timer:
+            timer.stop(e0)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(timer)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    kms = timer.mean_ms()
+    alg = 2.5 * w.flops()
+    tf, ktf = alg / ms / 1e9, alg / kms / 1e9
+    log(f"backward: {ms:.3f} ms/step, bwd_block {kms:.3f} ms, {tf:.1f} TFLOP/s step, {ktf:.1f} TFLOP/s kernels")
+    return {"workload": w.name + ", backward", "ms_per_step": round(ms, 3), "TFLOP/s": round(tf, 1),
+            "bwd_block_ms_mean": round(kms, 3), "bwd_block_TFLOP/s": round(ktf, 1),
+            "bwd_block_frac_of_bf16_peak": round(ktf / PEAK_BF16_TFLOPS, 4),
+            "algorithmic_flops_per_step": alg, "executed_mfma_flops_per_step": 3.5 * w.flops(),
+            "step": "zero dq/dk/dv, bwd_delta, bwd_block (dq_kernel + dkdv_kernel)"}
+
+
 def _smi_sample():
     """One amd-smi reading: (mean GFX clock over the XCDs in MHz, socket power in W) or None."""
     try:
@@ -468,7 +522,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="all",
                     choices=["all", "causal_prefill", "ring_share", "fanout", "shard_merge", "merge_scaled",
-                             "layouts", "fanout_prefill", "copy_calibration"])
+                             "layouts", "fanout_prefill", "backward", "copy_calibration"])
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -503,6 +557,8 @@ def main():
         secondary["fanout_prefill"] = bench_fanout_prefill(torch, ba, H, wl.FANOUT_PREFILL, args.steps, args.warmup)
     if only == "layouts":
         secondary["causal_ring_layouts"] = bench_layouts(torch, ba, H, wl.CAUSAL_RING_LAYOUTS, max(1, args.steps // 10))
+    if only == "backward":
+        secondary["backward"] = bench_backward(torch, ba, H, wl.CAUSAL_PREFILL, args.steps, args.warmup)
     if only == "copy_calibration":
         secondary["copy_calibration"] = copy_calibration(torch, args.steps)
     if only not in ("all", "causal_prefill"):
@@ -548,6 +604,7 @@ def main():
         secondary["fanout_prefill"] = bench_fanout_prefill(torch, ba, H, wl.FANOUT_PREFILL, args.steps, args.warmup)
         secondary["shard_merge"] = bench_shard_merge(torch, ba, H, wl.SHARD_MERGE, args.steps, args.warmup)
         secondary["merge_scaled"] = bench_merge_scaled(torch, ba, args.steps, args.warmup)
+        secondary["backward"] = bench_backward(torch, ba, H, w, args.steps, args.warmup)
         secondary["ring_share"] = bench_ring_share(torch, ba, H, wl.RING_SHARE, 2, 1)
         secondary["causal_ring_layouts"] = bench_layouts(torch, ba, H, wl.CAUSAL_RING_LAYOUTS, 2)
     if secondary:

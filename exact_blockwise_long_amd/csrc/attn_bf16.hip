@@ -69,7 +69,7 @@ __device__ inline void tile_compute(const lds_char* stage, int lane, const bf16x
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int row = 16 * kb + lr;
-      const bf16x8 kf = *(const lds_bf16x8*)(kl + row * C::ROWB + (((4 * dc + lg) ^ swz_k<D>(row)) * 16));
+      const bf16x8 kf = *(const lds_bf16x8*)(kl + row * C::ROWB + (((4 * dc + lg) ^ swz<D>(row)) * 16));
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
         s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][dc], s[kb][qb], 0, 0, 0);
@@ -153,8 +153,8 @@ __device__ inline void tile_compute(const lds_char* stage, int lane, const bf16x
       const int row1 = row0 + 16;
       const int cidx = 2 * db + ((lr & 3) >> 1);
       const int half = (lr & 1) * 8;
-      const lds_char* a0 = vl + row0 * C::ROWB + ((cidx ^ swz_v<D>(row0)) * 16) + half;
-      const lds_char* a1 = vl + row1 * C::ROWB + ((cidx ^ swz_v<D>(row1)) * 16) + half;
+      const lds_char* a0 = vl + row0 * C::ROWB + ((cidx ^ swz<D>(row0)) * 16) + half;
+      const lds_char* a1 = vl + row1 * C::ROWB + ((cidx ^ swz<D>(row1)) * 16) + half;
       const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a0);
       const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a1);
       const s16x8 xx = s16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};

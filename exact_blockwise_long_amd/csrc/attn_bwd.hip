@@ -95,8 +95,8 @@ __device__ inline void dq_tile(const lds_char* stage, int lane, const bf16x8 (&q
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int row = 32 * ch + 16 * h + lr;
-        const bf16x8 kf = *(const lds_bf16x8*)(kl + row * C::ROWB + (((4 * dc + lg) ^ swz_k<D>(row)) * 16));
-        const bf16x8 vf = *(const lds_bf16x8*)(vl + row * C::ROWB + (((4 * dc + lg) ^ swz_v<D>(row)) * 16));
+        const bf16x8 kf = *(const lds_bf16x8*)(kl + row * C::ROWB + (((4 * dc + lg) ^ swz<D>(row)) * 16));
+        const bf16x8 vf = *(const lds_bf16x8*)(vl + row * C::ROWB + (((4 * dc + lg) ^ swz<D>(row)) * 16));
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           s[h][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][dc], s[h][qb], 0, 0, 0);
@@ -145,8 +145,8 @@ __device__ inline void dq_tile(const lds_char* stage, int lane, const bf16x8 (&q
       const int row1 = row0 + 16;
       const int cidx = 2 * db + ((lr & 3) >> 1);
       const int half = (lr & 1) * 8;
-      const lds_char* a0 = kl + row0 * C::ROWB + ((cidx ^ swz_k<D>(row0)) * 16) + half;
-      const lds_char* a1 = kl + row1 * C::ROWB + ((cidx ^ swz_k<D>(row1)) * 16) + half;
+      const lds_char* a0 = kl + row0 * C::ROWB + ((cidx ^ swz<D>(row0)) * 16) + half;
+      const lds_char* a1 = kl + row1 * C::ROWB + ((cidx ^ swz<D>(row1)) * 16) + half;
       const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a0);
       const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a1);
       const s16x8 xx = s16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
@@ -236,7 +236,7 @@ struct BwdCfg {
 };
 
 // Issues the loads of query-row tile f0 .. f0 + 63 (flat rows of KV head g)
-// into the stage at `stage`: Q and dO rows (swizzled as K tiles are), then the
+// into the stage at `stage`: Q and dO rows (swizzled as the K/V tiles are), then the
 // rows' log-sum-exp and D.  Rows past the last are loaded as the last row; the
 // caller masks them.
 template <int D>
@@ -254,7 +254,7 @@ __device__ inline void issue_rows(const BwdArgs& a, __amdgpu_buffer_rsrc_t rq, _
     const int f = min(f0 + row, total - 1);
     const int t = f / qs.G;
     const int h = g * qs.G + (f - t * qs.G);
-    const uint32_t off = (uint32_t)(((int64_t)t * qs.qs_t + (int64_t)h * qs.qs_h) * 2) + (uint32_t)((p ^ swz_k<D>(row)) * 16);
+    const uint32_t off = (uint32_t)(((int64_t)t * qs.qs_t + (int64_t)h * qs.qs_h) * 2) + (uint32_t)((p ^ swz<D>(row)) * 16);
     const uint32_t dst = stage + (uint32_t)((wave * C::LPW + j) * C::RPI) * C::ROWB;
     lds_dma16(rq, dst, off, 0);
     lds_dma16(rg, dst + C::TILEB, off, 0);
@@ -294,7 +294,7 @@ __device__ inline void dkdv_tile(const lds_char* stage, int lane, const bf16x8 (
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       const int row = 16 * rb + lr;
-      const int off = row * C::ROWB + (((4 * dc + lg) ^ swz_k<D>(row)) * 16);
+      const int off = row * C::ROWB + (((4 * dc + lg) ^ swz<D>(row)) * 16);
       const bf16x8 qa = *(const lds_bf16x8*)(ql + off);
       const bf16x8 ga = *(const lds_bf16x8*)(gl + off);
       s[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[dc], s[rb], 0, 0, 0);
@@ -355,8 +355,8 @@ __device__ inline void dkdv_tile(const lds_char* stage, int lane, const bf16x8 (
       const int row1 = row0 + 16;
       const int cidx = 2 * db + ((lr & 3) >> 1);
       const int half = (lr & 1) * 8;
-      const int o0 = row0 * C::ROWB + ((cidx ^ swz_k<D>(row0)) * 16) + half;
-      const int o1 = row1 * C::ROWB + ((cidx ^ swz_k<D>(row1)) * 16) + half;
+      const int o0 = row0 * C::ROWB + ((cidx ^ swz<D>(row0)) * 16) + half;
+      const int o1 = row1 * C::ROWB + ((cidx ^ swz<D>(row1)) * 16) + half;
       const s16x4 g0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(gl + o0));
       const s16x4 g1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(gl + o1));
       const s16x4 q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(ql + o0));

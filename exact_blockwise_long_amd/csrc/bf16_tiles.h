@@ -36,11 +36,21 @@ struct Cfg {
   static constexpr int DB = D / 16;                   // 16-wide d blocks of O^T
 };
 
-// Chunk swizzles (XOR on the 16-byte chunk index within a row).
+// Chunk swizzle of every LDS tile: global 16-byte chunk c of tile row r sits
+// at chunk c ^ swz(r).  Tiles are read two ways: 16-byte row reads (lane l
+// reads row l % 16 of a 16-row block, chunk 4*dc + l / 16) and transposing
+// 8-byte reads (lane l reads 8 bytes of row 4*(l / 16) + (l % 16) / 4 of a
+// 16-row block, chunk pair 2*db + {0, 1}).  LDS has 64 banks of 4 bytes;
+// measured with a one-wave probe on the bank-conflict counter, a 16-byte read
+// is served in four 16-lane passes, each pairing lanes 8a .. 8a + 7 of one
+// quarter-wave with eight lanes of the other half of an odd quarter-wave, and
+// a transposing read in two 32-lane passes.  For D = 128 (one row per bank
+// line) (r & 7) << 1 keeps both kinds conflict-free, while r & 15 doubles the
+// transposing reads' passes; for D = 64 (two rows per bank line) r & 7 does.
 template <int D>
-__device__ inline int swz_k(int row) { return D == 128 ? (row & 15) : (row & 7); }
-template <int D>
-__device__ inline int swz_v(int row) { return D == 128 ? ((row & 7) << 1) : ((row & 3) << 1); }
+__device__ inline int swz(int row) {
+  return D == 128 ? ((row & 7) << 1) : (row & 7);
+}
 
 // Reductions over the 4 lanes that share lane % 16 (one query column).
 //
@@ -144,8 +154,8 @@ __device__ inline LaneOffs<D> lane_offsets(const KVSrc& src, int wave, int lane)
 #pragma unroll
   for (int j = 0; j < C::LPW; ++j) {
     const int row = (wave * C::LPW + j) * C::RPI + rsub;
-    o.k[j] = (uint32_t)row * src.kst + (uint32_t)((p ^ swz_k<D>(row)) * 16);
-    o.v[j] = (uint32_t)row * src.vst + (uint32_t)((p ^ swz_v<D>(row)) * 16);
+    o.k[j] = (uint32_t)row * src.kst + (uint32_t)((p ^ swz<D>(row)) * 16);
+    o.v[j] = (uint32_t)row * src.vst + (uint32_t)((p ^ swz<D>(row)) * 16);
   }
   return o;
 }

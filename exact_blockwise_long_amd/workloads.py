@@ -87,6 +87,12 @@ class BlockwiseWorkload:
         v = synth.normal(g, (self.kv_len, self.n_kv_heads, self.head_dim), self.v_scale, self.dtype)
         return q, k, v
 
+    def make_dout(self):
+        """The gradient of a loss with respect to the output, [q_len, Hq, D], for
+        backward workloads: N(0, 1) * q_scale from its own stream (seed + 1000)."""
+        g = synth.rng(self.seed + 1000)
+        return synth.normal(g, (self.q_len, self.n_q_heads, self.head_dim), self.q_scale, self.dtype)
+
 
 @dataclass
 class FanoutWorkload:
