@@ -391,6 +391,7 @@ ba_status blockattn_bwd_block(const ba_problem* p, const void* q, const void* do
   a.scale = a.qs.c / ba::kLog2e;
   a.q_bytes = (uint32_t)q_extent;
   a.rows_bytes = (uint32_t)(R * 4);
+  a.g_magic = 0xFFFFFFFFu / (uint32_t)a.qs.G;
   a.n_seg = 0;
   int tiles = 0;
   for (int j : v.idx) {

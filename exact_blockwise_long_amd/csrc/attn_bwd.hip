@@ -38,6 +38,14 @@ __device__ inline void lds_dma4(__amdgpu_buffer_rsrc_t rsrc, uint32_t dst, uint3
 // mapped to +inf so that exp2(s * c - L2) is 0 for them.
 __device__ inline float lse2(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }
 
+// n / G for 0 <= n < 2^32 with magic = floor((2^32 - 1) / G): the multiply-high
+// is n / G rounded down, less at most one (its error is below n / 2^32 < 1),
+// and one comparison of the remainder fixes it.
+__device__ inline uint32_t div_g(uint32_t n, uint32_t G, uint32_t magic) {
+  uint32_t q = __umulhi(n, magic);
+  return q + ((n - q * G) >= G ? 1u : 0u);
+}
+
 // ---------------------------------------------------------------- D = rowsum(dO * A)
 
 template <int D>
@@ -245,25 +253,27 @@ __device__ inline void issue_rows(const BwdArgs& a, __amdgpu_buffer_rsrc_t rq, _
                                   uint32_t stage, int wave, int lane) {
   using C = BwdCfg<D>;
   const QSide& qs = a.qs;
-  const int total = qs.q_len * qs.G;
+  const uint32_t G = (uint32_t)qs.G;
+  const uint32_t last = (uint32_t)(qs.q_len * qs.G - 1);
+  const uint32_t st = (uint32_t)qs.qs_t, sh = (uint32_t)qs.qs_h;   // q spans < 4 GiB: 32-bit offsets
   const int rsub = lane / C::CPR;
   const int p = lane % C::CPR;
 #pragma unroll
   for (int j = 0; j < C::LPW; ++j) {
     const int row = (wave * C::LPW + j) * C::RPI + rsub;
-    const int f = min(f0 + row, total - 1);
-    const int t = f / qs.G;
-    const int h = g * qs.G + (f - t * qs.G);
-    const uint32_t off = (uint32_t)(((int64_t)t * qs.qs_t + (int64_t)h * qs.qs_h) * 2) + (uint32_t)((p ^ swz<D>(row)) * 16);
+    const uint32_t f = min((uint32_t)(f0 + row), last);
+    const uint32_t t = div_g(f, G, a.g_magic);
+    const uint32_t h = (uint32_t)g * G + (f - t * G);
+    const uint32_t off = (t * st + h * sh) * 2u + (uint32_t)((p ^ swz<D>(row)) * 16);
     const uint32_t dst = stage + (uint32_t)((wave * C::LPW + j) * C::RPI) * C::ROWB;
     lds_dma16(rq, dst, off, 0);
     lds_dma16(rg, dst + C::TILEB, off, 0);
   }
   if (wave < 2) {
-    const int f = min(f0 + lane, total - 1);
-    const int t = f / qs.G;
-    const int h = g * qs.G + (f - t * qs.G);
-    const uint32_t off = (uint32_t)(((int64_t)t * qs.Hq + h) * 4);
+    const uint32_t f = min((uint32_t)(f0 + lane), last);
+    const uint32_t t = div_g(f, G, a.g_magic);
+    const uint32_t h = (uint32_t)g * G + (f - t * G);
+    const uint32_t off = (t * (uint32_t)qs.Hq + h) * 4u;
     lds_dma4(wave == 0 ? rl : rd, stage + 2 * C::TILEB + (uint32_t)(wave * kRowTile * 4), off, 0);
   }
 }
@@ -272,8 +282,8 @@ __device__ inline void issue_rows(const BwdArgs& a, __amdgpu_buffer_rsrc_t rq, _
 template <int D>
 __device__ inline void dkdv_tile(const lds_char* stage, int lane, const bf16x8 (&kf)[BwdCfg<D>::DC],
                                  const bf16x8 (&vf)[BwdCfg<D>::DC], f32x4 (&dk)[BwdCfg<D>::DB],
-                                 f32x4 (&dv)[BwdCfg<D>::DB], float c, bool need_mask, const QSide& qs, int f0,
-                                 int total, int key_idx, int n_keys, int64_t kpos) {
+                                 f32x4 (&dv)[BwdCfg<D>::DB], float c, bool need_mask, int f0, int f_begin,
+                                 int f_end) {
   using C = BwdCfg<D>;
   const lds_char* ql = stage;
   const lds_char* gl = stage + C::TILEB;
@@ -301,31 +311,32 @@ __device__ inline void dkdv_tile(const lds_char* stage, int lane, const bf16x8 (
       dp[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga, vf[dc], dp[rb], 0, 0, 0);
     }
   }
+  // A row that saw no key has L = -inf and gives exp2(+inf) here; every pair
+  // of such a row is masked below (an unmasked tile holds only rows that see
+  // all its keys), so no per-element test is needed.
   float p[4][4], d[4][4];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
-    const f32x4 l2 = *(const __attribute__((address_space(3))) f32x4*)(l2s + 16 * rb + 4 * lg);
+    const f32x4 lse = *(const __attribute__((address_space(3))) f32x4*)(l2s + 16 * rb + 4 * lg);
     const f32x4 dl = *(const __attribute__((address_space(3))) f32x4*)(dls + 16 * rb + 4 * lg);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float l2i = l2[i] == -INFINITY ? INFINITY : l2[i] * kLog2e;
-      p[rb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][i], c, -l2i));
+      p[rb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][i], c, -kLog2e * lse[i]));
       d[rb][i] = p[rb][i] * (dp[rb][i] - dl[i]);
     }
   }
   if (need_mask) {
-    // Key key_idx at absolute position kpos against flat row f0 + r.
+    // This lane's key is visible to flat rows f0 + r in [f_begin, f_end): from
+    // the first row of the first token at or after its position (causal) up
+    // to the last valid row; f_end is 0 for a key past the block's end.
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int f = f0 + 16 * rb + 4 * lg + i;
-        bool vis = key_idx < n_keys && f < total;
-        if (qs.causal) vis = vis && kpos <= qs.q_pos0 + f / qs.G;
-        if (!vis) {
-          p[rb][i] = 0.f;
-          d[rb][i] = 0.f;
-        }
+        const bool vis = (f >= f_begin) & (f < f_end);
+        p[rb][i] = vis ? p[rb][i] : 0.f;
+        d[rb][i] = vis ? d[rb][i] : 0.f;
       }
   }
   // P and dS in the B-operand layout of the products over query rows: k-slot
@@ -385,8 +396,16 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int key_idx = k0 + 16 * wave + (lane & 15);   // this lane's key (column of S)
   const int n_keys = sg.n;
-  const int64_t kpos = sg.pos0 + key_idx;
   const int total = qs.q_len * qs.G;
+  // Flat row from which a key at position pos is visible (causal): the first
+  // row of token pos - q_pos0, clamped to [0, total].
+  auto first_row = [&](int64_t pos) -> int {
+    if (!qs.causal) return 0;
+    const int64_t r = (pos - qs.q_pos0) * qs.G;
+    return (int)(r < 0 ? 0 : (r > total ? total : r));
+  };
+  const int f_begin = first_row(sg.pos0 + key_idx);
+  const int f_end = key_idx < n_keys ? total : 0;
 
   // The wave's 16 keys as B operands: key 16*wave + lane%16, d = 32*dc + 8*(lane/16) .. +7.
   bf16x8 kf[C::DC], vf[C::DC];
@@ -408,13 +427,12 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdArgs a) {
   }
 
   // Query-row tiles that can see a key of this tile: with the causal rule,
-  // rows from the first token at or after the tile's first key position.
-  const int64_t kpos_min = sg.pos0 + k0;
-  const int64_t kpos_max = sg.pos0 + min(k0 + kTileKeys, n_keys) - 1;
-  int64_t r_begin = 0;
-  if (qs.causal) r_begin = max((int64_t)0, (kpos_min - qs.q_pos0) * qs.G);
+  // rows from the first token at or after the tile's first key position.  Rows
+  // below full_from miss at least one of the tile's keys.
+  const int r_begin = first_row(sg.pos0 + k0);
+  const int full_from = first_row(sg.pos0 + min(k0 + kTileKeys, n_keys) - 1);
   const int t_end = (total + kRowTile - 1) / kRowTile;
-  const int t_begin = r_begin >= total ? t_end : (int)(r_begin / kRowTile);
+  const int t_begin = r_begin >= total ? t_end : r_begin / kRowTile;
 
   if (t_begin < t_end) {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(qs.q, a.q_bytes);
@@ -431,12 +449,9 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdArgs a) {
         issue_rows<D>(a, rq, rg, rl, rd, (t + 1) * kRowTile, g, lds_addr + (uint32_t)((cur ^ 1) * C::STAGEB),
                       wave, lane);
       const int f0 = t * kRowTile;
-      // Rows of the tile span positions q_pos0 + f0/G .. q_pos0 + (f0 + 63)/G.
-      const int64_t qpos_min = qs.q_pos0 + f0 / qs.G;
-      const bool need_mask = (k0 + kTileKeys > n_keys) || (f0 + kRowTile > total) ||
-                             (qs.causal && kpos_max > qpos_min);
-      dkdv_tile<D>((const lds_char*)lds + cur * C::STAGEB, lane, kf, vf, dk, dv, qs.c, need_mask, qs, f0, total,
-                   key_idx, n_keys, kpos);
+      const bool need_mask = (k0 + kTileKeys > n_keys) || (f0 + kRowTile > total) || (f0 < full_from);
+      dkdv_tile<D>((const lds_char*)lds + cur * C::STAGEB, lane, kf, vf, dk, dv, qs.c, need_mask, f0, f_begin,
+                   f_end);
     }
     wait_all_loads();
   }

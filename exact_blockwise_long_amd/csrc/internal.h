@@ -150,6 +150,7 @@ struct BwdArgs {
   float scale;
   uint32_t q_bytes;      // bytes from q (and dout) to the end of its last row
   uint32_t rows_bytes;   // bytes of lse and delta
+  uint32_t g_magic;      // floor((2^32 - 1) / G): flat row -> token by one multiply-high and one fix-up
   int32_t n_seg;
   int32_t tile_begin[kMaxSeg + 1];
   Seg seg[kMaxSeg];
