@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "internal.h"
@@ -394,7 +395,13 @@ ba_status blockattn_bwd_block(const ba_problem* p, const void* q, const void* do
   a.g_magic = 0xFFFFFFFFu / (uint32_t)a.qs.G;
   a.n_seg = 0;
   int tiles = 0;
-  for (int j : v.idx) {
+  // Blocks in key-position order: under the causal rule the earliest keys
+  // are seen by the most rows, so the dK/dV grid hands out its longest
+  // workgroups first.  The gradients are sums over blocks; the order only
+  // changes rounding.
+  std::vector<int> by_pos(v.idx.begin(), v.idx.end());
+  std::stable_sort(by_pos.begin(), by_pos.end(), [&](int x, int y) { return blocks[x].pos0 < blocks[y].pos0; });
+  for (int j : by_pos) {
     if (usable_keys(p, blocks[j]) == 0) continue;   // causal future or empty: no gradient terms
     if (!dk[j] || !dv[j]) return fail(BA_ERR_NULL, "dk or dv of visited block %d is NULL", j);
     if (((uintptr_t)dk[j] % 16) != 0 || ((uintptr_t)dv[j] % 16) != 0)

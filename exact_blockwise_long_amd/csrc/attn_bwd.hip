@@ -440,13 +440,17 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdArgs a) {
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse, a.rows_bytes);
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.delta, a.rows_bytes);
     const uint32_t lds_addr = (uint32_t)(size_t)(lds_char*)lds;
-    issue_rows<D>(a, rq, rg, rl, rd, t_begin * kRowTile, g, lds_addr, wave, lane);
-    for (int t = t_begin; t < t_end; ++t) {
-      const int cur = (t - t_begin) & 1;
+    // Row tiles are walked from the last one down: every workgroup of a KV
+    // head then starts at the same row tile and the resident ones stream Q
+    // and dO in step, so each tile is fetched once into L2 and read from there
+    // by the others (the causal rule only moves where a workgroup stops).
+    issue_rows<D>(a, rq, rg, rl, rd, (t_end - 1) * kRowTile, g, lds_addr, wave, lane);
+    for (int t = t_end - 1; t >= t_begin; --t) {
+      const int cur = (t_end - 1 - t) & 1;
       wait_all_loads();
       __syncthreads();
-      if (t + 1 < t_end)
-        issue_rows<D>(a, rq, rg, rl, rd, (t + 1) * kRowTile, g, lds_addr + (uint32_t)((cur ^ 1) * C::STAGEB),
+      if (t > t_begin)
+        issue_rows<D>(a, rq, rg, rl, rd, (t - 1) * kRowTile, g, lds_addr + (uint32_t)((cur ^ 1) * C::STAGEB),
                       wave, lane);
       const int f0 = t * kRowTile;
       const bool need_mask = (k0 + kTileKeys > n_keys) || (f0 + kRowTile > total) || (f0 < full_from);

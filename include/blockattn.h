@@ -303,8 +303,9 @@ ba_status blockattn_bwd_delta(int64_t rows, int32_t head_dim, const void* out, i
  * head_dim] (state-row order); dk and dv are HOST arrays of n_blocks device
  * pointers, entry b pointing at fp32 [blocks[b].len, n_kv_heads, head_dim]
  * (contiguous) for every visited block; all accumulate (+=), so one call per
- * ring step (reverse order or any order) builds the full gradients.  Blocks no
- * query of the block can see are skipped.  The dk/dv buffers of different
+ * ring step (reverse order or any order) builds the full gradients; within a
+ * call the blocks are processed in key-position order (order changes only
+ * rounding).  Blocks no query of the block can see are skipped.  The dk/dv buffers of different
  * blocks of one call are updated concurrently and must not overlap; calls that
  * share buffers must be ordered (one stream).  The caller owns every buffer;
  * nothing is kept after the call returns.  Results do not depend on scheduling
