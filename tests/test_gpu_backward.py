@@ -69,20 +69,21 @@ def make_case(seed, T, Hq, Hkv, D, lens):
     return q, k, v, do
 
 
-def device_blocks(kd, vd, lens):
+def device_blocks(kd, vd, lens, kpos0=0):
     blocks, off = [], 0
     for n in lens:
-        blocks.append((kd[off:off + n], vd[off:off + n], off))
+        blocks.append((kd[off:off + n], vd[off:off + n], kpos0 + off))
         off += n
     return blocks
 
 
-def gpu_grads(q, k, v, do, lens, order, *, Hkv, q_pos0, causal, per_visit):
+def gpu_grads(q, k, v, do, lens, order, *, Hkv, q_pos0, causal, per_visit, kpos0=0):
     """Forward on the GPU, then the backward over the same visits (reversed
-    and one call per visit when ``per_visit``, as a ring's backward runs)."""
+    and one call per visit when ``per_visit``, as a ring's backward runs).
+    The keys sit at positions kpos0, kpos0 + 1, ... in block order."""
     T, Hq, D = q.shape
     qd, kd, vd, dod = (H.to_device(x) for x in (q, k, v, do))
-    blocks = device_blocks(kd, vd, lens)
+    blocks = device_blocks(kd, vd, lens, kpos0)
     st = ba.new_state(T * Hq, D)
     ba.fwd_block(qd, blocks, order, st, reset=True, n_kv_heads=Hkv, q_pos0=q_pos0, causal=causal, split_mode=1)
     out, lse = ba.finalize(st)
@@ -101,11 +102,11 @@ def gpu_grads(q, k, v, do, lens, order, *, Hkv, q_pos0, causal, per_visit):
     return H.host(dq).reshape(T, Hq, D), H.host(dk), H.host(dv)
 
 
-def oracle_grads(q, k, v, do, q_pos0, causal):
+def oracle_grads(q, k, v, do, q_pos0, causal, kpos0=0):
     T, _, D = q.shape
     L = k.shape[0]
     return ora.attention_grads(q.f64(), k.f64(), v.f64(), do.f64(), 1.0 / np.sqrt(D), q_pos0 + np.arange(T),
-                               np.arange(L), causal)
+                               kpos0 + np.arange(L), causal)
 
 
 CASES = [
@@ -160,3 +161,18 @@ def test_delta_is_rowsum_of_dout_times_out(out_dtype):
     ref = terms.sum(axis=1)
     bound = 1e-5 * np.abs(terms).sum(axis=1)
     assert np.all(np.abs(got - ref) <= bound), f"worst {np.max(np.abs(got - ref) / bound):.3e} of the bound"
+
+
+def test_backward_rows_that_see_no_key():
+    """Causal rows before every key: the forward leaves them empty (L = -inf)
+    and the backward must give them exactly zero dQ and add nothing to any dK,
+    dV, with no NaN from exp2(+inf) leaking through the mask."""
+    seed, T, Hq, Hkv, D, lens, order, kpos0 = 46, 70, 4, 2, 128, [50, 64], [1, 0], 20
+    announce(f"bwd rows without keys seed {seed} T={T} keys at {kpos0}..{kpos0 + sum(lens) - 1} q_pos0=0")
+    q, k, v, do = make_case(seed, T, Hq, Hkv, D, lens)
+    dq, dk, dv = gpu_grads(q, k, v, do, lens, order, Hkv=Hkv, q_pos0=0, causal=True, per_visit=False, kpos0=kpos0)
+    rq, rk, rv = oracle_grads(q, k, v, do, 0, True, kpos0)
+    assert not dq[:kpos0].any(), "rows that see no key got a gradient"
+    check_grad(dq, rq, f"seed{seed} dQ")
+    check_grad(dk, rk, f"seed{seed} dK")
+    check_grad(dv, rv, f"seed{seed} dV")
