@@ -67,7 +67,12 @@ ba_status check_problem(const ba_problem* p, const void* q) {
   return BA_OK;
 }
 
-ba_status check_block(const ba_kv_block& b, int i, int dtype) {
+// Bytes one KV head of `len` keys spans at `stride_token` bf16 elements per key.
+int64_t head_extent_bf16(int64_t len, int64_t stride_token, int head_dim) {
+  return len <= 0 ? 0 : ((len - 1) * stride_token + head_dim) * 2;
+}
+
+ba_status check_block(const ba_kv_block& b, int i, int dtype, int head_dim) {
   if (b.len < 0) return fail(BA_ERR_SHAPE, "block %d: len %d < 0", i, b.len);
   if (b.len == 0) return BA_OK;
   if (!b.k || !b.v) return fail(BA_ERR_NULL, "block %d: k or v is NULL", i);
@@ -78,6 +83,11 @@ ba_status check_block(const ba_kv_block& b, int i, int dtype) {
       return fail(BA_ERR_SHAPE, "block %d: k/v not 16-byte aligned", i);
     if (b.k_stride_token % 8 || b.k_stride_head % 8 || b.v_stride_token % 8 || b.v_stride_head % 8)
       return fail(BA_ERR_SHAPE, "block %d: bf16 strides must be multiples of 8 elements", i);
+    // The bf16 kernels read one KV head of a block through a buffer resource
+    // with 32-bit byte offsets.
+    if (head_extent_bf16(b.len, b.k_stride_token, head_dim) > (int64_t)UINT32_MAX ||
+        head_extent_bf16(b.len, b.v_stride_token, head_dim) > (int64_t)UINT32_MAX)
+      return fail(BA_ERR_SHAPE, "block %d: one KV head spans 4 GiB or more (bf16 kernels use 32-bit offsets)", i);
   }
   return BA_OK;
 }
@@ -214,7 +224,7 @@ ba_status prepare_fwd(const ba_problem* p, const void* q, const ba_kv_block* blo
   st = resolve_order(n_blocks, order, n_visit, v);
   if (st) return st;
   for (int j : v.idx) {
-    st = check_block(blocks[j], j, p->dtype);
+    st = check_block(blocks[j], j, p->dtype, p->head_dim);
     if (st) return st;
   }
   split = fwd_uses_split(p);
@@ -369,7 +379,7 @@ ba_status blockattn_bwd_block(const ba_problem* p, const void* q, const void* do
   st = resolve_order(n_blocks, order, n_visit, v);
   if (st) return st;
   for (int j : v.idx) {
-    st = check_block(blocks[j], j, p->dtype);
+    st = check_block(blocks[j], j, p->dtype, p->head_dim);
     if (st) return st;
   }
   if (p->q_len == 0 || v.idx.empty()) return ok();
@@ -424,7 +434,7 @@ size_t blockattn_shard_workspace_bytes(const ba_problem* p, const ba_kv_block* b
   if (p->dtype != BA_BF16 || p->q_len == 0) return 0;
   std::vector<int64_t> keys;
   for (int i = 0; i < n_blocks; ++i) {
-    if (check_block(blocks[i], i, p->dtype) != BA_OK) return 0;
+    if (check_block(blocks[i], i, p->dtype, p->head_dim) != BA_OK) return 0;
     keys.push_back(usable_keys(p, blocks[i]));
   }
   SplitPlan sp = plan_split(keys, row_tiles(p));
@@ -442,7 +452,7 @@ ba_status blockattn_shard_states(const ba_problem* p, const void* q, const ba_kv
   if (!blocks || !states_out) return fail(BA_ERR_NULL, "blocks or states_out is NULL");
   std::vector<int64_t> keys;
   for (int i = 0; i < n_blocks; ++i) {
-    st = check_block(blocks[i], i, p->dtype);
+    st = check_block(blocks[i], i, p->dtype, p->head_dim);
     if (st) return st;
     st = check_state(states_out[i], "states_out");
     if (st) return st;
@@ -565,6 +575,11 @@ ba_status check_fanout_shape(const FanoutShape& f) {
   if (f.nb < 0 || f.P < 0 || f.S < 0) return fail(BA_ERR_SHAPE, "negative size");
   if (f.nb > 0 && f.P + f.S == 0) return fail(BA_ERR_SHAPE, "no keys to attend to");
   if ((int64_t)f.nb * f.T * f.Hq > ((int64_t)1 << 31) / 2) return fail(BA_ERR_SHAPE, "too many query rows");
+  // One KV head of the prefix, and of one branch's suffix, is read through a
+  // buffer resource with 32-bit byte offsets.
+  if (head_extent_bf16(f.P, (int64_t)f.Hkv * f.D, f.D) > (int64_t)UINT32_MAX ||
+      head_extent_bf16(f.S, (int64_t)f.Hkv * f.D, f.D) > (int64_t)UINT32_MAX)
+    return fail(BA_ERR_SHAPE, "prefix or suffix: one KV head spans 4 GiB or more (32-bit offsets)");
   return BA_OK;
 }
 

@@ -147,7 +147,8 @@ typedef struct {
  *
  * Errors: BA_ERR_NULL (p, q, blocks with n_visit > 0, a block's k/v with
  * len > 0, or a state array); BA_ERR_SHAPE (bad head counts, head_dim, negative
- * lengths, non-positive strides); BA_ERR_ORDER (duplicate/out-of-range order
+ * lengths, non-positive strides, a bf16 block one of whose KV heads spans
+ * 4 GiB or more: the bf16 kernels address it with 32-bit offsets); BA_ERR_ORDER (duplicate/out-of-range order
  * entry, n_visit > BLOCKATTN_MAX_VISITS or > n_blocks); BA_ERR_UNSUPPORTED
  * (dtype); BA_ERR_WORKSPACE. */
 ba_status blockattn_fwd_block(const ba_problem* p, const void* q,
@@ -218,7 +219,8 @@ ba_status blockattn_finalize(ba_state st, int64_t rows, int32_t head_dim,
  * merged by log-sum-exp and finalised.  Writes out [n_branches, n_q_heads,
  * head_dim] bf16 and, if lse is not NULL, lse [n_branches, n_q_heads] fp32.
  * Needs fanout_workspace_bytes() bytes of workspace.  Errors: BA_ERR_NULL,
- * BA_ERR_SHAPE (no keys at all, bad heads or head_dim), BA_ERR_WORKSPACE. */
+ * BA_ERR_SHAPE (no keys at all, bad heads or head_dim, one KV head of the
+ * prefix or of a suffix spanning 4 GiB or more), BA_ERR_WORKSPACE. */
 ba_status fanout_prefix_decode(const ba_fanout* f, const void* q,
                                const void* prefix_k, const void* prefix_v,
                                const void* suffix_k, const void* suffix_v,

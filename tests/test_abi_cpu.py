@@ -251,3 +251,17 @@ def test_bwd_delta_validation(lib):
     assert call(os_=64) == 2
     assert call(gs=132) == 2
     assert call(dout=FAKE + 8) == 2
+
+
+def test_bf16_blocks_beyond_32bit_offsets_are_rejected(lib):
+    """One KV head of a bf16 block must span less than 4 GiB (the kernels'
+    buffer offsets are 32-bit): 2^21 + 1 keys at 1024 elements per key span
+    4 GiB + 256 B and are rejected.  (Only rejected calls here: nothing may
+    reach a kernel launch with the fake pointers.)"""
+    big = _blocks(1, length=(1 << 21) + 1)
+    big[0].k_stride_token = big[0].v_stride_token = 1024
+    assert _fwd(lib, _problem(), big, 1, None, 1) == 2
+    assert b"4 GiB" in lib.blockattn_last_error()
+    assert _bwd(lib, blocks=big, n_blocks=1, order=None, n_visit=1, dk=(FAKE,), dv=(FAKE,)) == 2
+    f = ba.Fanout(4, 64, 8, 128, (1 << 21) + 1, 16, 0.0)
+    assert lib.fanout_prefix_decode(ctypes.byref(f), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 2
