@@ -166,6 +166,28 @@ def _dim_contig(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be [tokens, heads, head_dim] with a contiguous head_dim axis")
 
 
+def _check_state(state, rows: int, head_dim: int, name: str = "state"):
+    """The library reads and writes the first rows entries of m and l and the
+    first rows x head_dim of o: the tensors must be contiguous fp32 holding at
+    least that (o with rows of exactly head_dim)."""
+    m, l, o = state
+    for t, n in ((m, "m"), (l, "l")):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() < rows:
+            raise ValueError(f"{name}.{n} must be contiguous fp32 with at least {rows} entries")
+    if o.dtype != torch.float32 or not o.is_contiguous() or o.dim() != 2 or o.shape[1] != head_dim or \
+            o.shape[0] < rows:
+        raise ValueError(f"{name}.o must be contiguous fp32 [>= {rows}, {head_dim}]")
+
+
+def _check_blocks(blocks, n_kv_heads: int, head_dim: int, dtype):
+    """Every K/V block must carry n_kv_heads heads of head_dim in the problem's dtype."""
+    for i, (k, v, _) in enumerate(blocks):
+        for t, n in ((k, "k"), (v, "v")):
+            if t.dim() != 3 or t.shape[1] != n_kv_heads or t.shape[2] != head_dim or t.dtype != dtype:
+                raise ValueError(f"block {i}: {n} must be [len, {n_kv_heads}, {head_dim}] {dtype}, got "
+                                 f"{tuple(t.shape)} {t.dtype}")
+
+
 def new_state(rows: int, head_dim: int, device="cuda") -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Uninitialised fp32 state buffers (m [rows], l [rows], o [rows, D])."""
     return (torch.empty(rows, dtype=torch.float32, device=device),
@@ -205,6 +227,9 @@ def fwd_block(q: torch.Tensor, blocks: Sequence[Tuple[torch.Tensor, torch.Tensor
     """blockattn_fwd_block: walk ``blocks`` in ``order`` updating ``state`` (m, l, o) in place."""
     lib = load()
     p = make_problem(q, n_kv_heads, q_pos0, causal, scale, split_mode)
+    T, Hq, D = q.shape
+    _check_blocks(blocks, n_kv_heads, D, q.dtype)
+    _check_state(state, T * Hq, D)
     arr = make_blocks(blocks)
     n_visit = len(order) if order is not None else len(blocks)
     order_arr = (ctypes.c_int32 * max(1, n_visit))(*(order or []))
@@ -235,8 +260,14 @@ def shard_states(q: torch.Tensor, blocks, states_out, *, n_kv_heads: int, q_pos0
     """blockattn_shard_states: one partial state per block into ``states_out``."""
     lib = load()
     p = make_problem(q, n_kv_heads, q_pos0, causal, scale, 0)
+    T, Hq, D = q.shape
+    _check_blocks(blocks, n_kv_heads, D, q.dtype)
+    if len(states_out) != len(blocks):
+        raise ValueError("one output state per block")
+    for i, st in enumerate(states_out):
+        _check_state(st, T * Hq, D, f"states_out[{i}]")
     arr = make_blocks(blocks)
-    sts = (State * len(blocks))(*[_state(s) for s in states_out])
+    sts = (State * max(1, len(blocks)))(*[_state(s) for s in states_out])
     need = lib.blockattn_shard_workspace_bytes(ctypes.byref(p), arr, len(blocks))
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -250,7 +281,10 @@ def merge_states(parts, out, stream=None):
     """blockattn_merge_states over a list of (m, l, o) states into ``out``."""
     lib = load()
     rows, D = out[2].shape
-    arr = (State * len(parts))(*[_state(s) for s in parts])
+    _check_state(out, rows, D, "out")
+    for i, st in enumerate(parts):
+        _check_state(st, rows, D, f"parts[{i}]")
+    arr = (State * max(1, len(parts)))(*[_state(s) for s in parts])
     _check(lib.blockattn_merge_states(len(parts), arr, rows, D, _state(out), _stream(stream)),
            "blockattn_merge_states")
     return out
@@ -262,14 +296,40 @@ def finalize(state, out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None
     lib = load()
     m, l, o = state
     rows, D = o.shape
+    _check_state(state, rows, D)
     if out is None:
         out = torch.empty(rows, D, dtype=out_dtype, device=o.device)
+    elif out.dim() != 2 or out.shape[0] != rows or out.shape[1] != D or out.stride(1) != 1 or \
+            out.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"out must be bf16 or fp32 [{rows}, {D}] with contiguous rows")
     if lse is None and want_lse:
         lse = torch.empty(rows, dtype=torch.float32, device=o.device)
+    elif lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != rows):
+        raise ValueError(f"lse must be contiguous fp32 with {rows} entries")
     code = BA_BF16 if out.dtype == torch.bfloat16 else BA_F32
     _check(lib.blockattn_finalize(_state(state), rows, D, _ptr(out), code, out.stride(0), _ptr(lse),
                                   _stream(stream)), "blockattn_finalize")
     return out, lse
+
+
+def _check_fanout(q, prefix_k, prefix_v, suffix_k, suffix_v, out, lse, rows_shape, Hkv, D, P, S):
+    """Shapes the fan-out entry points read and write: q and out are
+    rows_shape + [D] (out bf16), lse rows_shape (fp32), the prefix [P, Hkv, D]
+    and each suffix [nb, S, Hkv, D]; all contiguous."""
+    nb = rows_shape[0]
+    want = {"prefix_k": (prefix_k, (P, Hkv, D)), "prefix_v": (prefix_v, (P, Hkv, D)),
+            "suffix_k": (suffix_k, (nb, S, Hkv, D)), "suffix_v": (suffix_v, (nb, S, Hkv, D))}
+    for name, (t, shape) in want.items():
+        if t is not None and tuple(t.shape) != shape:
+            raise ValueError(f"{name} must have shape {shape}, got {tuple(t.shape)}")
+    if (prefix_k is None) != (prefix_v is None) or (suffix_k is None) != (suffix_v is None):
+        raise ValueError("k and v come in pairs (prefix and suffix)")
+    if out is not None and (tuple(out.shape) != tuple(rows_shape) + (D,) or out.dtype != torch.bfloat16
+                            or not out.is_contiguous()):
+        raise ValueError(f"out must be contiguous bf16 of shape {tuple(rows_shape) + (D,)}")
+    if lse is not None and (tuple(lse.shape) != tuple(rows_shape) or lse.dtype != torch.float32
+                            or not lse.is_contiguous()):
+        raise ValueError(f"lse must be contiguous fp32 of shape {tuple(rows_shape)}")
 
 
 def fanout_prefix_decode(q, prefix_k, prefix_v, suffix_k, suffix_v, scale: float = 0.0,
@@ -285,6 +345,7 @@ def fanout_prefix_decode(q, prefix_k, prefix_v, suffix_k, suffix_v, scale: float
                     ("suffix_v", suffix_v)):
         if t is not None and (not t.is_contiguous() or t.dtype != torch.bfloat16):
             raise ValueError(f"{name} must be contiguous bf16")
+    _check_fanout(q, prefix_k, prefix_v, suffix_k, suffix_v, out, lse, (nb, Hq), Hkv, D, P, S)
     f = Fanout(nb, Hq, Hkv, D, P, S, scale)
     need = lib.fanout_workspace_bytes(ctypes.byref(f))
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
@@ -320,6 +381,7 @@ def fanout_prefix_prefill(q, prefix_k, prefix_v, suffix_k, suffix_v, scale: floa
                     ("suffix_v", suffix_v)):
         if t is not None and (not t.is_contiguous() or t.dtype != torch.bfloat16):
             raise ValueError(f"{name} must be contiguous bf16")
+    _check_fanout(q, prefix_k, prefix_v, suffix_k, suffix_v, out, lse, (nb, T, Hq), Hkv, D, P, S)
     f = FanoutPrefill(nb, T, Hq, Hkv, D, P, S, scale)
     need = lib.fanout_prefill_workspace_bytes(ctypes.byref(f))
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
@@ -350,9 +412,15 @@ def bwd_delta(out: torch.Tensor, dout: torch.Tensor, delta: Optional[torch.Tenso
     g2 = dout.reshape(-1, D)
     if o2.stride(1) != 1 or g2.stride(1) != 1 or dout.dtype != torch.bfloat16:
         raise ValueError("out and dout need a contiguous last axis; dout must be bf16")
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out must be bf16 or fp32")
     rows = o2.shape[0]
+    if g2.shape != o2.shape:
+        raise ValueError(f"dout {tuple(g2.shape)} must match out {tuple(o2.shape)} row for row")
     if delta is None:
         delta = torch.empty(rows, dtype=torch.float32, device=out.device)
+    elif delta.dtype != torch.float32 or not delta.is_contiguous() or delta.numel() != rows:
+        raise ValueError(f"delta must be contiguous fp32 with {rows} entries")
     code = BA_BF16 if out.dtype == torch.bfloat16 else BA_F32
     _check(lib.blockattn_bwd_delta(rows, D, _ptr(o2), code, o2.stride(0), _ptr(g2), g2.stride(0), _ptr(delta),
                                    _stream(stream)), "blockattn_bwd_delta")
@@ -369,16 +437,13 @@ def bwd_block(q: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor, delta: tor
     if dout.shape != q.shape or dout.stride() != q.stride() or dout.dtype != torch.bfloat16:
         raise ValueError("dout must be bf16 with q's shape and strides")
     p = make_problem(q, n_kv_heads, q_pos0, causal, scale, 0)
-    arr = make_blocks(blocks)
-    n_visit = len(order) if order is not None else len(blocks)
-    order_arr = (ctypes.c_int32 * max(1, n_visit))(*(order or []))
-    dks = (ctypes.c_void_p * max(1, len(blocks)))(*[t[0].data_ptr() for t in dkv])
-    dvs = (ctypes.c_void_p * max(1, len(blocks)))(*[t[1].data_ptr() for t in dkv])
     T, Hq, D = q.shape
+    _check_blocks(blocks, n_kv_heads, D, q.dtype)
     if dq.dtype != torch.float32 or not dq.is_contiguous() or dq.numel() != T * Hq * D:
         raise ValueError("dq must be contiguous fp32 with q_len * n_q_heads * head_dim elements")
-    if lse.numel() != T * Hq or delta.numel() != T * Hq:
-        raise ValueError("lse and delta need one fp32 entry per (token, query head)")
+    for name, t in (("lse", lse), ("delta", delta)):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != T * Hq:
+            raise ValueError(f"{name} must be contiguous fp32 with one entry per (token, query head)")
     if len(dkv) != len(blocks):
         raise ValueError("one (dk, dv) pair per block")
     for (kb, _, _), (dk, dv) in zip(blocks, dkv):
@@ -387,6 +452,11 @@ def bwd_block(q: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor, delta: tor
             raise ValueError("dk and dv must be contiguous fp32")
         if tuple(dk.shape) != want or tuple(dv.shape) != want:
             raise ValueError(f"dk and dv of a block of {kb.shape[0]} keys must have shape {want}")
+    arr = make_blocks(blocks)
+    n_visit = len(order) if order is not None else len(blocks)
+    order_arr = (ctypes.c_int32 * max(1, n_visit))(*(order or []))
+    dks = (ctypes.c_void_p * max(1, len(blocks)))(*[t[0].data_ptr() for t in dkv])
+    dvs = (ctypes.c_void_p * max(1, len(blocks)))(*[t[1].data_ptr() for t in dkv])
     _check(lib.blockattn_bwd_block(ctypes.byref(p), _ptr(q), _ptr(dout), _ptr(lse), _ptr(delta), arr, len(blocks),
                                    order_arr if order is not None else None, n_visit, _ptr(dq), dks, dvs,
                                    _stream(stream)), "blockattn_bwd_block")
