@@ -460,6 +460,50 @@ def fanout_prefill(q, prefix_k, prefix_v, suffix_k, suffix_v, scale):
     return a, lse
 
 
+def page_gather(pool, pages, n, page_len, n_pool):
+    """The tokens of a paged sequence ([AHBM] 3.1: a context is a page table
+    over pages that are referenced, not copied).  Token t (0 <= t < n) is row
+    t % page_len of pool page pages[t // page_len]; a page id outside
+    [0, n_pool) holds no tokens (the reading taken: its tokens are left out and
+    no other token moves).  Returns (rows [m, ...], token indices [m]) in token
+    order."""
+    rows, idx = [], []
+    for t in range(n):
+        pid = int(pages[t // page_len])
+        if 0 <= pid < n_pool:
+            rows.append(np.asarray(pool[pid][t % page_len], dtype=np.float64))
+            idx.append(t)
+    shape = np.asarray(pool).shape[2:]
+    return (np.stack(rows) if rows else np.zeros((0,) + tuple(shape))), np.asarray(idx, dtype=np.int64)
+
+
+def fanout_paged(q, k_pool, v_pool, prefix_pages, suffix_pages, page_len, P, S, scale):
+    """Fan-out over paged K/V, by definition: branch b's context is the shared
+    prefix pages followed by its own suffix pages ([AHBM] 3.1), gathered by
+    page_gather; prefix token t sits at position t, suffix token j at P + j,
+    the branch's new token i at P + S - T + i, and the causal rule applies (as
+    in fanout_prefill).  q [nb, T, Hq, D]; pools [n_pool, page_len, Hkv, D];
+    suffix_pages [nb, ceil(S / page_len)].  Returns (A [nb, T, Hq, D], LSE [nb, T, Hq])."""
+    q = np.asarray(q, dtype=np.float64)
+    nb, T = q.shape[:2]
+    n_pool = np.asarray(k_pool).shape[0]
+    pk, pt = page_gather(k_pool, prefix_pages, P, page_len, n_pool)
+    pv, _ = page_gather(v_pool, prefix_pages, P, page_len, n_pool)
+    a = np.empty(q.shape)
+    lse = np.empty(q.shape[:3])
+    for b in range(nb):
+        sk, st = page_gather(k_pool, suffix_pages[b], S, page_len, n_pool)
+        sv, _ = page_gather(v_pool, suffix_pages[b], S, page_len, n_pool)
+        keys = np.concatenate([pk, sk], axis=0)
+        vals = np.concatenate([pv, sv], axis=0)
+        k_pos = np.concatenate([pt, P + st])
+        q_pos = P + S - T + np.arange(T)
+        ab, _, _, lb = attend(q[b], keys, vals, scale, q_pos, k_pos, causal=True)
+        a[b] = ab
+        lse[b] = lb
+    return a, lse
+
+
 def fanout_state_rows(q, k, v, scale):
     """Partial state of fan-out rows against one KV range (no mask).
 

@@ -345,6 +345,62 @@ def pin_fanout_prefill():
         _close(lse[b], LSE, 1e-13, 0, "prefill brute lse")
 
 
+def _pages_of(x, page_len):
+    """Cut x [n, ...] into page_len-row pages (the last zero-padded)."""
+    n = x.shape[0]
+    out = []
+    for p0 in range(0, n, page_len):
+        page = np.zeros((page_len,) + x.shape[1:])
+        page[:min(page_len, n - p0)] = x[p0:p0 + page_len]
+        out.append(page)
+    return out
+
+
+def pin_fanout_paged():
+    """Paged fan-out: pages scattered over a pool in a random order give the
+    contiguous fan-out prefill exactly; a prefix page with an id outside the
+    pool gives the prefill over the prefix with that page's tokens removed."""
+    g = _rng(97)
+    nb, T, Hq, Hkv, D, P, S, PL = 2, 3, 4, 2, 8, 10, 6, 4
+    q = g.standard_normal((nb, T, Hq, D))
+    pk, pv = g.standard_normal((P, Hkv, D)), g.standard_normal((P, Hkv, D))
+    sk, sv = g.standard_normal((nb, S, Hkv, D)), g.standard_normal((nb, S, Hkv, D))
+    s = 1.0 / math.sqrt(D)
+    kp, vp = _pages_of(pk, PL), _pages_of(pv, PL)
+    ks = [_pages_of(sk[b], PL) for b in range(nb)]
+    vs = [_pages_of(sv[b], PL) for b in range(nb)]
+    n_used = len(kp) + sum(len(x) for x in ks)
+    n_pool = n_used + 2
+    perm = g.permutation(n_pool)
+    k_pool = g.standard_normal((n_pool, PL, Hkv, D))   # unused pool pages hold noise
+    v_pool = g.standard_normal((n_pool, PL, Hkv, D))
+    slots = iter(perm[:n_used])
+    prefix_pages = []
+    for kpg, vpg in zip(kp, vp):
+        i = next(slots)
+        k_pool[i], v_pool[i] = kpg, vpg
+        prefix_pages.append(i)
+    suffix_pages = []
+    for b in range(nb):
+        row = []
+        for kpg, vpg in zip(ks[b], vs[b]):
+            i = next(slots)
+            k_pool[i], v_pool[i] = kpg, vpg
+            row.append(i)
+        suffix_pages.append(row)
+    a, lse = ora.fanout_paged(q, k_pool, v_pool, prefix_pages, suffix_pages, PL, P, S, s)
+    ra, rlse = ora.fanout_prefill(q, pk, pv, sk, sv, s)
+    _close(a, ra, 1e-13, 1e-14, "paged vs contiguous")
+    _close(lse, rlse, 1e-13, 0, "paged vs contiguous lse")
+    bad = list(prefix_pages)
+    bad[1] = n_pool + 5
+    a2, lse2 = ora.fanout_paged(q, k_pool, v_pool, bad, suffix_pages, PL, P, S, s)
+    keep = np.r_[0:PL, 2 * PL:P]
+    ra2, rlse2 = ora.fanout_prefill(q, pk[keep], pv[keep], sk, sv, s)
+    _close(a2, ra2, 1e-13, 1e-14, "paged with a page outside the pool")
+    _close(lse2, rlse2, 1e-13, 0, "paged with a page outside the pool lse")
+
+
 def _loss_and_grads_fd(q, k, v, d_out, scale, q_pos, k_pos, causal, eps=1e-6):
     """Central finite differences of sum(A * d_out) -- independent of any gradient formula."""
     def loss(q_, k_, v_):
@@ -538,6 +594,7 @@ ALL_PINS = [
     pin_ring_emulation,
     pin_fanout_decode,
     pin_fanout_prefill,
+    pin_fanout_paged,
     pin_attention_grads_finite_differences,
     pin_attention_grads_autograd,
     pin_backward_ring_is_full_gradient,

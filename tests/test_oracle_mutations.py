@@ -156,7 +156,16 @@ def _grads_dk_unscaled(q, k, v, d_out, scale, q_pos=None, k_pos=None, causal=Fal
     return dq, dk / scale, dv
 
 
+_orig_page_gather = ora.page_gather
+
+
+def _page_row_shifted(pool, pages, n, page_len, n_pool):
+    shifted = [np.roll(np.asarray(x), 1, axis=0) for x in pool]
+    return _orig_page_gather(np.stack(shifted), pages, n, page_len, n_pool)
+
+
 MUTATIONS = {
+    "page row offset by one": ("page_gather", _page_row_shifted),
     "softmax Jacobian row term dropped": ("attention_grads", _grads_without_delta),
     "dK missing the scale": ("attention_grads", _grads_dk_unscaled),
     "prefill new tokens one position early": ("fanout_prefill", _prefill_offset_by_one),
