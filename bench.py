@@ -307,6 +307,48 @@ def bench_fanout(torch, ba, H, w, steps, warmup):
             "timing": "median over steps, HIP events around the call, 1 GiB read between calls evicts the caches"}
 
 
+def bench_fanout_paged(torch, ba, H, w, steps, warmup, page_len=256):
+    """The fan-out decode workload with its prefix and private suffixes in a
+    page pool (page_len-token pages, seeded random pool order), timed like
+    bench_fanout; the algorithmic bytes are the same."""
+    from exact_blockwise_long_amd import workloads as wl
+    log(f"inputs: {w.name}, paged (page_len {page_len})")
+    q, pk, pv, sk, sv = w.make_inputs()
+    g = np.random.Generator(np.random.PCG64(w.seed + 500))
+    n_pool, pp, sp = wl.paged_layout(g, w.n_branches, w.prefix_len, w.suffix_len, page_len)
+    kd = H.to_device(wl.scatter_pages(g, pk, sk, n_pool, pp, sp, page_len))
+    vd = H.to_device(wl.scatter_pages(g, pv, sv, n_pool, pp, sp, page_len))
+    del pk, pv, sk, sv
+    qd = H.to_device(q)
+    ppd, spd = torch.from_numpy(pp).cuda(), torch.from_numpy(sp).cuda()
+    nb, Hq, D = qd.shape
+    out = torch.empty(nb, Hq, D, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(nb, Hq, dtype=torch.float32, device="cuda")
+    ws = torch.empty(ba.fanout_workspace_bytes(nb, Hq, w.n_kv_heads, D, w.prefix_len, w.suffix_len),
+                     dtype=torch.uint8, device="cuda")
+    flush = flush_buffer(torch)
+
+    def call():
+        ba.fanout_prefix_decode_paged(qd, kd, vd, ppd, spd, w.prefix_len, w.suffix_len, workspace=ws, out=out,
+                                      lse=lse)
+
+    for _ in range(warmup):
+        call()
+    timer = Timer(torch)
+    for _ in range(steps):
+        flush()
+        e0 = timer.start()
+        call()
+        timer.stop(e0)
+    torch.cuda.synchronize()
+    ms = timer.median_ms()
+    gbs = w.bytes() / ms / 1e6
+    log(f"fanout paged: {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
+    return {"workload": w.name + f", paged (page_len {page_len}, random pool order)", "us": round(ms * 1e3, 2),
+            "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "pool_pages": int(n_pool),
+            "timing": "median over steps, HIP events around the call, 1 GiB read between calls evicts the caches"}
+
+
 def bench_shard_merge(torch, ba, H, w, steps, warmup):
     log(f"inputs: {w.name}")
     q, k, v = w.make_inputs()
@@ -522,7 +564,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="all",
                     choices=["all", "causal_prefill", "ring_share", "fanout", "shard_merge", "merge_scaled",
-                             "layouts", "fanout_prefill", "backward", "copy_calibration"])
+                             "layouts", "fanout_prefill", "fanout_paged", "backward", "copy_calibration"])
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -557,6 +599,8 @@ def main():
         secondary["fanout_prefill"] = bench_fanout_prefill(torch, ba, H, wl.FANOUT_PREFILL, args.steps, args.warmup)
     if only == "layouts":
         secondary["causal_ring_layouts"] = bench_layouts(torch, ba, H, wl.CAUSAL_RING_LAYOUTS, max(1, args.steps // 10))
+    if only == "fanout_paged":
+        secondary["fanout_decode_paged"] = bench_fanout_paged(torch, ba, H, wl.FANOUT_DECODE, args.steps, args.warmup)
     if only == "backward":
         secondary["backward"] = bench_backward(torch, ba, H, wl.CAUSAL_PREFILL, args.steps, args.warmup)
     if only == "copy_calibration":
@@ -601,6 +645,8 @@ def main():
             line["roofline"]["clock"] = clk
     if not args.no_secondary and only == "all":
         secondary["fanout_decode"] = bench_fanout(torch, ba, H, wl.FANOUT_DECODE, args.steps, args.warmup)
+        secondary["fanout_decode_paged"] = bench_fanout_paged(torch, ba, H, wl.FANOUT_DECODE, args.steps,
+                                                               args.warmup)
         secondary["fanout_prefill"] = bench_fanout_prefill(torch, ba, H, wl.FANOUT_PREFILL, args.steps, args.warmup)
         secondary["shard_merge"] = bench_shard_merge(torch, ba, H, wl.SHARD_MERGE, args.steps, args.warmup)
         secondary["merge_scaled"] = bench_merge_scaled(torch, ba, args.steps, args.warmup)

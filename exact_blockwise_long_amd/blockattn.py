@@ -71,11 +71,18 @@ class FanoutPrefill(ctypes.Structure):
     ]
 
 
+class KVPages(ctypes.Structure):
+    _fields_ = [
+        ("prefix_pages", ctypes.c_void_p), ("suffix_pages", ctypes.c_void_p), ("page_len", ctypes.c_int32),
+        ("n_pool_pages", ctypes.c_int32),
+    ]
+
+
 EXPORTS = [
     "blockattn_fwd_block", "blockattn_fwd_workspace_bytes", "blockattn_shard_states",
     "blockattn_shard_workspace_bytes", "blockattn_merge_states", "blockattn_finalize",
     "fanout_prefix_decode", "fanout_workspace_bytes", "fanout_prefix_prefill",
-    "fanout_prefill_workspace_bytes", "blockattn_bwd_delta", "blockattn_bwd_block", "blockattn_status_str",
+    "fanout_prefill_workspace_bytes", "fanout_prefix_decode_paged", "fanout_prefix_prefill_paged", "blockattn_bwd_delta", "blockattn_bwd_block", "blockattn_status_str",
     "blockattn_last_error", "blockattn_abi_version",
 ]
 
@@ -128,6 +135,10 @@ def load():
     lib.fanout_prefix_prefill.restype = i32
     lib.fanout_prefill_workspace_bytes.argtypes = [P(FanoutPrefill)]
     lib.fanout_prefill_workspace_bytes.restype = sz
+    lib.fanout_prefix_decode_paged.argtypes = [P(Fanout), P(KVPages), vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.fanout_prefix_decode_paged.restype = i32
+    lib.fanout_prefix_prefill_paged.argtypes = [P(FanoutPrefill), P(KVPages), vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.fanout_prefix_prefill_paged.restype = i32
     lib.blockattn_status_str.argtypes = [i32]
     lib.blockattn_status_str.restype = ctypes.c_char_p
     lib.blockattn_last_error.argtypes = []
@@ -461,3 +472,83 @@ def bwd_block(q: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor, delta: tor
                                    order_arr if order is not None else None, n_visit, _ptr(dq), dks, dvs,
                                    _stream(stream)), "blockattn_bwd_block")
     return dq, dkv
+
+
+def _paged_args(q, k_pool, v_pool, prefix_pages, suffix_pages, prefix_len, suffix_len, rows_shape, out, lse):
+    """Checks the pools and page tables of the paged fan-out and returns
+    (n_kv_heads, head_dim, KVPages)."""
+    if k_pool.dim() != 4 or tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError("k_pool and v_pool must be [n_pool_pages, page_len, n_kv_heads, head_dim], same shape")
+    n_pool, PL, Hkv, D = k_pool.shape
+    for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool)):
+        if not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be contiguous bf16")
+    if q.shape[-1] != D:
+        raise ValueError(f"q head_dim {q.shape[-1]} != pool head_dim {D}")
+    nb = rows_shape[0]
+    per_branch = -(-suffix_len // PL) if PL > 0 else 0
+    for name, t, need in (("prefix_pages", prefix_pages, -(-prefix_len // PL) if PL > 0 else 0),
+                          ("suffix_pages", suffix_pages, nb * per_branch)):
+        if need == 0:
+            continue
+        if t is None or t.dtype != torch.int32 or not t.is_contiguous() or t.numel() < need:
+            raise ValueError(f"{name} must be contiguous int32 with at least {need} entries")
+    if suffix_len > 0 and suffix_pages.dim() == 2 and tuple(suffix_pages.shape) != (nb, per_branch):
+        raise ValueError(f"suffix_pages must be [{nb}, {per_branch}]")
+    if out is not None and (tuple(out.shape) != tuple(rows_shape) + (D,) or out.dtype != torch.bfloat16
+                            or not out.is_contiguous()):
+        raise ValueError(f"out must be contiguous bf16 of shape {tuple(rows_shape) + (D,)}")
+    if lse is not None and (tuple(lse.shape) != tuple(rows_shape) or lse.dtype != torch.float32
+                            or not lse.is_contiguous()):
+        raise ValueError(f"lse must be contiguous fp32 of shape {tuple(rows_shape)}")
+    pages = KVPages(prefix_pages.data_ptr() if prefix_pages is not None else None,
+                    suffix_pages.data_ptr() if suffix_pages is not None else None, PL, n_pool)
+    return Hkv, D, pages
+
+
+def fanout_prefix_decode_paged(q, k_pool, v_pool, prefix_pages, suffix_pages, prefix_len: int, suffix_len: int,
+                               scale: float = 0.0, workspace: Optional[torch.Tensor] = None, want_lse: bool = True,
+                               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, stream=None):
+    """fanout_prefix_decode_paged: q [nb, Hq, D]; pools [n_pool, page_len, Hkv, D] bf16; prefix_pages int32
+    [>= ceil(P / page_len)] and suffix_pages int32 [nb, ceil(S / page_len)] (device).  Returns (out, lse)."""
+    lib = load()
+    nb, Hq, D = q.shape
+    Hkv, D, pages = _paged_args(q, k_pool, v_pool, prefix_pages, suffix_pages, prefix_len, suffix_len, (nb, Hq),
+                                out, lse)
+    f = Fanout(nb, Hq, Hkv, D, prefix_len, suffix_len, scale)
+    need = lib.fanout_workspace_bytes(ctypes.byref(f))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if out is None:
+        out = torch.empty(nb, Hq, D, dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty(nb, Hq, dtype=torch.float32, device=q.device)
+    _check(lib.fanout_prefix_decode_paged(ctypes.byref(f), ctypes.byref(pages), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                          _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)),
+           "fanout_prefix_decode_paged")
+    return out, lse
+
+
+def fanout_prefix_prefill_paged(q, k_pool, v_pool, prefix_pages, suffix_pages, prefix_len: int, suffix_len: int,
+                                scale: float = 0.0, workspace: Optional[torch.Tensor] = None, want_lse: bool = True,
+                                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, stream=None):
+    """fanout_prefix_prefill_paged: q [nb, T, Hq, D] (each branch's T newest tokens, the last T of its suffix);
+    pools and page tables as fanout_prefix_decode_paged.  Returns (out [nb, T, Hq, D], lse [nb, T, Hq])."""
+    lib = load()
+    nb, T, Hq, D = q.shape
+    Hkv, D, pages = _paged_args(q, k_pool, v_pool, prefix_pages, suffix_pages, prefix_len, suffix_len,
+                                (nb, T, Hq), out, lse)
+    f = FanoutPrefill(nb, T, Hq, Hkv, D, prefix_len, suffix_len, scale)
+    need = lib.fanout_prefill_workspace_bytes(ctypes.byref(f))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if out is None:
+        out = torch.empty(nb, T, Hq, D, dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty(nb, T, Hq, dtype=torch.float32, device=q.device)
+    _check(lib.fanout_prefix_prefill_paged(ctypes.byref(f), ctypes.byref(pages), _ptr(q), _ptr(k_pool),
+                                           _ptr(v_pool), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+                                           _stream(stream)), "fanout_prefix_prefill_paged")
+    return out, lse

@@ -575,11 +575,6 @@ ba_status check_fanout_shape(const FanoutShape& f) {
   if (f.nb < 0 || f.P < 0 || f.S < 0) return fail(BA_ERR_SHAPE, "negative size");
   if (f.nb > 0 && f.P + f.S == 0) return fail(BA_ERR_SHAPE, "no keys to attend to");
   if ((int64_t)f.nb * f.T * f.Hq > ((int64_t)1 << 31) / 2) return fail(BA_ERR_SHAPE, "too many query rows");
-  // One KV head of the prefix, and of one branch's suffix, is read through a
-  // buffer resource with 32-bit byte offsets.
-  if (head_extent_bf16(f.P, (int64_t)f.Hkv * f.D, f.D) > (int64_t)UINT32_MAX ||
-      head_extent_bf16(f.S, (int64_t)f.Hkv * f.D, f.D) > (int64_t)UINT32_MAX)
-    return fail(BA_ERR_SHAPE, "prefix or suffix: one KV head spans 4 GiB or more (32-bit offsets)");
   return BA_OK;
 }
 
@@ -662,13 +657,34 @@ size_t fanout_bytes(const FanoutShape& f) {
   return partial_bytes(fp.slots, (int64_t)f.nb * f.T * f.Hq, f.D);
 }
 
+// With `pages`, prefix_k / prefix_v are the page pools and suffix_k /
+// suffix_v are unused.
 ba_status fanout_run(const FanoutShape& f, const void* q, const void* prefix_k, const void* prefix_v,
                      const void* suffix_k, const void* suffix_v, void* out, float* lse, void* workspace,
-                     size_t workspace_bytes, hipStream_t stream) {
+                     size_t workspace_bytes, hipStream_t stream, const ba_kv_pages* pages = nullptr) {
   if (f.nb == 0) return ok();
   if (!q || !out) return fail(BA_ERR_NULL, "q or out is NULL");
-  if (f.P > 0 && (!prefix_k || !prefix_v)) return fail(BA_ERR_NULL, "prefix k/v is NULL");
-  if (f.S > 0 && (!suffix_k || !suffix_v)) return fail(BA_ERR_NULL, "suffix k/v is NULL");
+  if (pages) {
+    if (!prefix_k || !prefix_v) return fail(BA_ERR_NULL, "k_pool or v_pool is NULL");
+    if (((uintptr_t)prefix_k % 16) != 0 || ((uintptr_t)prefix_v % 16) != 0)
+      return fail(BA_ERR_SHAPE, "k_pool/v_pool not 16-byte aligned");
+    if (pages->page_len <= 0 || pages->page_len % 64 != 0)
+      return fail(BA_ERR_SHAPE, "page_len %d is not a positive multiple of 64", pages->page_len);
+    if (pages->n_pool_pages < 1) return fail(BA_ERR_SHAPE, "n_pool_pages %d < 1", pages->n_pool_pages);
+    if (f.P > 0 && !pages->prefix_pages) return fail(BA_ERR_NULL, "prefix_pages is NULL");
+    if (f.S > 0 && !pages->suffix_pages) return fail(BA_ERR_NULL, "suffix_pages is NULL");
+    // Each segment is a piece of one page, read through a 32-bit buffer range.
+    if (head_extent_bf16(pages->page_len, (int64_t)f.Hkv * f.D, f.D) > (int64_t)UINT32_MAX)
+      return fail(BA_ERR_SHAPE, "one KV head of a page spans 4 GiB or more");
+  } else {
+    if (f.P > 0 && (!prefix_k || !prefix_v)) return fail(BA_ERR_NULL, "prefix k/v is NULL");
+    if (f.S > 0 && (!suffix_k || !suffix_v)) return fail(BA_ERR_NULL, "suffix k/v is NULL");
+    // One KV head of the prefix, and of one branch's suffix, is read through a
+    // buffer resource with 32-bit byte offsets.
+    if (head_extent_bf16(f.P, (int64_t)f.Hkv * f.D, f.D) > (int64_t)UINT32_MAX ||
+        head_extent_bf16(f.S, (int64_t)f.Hkv * f.D, f.D) > (int64_t)UINT32_MAX)
+      return fail(BA_ERR_SHAPE, "prefix or suffix: one KV head spans 4 GiB or more (32-bit offsets)");
+  }
   const int D = f.D;
   const int64_t R = (int64_t)f.nb * f.T * f.Hq;
   const FanoutPlan fp = plan_fanout(f);
@@ -715,6 +731,16 @@ ba_status fanout_run(const FanoutShape& f, const void* q, const void* prefix_k, 
   a.suffix_slot = fp.suffix_slot;
   a.srt = fp.srt;
   a.bpj = fp.bpj;
+  if (pages) {
+    // The kernel takes the paged path for a job kind when its table is set.
+    a.sk = nullptr;
+    a.sv = nullptr;
+    a.prefix_pages = f.P > 0 ? pages->prefix_pages : nullptr;
+    a.suffix_pages = f.S > 0 ? pages->suffix_pages : nullptr;
+    a.page_len = pages->page_len;
+    a.n_pool_pages = pages->n_pool_pages;
+    a.suffix_pages_per_branch = (f.S + pages->page_len - 1) / pages->page_len;
+  }
   a.ws_m = wm;
   a.ws_l = wl;
   a.ws_o = wo;
@@ -795,6 +821,26 @@ ba_status fanout_prefix_prefill(const ba_fanout_prefill* f, const void* q, const
   ba_status st = prefill_shape(f, &s);
   if (st) return st;
   return fanout_run(s, q, prefix_k, prefix_v, suffix_k, suffix_v, out, lse, workspace, workspace_bytes, stream);
+}
+
+ba_status fanout_prefix_decode_paged(const ba_fanout* f, const ba_kv_pages* pages, const void* q,
+                                     const void* k_pool, const void* v_pool, void* out, float* lse,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  ba_status st = check_fanout(f);
+  if (st) return st;
+  if (!pages) return fail(BA_ERR_NULL, "pages is NULL");
+  return fanout_run(decode_shape(f), q, k_pool, v_pool, nullptr, nullptr, out, lse, workspace, workspace_bytes,
+                    stream, pages);
+}
+
+ba_status fanout_prefix_prefill_paged(const ba_fanout_prefill* f, const ba_kv_pages* pages, const void* q,
+                                      const void* k_pool, const void* v_pool, void* out, float* lse,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  FanoutShape s;
+  ba_status st = prefill_shape(f, &s);
+  if (st) return st;
+  if (!pages) return fail(BA_ERR_NULL, "pages is NULL");
+  return fanout_run(s, q, k_pool, v_pool, nullptr, nullptr, out, lse, workspace, workspace_bytes, stream, pages);
 }
 
 }  // extern "C"

@@ -274,10 +274,11 @@ __device__ inline Seg chunk_seg(const Seg* seg, int n_seg, const int32_t* chunk_
   return cs;
 }
 
-// Partial state of one row tile over one key range, written to a workspace slot.
-template <int D>
-__device__ inline void partial_job(const QSide& qs, int f0, int f1, int g, const Seg& sg, float* ws_m,
-                                   float* ws_l, float* ws_o, int64_t row_base, lds_char* lds) {
+// Partial state of one row tile over the keys of n_seg segments (get_seg(i)
+// returns segment i), written to a workspace slot.
+template <int D, class GetSeg>
+__device__ inline void partial_job_segs(const QSide& qs, int f0, int f1, int g, int n_seg, GetSeg get_seg,
+                                        float* ws_m, float* ws_l, float* ws_o, int64_t row_base, lds_char* lds) {
   const RowCtx rc = make_rowctx(qs, f0, f1, g);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -288,12 +289,69 @@ __device__ inline void partial_job(const QSide& qs, int f0, int f1, int g, const
   Acc<D> acc;
   init_acc<D>(acc);
   run_segments<D>(
-      qs, rc, 1, [&](int) -> const Seg& { return sg; },
+      qs, rc, n_seg, get_seg,
       [&](const lds_char* stage, bool need_mask, int n_valid, int krel) {
         tile_compute<D>(stage, lane, qf, acc, qs.c, need_mask, qs.causal != 0, n_valid, krel, lr.qrel);
       },
       lds, wave_active);
   store_acc<D>(acc, lane_rows(qs, rc, wave, lane), lane, ws_m, ws_l, ws_o, row_base);
+}
+
+template <int D>
+__device__ inline void partial_job(const QSide& qs, int f0, int f1, int g, const Seg& sg, float* ws_m,
+                                   float* ws_l, float* ws_o, int64_t row_base, lds_char* lds) {
+  partial_job_segs<D>(qs, f0, f1, g, 1, [&](int) -> const Seg& { return sg; }, ws_m, ws_l, ws_o, row_base, lds);
+}
+
+// The page ids of one job's key range [k0, k1) of a paged sequence whose
+// page p is pool page ids[p] ("AHBM Agentic Runtime Architecture" s.3.1: a
+// branch's page table).  Lane i loads the id of the range's i-th page when
+// the job starts, so the key walk reads ids from registers (v_readlane) and
+// never waits on memory at a page boundary; a range of more than 64 pages
+// reads the rest from memory.
+struct PageIds {
+  const int32_t* ids;
+  int first;     // page of key k0
+  int lane_id;   // this lane's page id (lane < 64 pages of the range)
+};
+
+__device__ inline int paged_segments(int k0, int k1, int page_len) {
+  return k1 > k0 ? (k1 - 1) / page_len - k0 / page_len + 1 : 0;
+}
+
+__device__ inline PageIds load_page_ids(const int32_t* ids, int k0, int k1, int page_len) {
+  PageIds pi;
+  pi.ids = ids;
+  pi.first = k0 / page_len;
+  const int lane = threadIdx.x & 63;
+  pi.lane_id = lane < paged_segments(k0, k1, page_len) ? ids[pi.first + lane] : -1;
+  return pi;
+}
+
+// Segment i of the range: the piece of page first + i inside [k0, k1), at
+// positions pos_base + key.  A page id outside the pool gives an empty
+// segment (its keys are left out, nothing is read).
+template <int D>
+__device__ inline Seg paged_seg(const FanoutArgs& a, const PageIds& pi, int k0, int k1, int i, int64_t pos_base) {
+  const int PL = a.page_len;
+  const int p = pi.first + i;
+  const int s0 = max(k0, p * PL);
+  const int s1 = min(k1, (p + 1) * PL);
+  const int id = i < 64 ? __builtin_amdgcn_readlane(pi.lane_id, i) : pi.ids[p];
+  const bool ok = id >= 0 && id < a.n_pool_pages;
+  const int64_t tok = (int64_t)a.qs.Hkv * D;
+  const int64_t off = ok ? ((int64_t)id * PL + (s0 - p * PL)) * tok : 0;
+  Seg sg;
+  sg.k = (const uint16_t*)a.prefix.k + off;
+  sg.v = (const uint16_t*)a.prefix.v + off;
+  sg.ks_t = tok;
+  sg.vs_t = tok;
+  sg.ks_h = D;
+  sg.vs_h = D;
+  sg.pos0 = pos_base + s0;
+  sg.n = ok ? s1 - s0 : 0;
+  sg.pad_ = 0;
+  return sg;
 }
 
 template <int D>
@@ -333,11 +391,20 @@ __global__ __launch_bounds__(kThreads, 2) void fanout_kernel(FanoutArgs a) {
     const int f0 = (x / Hkv) * kTileRows;
     const int f1 = min(f0 + kTileRows, total);
     const int k_off = chunk * a.chunk_len;
+    const int k_end = min(k_off + a.chunk_len, a.prefix.n);
+    if (a.prefix_pages) {
+      const PageIds pi = load_page_ids(a.prefix_pages, k_off, k_end, a.page_len);
+      partial_job_segs<D>(
+          a.qs, f0, f1, g, paged_segments(k_off, k_end, a.page_len),
+          [&](int i) { return paged_seg<D>(a, pi, k_off, k_end, i, 0); }, a.ws_m, a.ws_l, a.ws_o,
+          (int64_t)chunk * a.R, (lds_char*)lds);
+      return;
+    }
     Seg sg = a.prefix;
     sg.k = (const uint16_t*)sg.k + (int64_t)k_off * sg.ks_t;
     sg.v = (const uint16_t*)sg.v + (int64_t)k_off * sg.vs_t;
     sg.pos0 = k_off;
-    sg.n = min(a.chunk_len, a.prefix.n - k_off);
+    sg.n = k_end - k_off;
     partial_job<D>(a.qs, f0, f1, g, sg, a.ws_m, a.ws_l, a.ws_o, (int64_t)chunk * a.R, (lds_char*)lds);
     return;
   }
@@ -358,6 +425,20 @@ __global__ __launch_bounds__(kThreads, 2) void fanout_kernel(FanoutArgs a) {
   const int64_t tok = (int64_t)Hkv * D;
   for (int b = b0; b < b1; ++b) {
     if (b > b0) __syncthreads();  // every wave is done with the previous branch's LDS tiles
+    // Suffix positions: key j at j, branch b's new token i (query token b*T + i)
+    // at S - T + i.
+    QSide qs = a.qs;
+    qs.causal = 1;
+    qs.q_pos0 = (int64_t)(a.S - a.T) - (int64_t)b * a.T;
+    const int f0 = b * TG + rt * kTileRows;
+    const int f1 = min(f0 + kTileRows, (b + 1) * TG);
+    if (a.suffix_pages) {
+      const PageIds pi = load_page_ids(a.suffix_pages + (int64_t)b * a.suffix_pages_per_branch, 0, a.S, a.page_len);
+      partial_job_segs<D>(
+          qs, f0, f1, g, paged_segments(0, a.S, a.page_len), [&](int i) { return paged_seg<D>(a, pi, 0, a.S, i, 0); },
+          a.ws_m, a.ws_l, a.ws_o, (int64_t)a.suffix_slot * a.R, (lds_char*)lds);
+      continue;
+    }
     Seg sg;
     sg.k = (const uint16_t*)a.sk + (int64_t)b * a.S * tok;
     sg.v = (const uint16_t*)a.sv + (int64_t)b * a.S * tok;
@@ -368,13 +449,6 @@ __global__ __launch_bounds__(kThreads, 2) void fanout_kernel(FanoutArgs a) {
     sg.pos0 = 0;
     sg.n = a.S;
     sg.pad_ = 0;
-    // Suffix positions: key j at j, branch b's new token i (query token b*T + i)
-    // at S - T + i.
-    QSide qs = a.qs;
-    qs.causal = 1;
-    qs.q_pos0 = (int64_t)(a.S - a.T) - (int64_t)b * a.T;
-    const int f0 = b * TG + rt * kTileRows;
-    const int f1 = min(f0 + kTileRows, (b + 1) * TG);
     partial_job<D>(qs, f0, f1, g, sg, a.ws_m, a.ws_l, a.ws_o, (int64_t)a.suffix_slot * a.R, (lds_char*)lds);
   }
 }

@@ -90,6 +90,13 @@ struct FanoutArgs {
   int32_t suffix_slot;
   int32_t srt;       // 128-row tiles of one branch's rows
   int32_t bpj;       // branches per suffix job (srt == 1)
+  // Paged K/V (prefix_pages != nullptr): prefix.k / prefix.v are the pools,
+  // page p of a table starts page_len * Hkv * D elements after the pool base.
+  const int32_t* prefix_pages;
+  const int32_t* suffix_pages;   // n_branches rows of suffix_pages_per_branch ids
+  int32_t page_len;
+  int32_t n_pool_pages;
+  int32_t suffix_pages_per_branch;
   float* ws_m;
   float* ws_l;
   float* ws_o;

@@ -315,3 +315,38 @@ CAUSAL_RING_LAYOUTS = CausalRingWorkload(
     seq_len=32768, n_devices=8, n_q_heads=64, n_kv_heads=8, head_dim=128, seed=6)
 
 ALL = [TINY_EXACT, CAUSAL_PREFILL, RING_SHARE, FANOUT_DECODE, SHARD_MERGE]
+
+
+def paged_layout(g: np.random.Generator, n_branches: int, prefix_len: int, suffix_len: int, page_len: int,
+                 extra_pages: int = 3):
+    """Seeded page tables for a paged fan-out: the prefix's ceil(P / page_len)
+    pages and every branch's ceil(S / page_len) private pages at distinct pool
+    pages in random order, plus ``extra_pages`` pages nothing refers to.
+    Returns (n_pool, prefix_pages int32 [n_p], suffix_pages int32 [nb, n_s])."""
+    n_p = -(-prefix_len // page_len)
+    n_s = -(-suffix_len // page_len)
+    n_pool = n_p + n_branches * n_s + extra_pages
+    perm = g.permutation(n_pool).astype(np.int32)
+    prefix_pages = perm[:n_p].copy()
+    suffix_pages = perm[n_p:n_p + n_branches * n_s].reshape(n_branches, n_s).copy()
+    return n_pool, prefix_pages, suffix_pages
+
+
+def scatter_pages(g: np.random.Generator, prefix: synth.Tensor, suffix: synth.Tensor, n_pool: int,
+                  prefix_pages: np.ndarray, suffix_pages: np.ndarray, page_len: int, scale: float = 0.5):
+    """A bf16 page pool [n_pool, page_len, Hkv, D] holding ``prefix`` [P, Hkv, D]
+    and each branch's ``suffix`` [nb, S, Hkv, D] at the given pages; every
+    other row (unused pages, the tails of partial pages) is N(0,1)*scale noise
+    that no correct read touches."""
+    tail = prefix.shape[1:] if prefix.shape[0] else suffix.shape[2:]
+    pool = synth.normal(g, (n_pool, page_len) + tuple(tail), scale, "bf16").storage.copy()
+
+    def put(x, pages):
+        for i, pid in enumerate(pages):
+            rows = x[i * page_len:(i + 1) * page_len]
+            pool[pid, :rows.shape[0]] = rows
+
+    put(prefix.storage, prefix_pages)
+    for b in range(suffix.shape[0]):
+        put(suffix.storage[b], suffix_pages[b])
+    return synth.Tensor(pool, "bf16")

@@ -271,6 +271,43 @@ ba_status fanout_prefix_prefill(const ba_fanout_prefill* f, const void* q,
 
 size_t fanout_prefill_workspace_bytes(const ba_fanout_prefill* f);
 
+/* Paged KV for the fan-out ([AHBM] s.3.1, s.5.12; [TEX] fork by page table):
+ * a branch's context is a page table of the shared prefix pages followed by
+ * its private pages, all in one pool, and the shared pages are referenced,
+ * never copied.  Pools k_pool and v_pool are [n_pool_pages, page_len,
+ * n_kv_heads, head_dim] bf16, contiguous, 16-byte aligned.  Prefix token t is
+ * row t % page_len of pool page prefix_pages[t / page_len]; suffix token j of
+ * branch b is row j % page_len of page
+ * suffix_pages[b * ceil(suffix_len / page_len) + j / page_len].  Both tables
+ * are DEVICE int32 arrays of at least ceil(prefix_len / page_len) and
+ * n_branches * ceil(suffix_len / page_len) entries; the caller owns them and
+ * must not change them until the call has run on its stream.  page_len is a
+ * positive multiple of 64, so no 64-key tile straddles two pages.  A page id
+ * outside [0, n_pool_pages) contributes no keys (its tokens are left out;
+ * positions of the other tokens do not move). */
+typedef struct {
+  const int32_t* prefix_pages;
+  const int32_t* suffix_pages;
+  int32_t page_len;
+  int32_t n_pool_pages;
+} ba_kv_pages;
+
+/* fanout_prefix_decode and fanout_prefix_prefill over paged K/V: the same
+ * attention, positions, outputs and workspace sizes (fanout_workspace_bytes,
+ * fanout_prefill_workspace_bytes).  With every id valid the results equal the
+ * contiguous entry points' bit for bit.  Errors: as the contiguous entry
+ * points, plus BA_ERR_NULL (pages, a needed page table, a pool) and
+ * BA_ERR_SHAPE (page_len not a positive multiple of 64, n_pool_pages < 1,
+ * misaligned pool). */
+ba_status fanout_prefix_decode_paged(const ba_fanout* f, const ba_kv_pages* pages, const void* q,
+                                     const void* k_pool, const void* v_pool, void* out, float* lse,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+ba_status fanout_prefix_prefill_paged(const ba_fanout_prefill* f, const ba_kv_pages* pages,
+                                      const void* q, const void* k_pool, const void* v_pool,
+                                      void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
+
 /* Static description of a status code; never NULL. */
 const char* blockattn_status_str(int32_t status);
 

@@ -265,3 +265,31 @@ def test_bf16_blocks_beyond_32bit_offsets_are_rejected(lib):
     assert _bwd(lib, blocks=big, n_blocks=1, order=None, n_visit=1, dk=(FAKE,), dv=(FAKE,)) == 2
     f = ba.Fanout(4, 64, 8, 128, (1 << 21) + 1, 16, 0.0)
     assert lib.fanout_prefix_decode(ctypes.byref(f), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 2
+
+
+def test_fanout_paged_validation(lib):
+    f = ba.Fanout(4, 64, 8, 128, 1000, 100, 0.0)
+    fp = ba.FanoutPrefill(4, 20, 64, 8, 128, 1000, 100, 0.0)
+
+    def call(pages=True, prefix_pages=FAKE, suffix_pages=FAKE, page_len=256, n_pool=64, k=FAKE, v=FAKE,
+             prefill=False, desc=None):
+        pg = ba.KVPages(prefix_pages, suffix_pages, page_len, n_pool)
+        pp = ctypes.byref(pg) if pages else None
+        if prefill:
+            return lib.fanout_prefix_prefill_paged(ctypes.byref(desc or fp), pp, FAKE, k, v, FAKE, None, None, 0,
+                                                   None)
+        return lib.fanout_prefix_decode_paged(ctypes.byref(desc or f), pp, FAKE, k, v, FAKE, None, None, 0, None)
+
+    for prefill in (False, True):
+        assert call(pages=False, prefill=prefill) == 1
+        assert call(page_len=100, prefill=prefill) == 2
+        assert call(page_len=0, prefill=prefill) == 2
+        assert call(n_pool=0, prefill=prefill) == 2
+        assert call(prefix_pages=None, prefill=prefill) == 1
+        assert call(suffix_pages=None, prefill=prefill) == 1
+        assert call(k=None, prefill=prefill) == 1
+        assert call(v=FAKE + 8, prefill=prefill) == 2
+        assert call(prefill=prefill) == 5                   # valid; no workspace given
+    # a prefix of 4M tokens is fine when paged (each page is its own 32-bit range)
+    assert call(desc=ba.Fanout(4, 64, 8, 128, 1 << 22, 100, 0.0)) == 5
+    assert call(desc=ba.Fanout(4, 64, 8, 128, 1000, 0, 0.0), suffix_pages=None) == 5

@@ -112,6 +112,35 @@ def test_fanout_decode_full_size_all_rows():
     print(f"    all {w.rows} rows: max/mean abs err {stats[0]:.2e}/{stats[1]:.2e}", flush=True)
 
 
+def test_fanout_decode_paged_full_size():
+    """The 64K fan-out decode with its prefix and private suffixes scattered
+    over a page pool (256-token pages, seeded random order): bit for bit the
+    contiguous entry point's result (checked on every row above), and two
+    branches against the paged definition directly."""
+    w = wl.FANOUT_DECODE
+    PL = 256
+    announce(f"{w.name}, paged: page_len {PL}, pages in random pool order (seed {w.seed + 500})")
+    q, pk, pv, sk, sv = w.make_inputs()
+    g = np.random.Generator(np.random.PCG64(w.seed + 500))
+    n_pool, pp, sp = wl.paged_layout(g, w.n_branches, w.prefix_len, w.suffix_len, PL)
+    k_pool = wl.scatter_pages(g, pk, sk, n_pool, pp, sp, PL)
+    v_pool = wl.scatter_pages(g, pv, sv, n_pool, pp, sp, PL)
+    qd = H.to_device(q)
+    out, lse = ba.fanout_prefix_decode_paged(qd, H.to_device(k_pool), H.to_device(v_pool),
+                                             torch.from_numpy(pp).cuda(), torch.from_numpy(sp).cuda(),
+                                             w.prefix_len, w.suffix_len)
+    o2, l2 = ba.fanout_prefix_decode(qd, *[H.to_device(t) for t in (pk, pv, sk, sv)])
+    torch.cuda.synchronize()
+    assert torch.equal(out, o2) and torch.equal(lse, l2), "paged differs from contiguous"
+    b = [0, w.n_branches - 1]
+    a_ref, lse_ref = ora.fanout_paged(q.f64()[b][:, None], k_pool.f64(), v_pool.f64(), pp, sp[b], PL,
+                                      w.prefix_len, w.suffix_len, w.scale)
+    stats = H.assert_bf16_out(H.host(out)[b], a_ref[:, 0], "paged fanout")
+    H.assert_close(H.host(lse)[b], lse_ref[:, 0], H.BF16_LSE, "paged fanout lse")
+    print(f"    branches {b}: max/mean abs err {stats[0]:.2e}/{stats[1]:.2e}; all rows equal the contiguous call",
+          flush=True)
+
+
 def test_shard_merge_full_size_all_rows():
     w = wl.SHARD_MERGE
     announce(w.name)

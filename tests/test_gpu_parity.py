@@ -352,6 +352,71 @@ def test_fanout_prefill(nb, T, Hq, Hkv, D, P, S):
     H.assert_close(H.host(lse), lse_ref, H.BF16_LSE, "fanout prefill lse")
 
 
+# ---------------------------------------------------------------- paged fan-out
+
+# (seed, nb, T, Hq, Hkv, D, P, S, page_len, out_of_pool): T = 1 goes through the
+# decode entry point, T > 1 through the prefill one.  Pages sit at random pool
+# pages among noise pages; the last prefix page and suffix pages are partial.
+# out_of_pool lists (table, index) entries set to an id outside the pool.
+PAGED_CASES = [
+    (61, 3, 1, 8, 2, 128, 1000, 37, 64, []),
+    (62, 2, 20, 64, 8, 128, 700, 90, 128, []),
+    (63, 4, 7, 8, 2, 64, 300, 70, 256, [("prefix", 1), ("suffix", (2, 0))]),
+    (64, 16, 1, 64, 8, 128, 4096, 512, 256, []),
+    (65, 5, 3, 8, 2, 128, 0, 200, 64, []),
+]
+
+
+def paged_inputs(seed, nb, T, Hq, Hkv, D, P, S, PL):
+    g = synth.rng(seed)
+    q = synth.normal(g, (nb, T, Hq, D), 0.5, "bf16")
+    pk = synth.normal(g, (P, Hkv, D), 0.5, "bf16")
+    pv = synth.normal(g, (P, Hkv, D), 0.5, "bf16")
+    sk = synth.normal(g, (nb, S, Hkv, D), 0.5, "bf16")
+    sv = synth.normal(g, (nb, S, Hkv, D), 0.5, "bf16")
+    n_pool, pp, sp = wl.paged_layout(g, nb, P, S, PL)
+    k_pool = wl.scatter_pages(g, pk, sk, n_pool, pp, sp, PL)
+    v_pool = wl.scatter_pages(g, pv, sv, n_pool, pp, sp, PL)
+    return q, pk, pv, sk, sv, n_pool, pp, sp, k_pool, v_pool
+
+
+@pytest.mark.parametrize("case", PAGED_CASES, ids=lambda c: f"seed{c[0]}")
+def test_fanout_paged(case):
+    seed, nb, T, Hq, Hkv, D, P, S, PL, bad = case
+    announce(f"paged fanout nb={nb} T={T} Hq={Hq} Hkv={Hkv} D={D} P={P} S={S} page_len={PL} out_of_pool={bad} "
+             f"seed {seed}")
+    q, pk, pv, sk, sv, n_pool, pp, sp, k_pool, v_pool = paged_inputs(seed, nb, T, Hq, Hkv, D, P, S, PL)
+    for table, i in bad:
+        if table == "prefix":
+            pp[i] = n_pool + 7
+        else:
+            sp[i] = -3
+    kd, vd = H.to_device(k_pool), H.to_device(v_pool)
+    ppd = torch.from_numpy(pp).cuda() if P else None
+    spd = torch.from_numpy(sp).cuda() if S else None
+    if T == 1:
+        qd = H.to_device(q)[:, 0].contiguous()
+        out, lse = ba.fanout_prefix_decode_paged(qd, kd, vd, ppd, spd, P, S)
+        out, lse = out[:, None], lse[:, None]
+    else:
+        qd = H.to_device(q)
+        out, lse = ba.fanout_prefix_prefill_paged(qd, kd, vd, ppd, spd, P, S)
+    torch.cuda.synchronize()
+    a_ref, lse_ref = ora.fanout_paged(q.f64(), k_pool.f64(), v_pool.f64(), pp, sp, PL, P, S, 1.0 / np.sqrt(D))
+    H.assert_bf16_out(H.host(out), a_ref, "paged fanout")
+    H.assert_close(H.host(lse), lse_ref, H.BF16_LSE, "paged fanout lse")
+    if not bad:
+        # the same tiles in the same order as the contiguous entry points: bit for bit
+        dev = [H.to_device(t) if t.storage.size else None for t in (pk, pv, sk, sv)]
+        if T == 1:
+            o2, l2 = ba.fanout_prefix_decode(qd, *dev)
+            o2, l2 = o2[:, None], l2[:, None]
+        else:
+            o2, l2 = ba.fanout_prefix_prefill(qd, *dev)
+        torch.cuda.synchronize()
+        assert torch.equal(out, o2) and torch.equal(lse, l2), "paged differs from contiguous"
+
+
 def test_fanout_prefill_one_token_is_the_decode():
     nb, Hq, Hkv, D, P, S = 5, 8, 2, 128, 900, 33
     announce(f"fanout prefill T=1 vs decode nb={nb} P={P} S={S} seed 74")
