@@ -108,3 +108,26 @@ def test_fanout_bindings_check_shapes():
         ba.fanout_prefix_prefill(qp, pk, pv, sk, sv, out=bf16(4, 16, 128))
     with pytest.raises(ValueError, match="suffix_k"):
         ba.fanout_prefix_prefill(qp, pk, pv, bf16(4, 10, 1, 128), sv)
+
+
+def test_paged_fanout_bindings_check_pools_and_tables():
+    q = bf16(4, 16, 128)
+    pool = bf16(20, 64, 2, 128)
+    pp = torch.zeros(16, dtype=torch.int32)          # 1000 prefix tokens / 64 = 16 pages
+    sp = torch.zeros(4, 2, dtype=torch.int32)        # 100 suffix tokens / 64 = 2 pages per branch
+    with pytest.raises(ValueError, match="same shape"):
+        ba.fanout_prefix_decode_paged(q, pool, bf16(20, 64, 2, 64), pp, sp, 1000, 100)
+    with pytest.raises(ValueError, match="prefix_pages"):
+        ba.fanout_prefix_decode_paged(q, pool, pool, pp[:15], sp, 1000, 100)
+    with pytest.raises(ValueError, match="prefix_pages"):
+        ba.fanout_prefix_decode_paged(q, pool, pool, pp.to(torch.int64), sp, 1000, 100)
+    with pytest.raises(ValueError, match="suffix_pages"):
+        ba.fanout_prefix_decode_paged(q, pool, pool, pp, sp[:, :1], 1000, 100)
+    with pytest.raises(ValueError, match="suffix_pages"):
+        ba.fanout_prefix_decode_paged(q, pool, pool, pp, None, 1000, 100)
+    with pytest.raises(ValueError, match="head_dim"):
+        ba.fanout_prefix_decode_paged(bf16(4, 16, 64), pool, pool, pp, sp, 1000, 100)
+    with pytest.raises(ValueError, match="out must be"):
+        ba.fanout_prefix_decode_paged(q, pool, pool, pp, sp, 1000, 100, out=bf16(4, 16, 64))
+    with pytest.raises(ValueError, match="lse must be"):
+        ba.fanout_prefix_prefill_paged(bf16(4, 3, 16, 128), pool, pool, pp, sp, 1000, 100, lse=f32(4, 16))
