@@ -105,11 +105,15 @@ __device__ inline void tile_compute(const lds_char* stage, int lane, const bf16x
     acc.mt[qb] = fmaxf(acc.mt[qb], mx);
     const float m_old = acc.m2[qb];
     // Move the reference only when the tile max is more than kTau above it
-    // (always the case while the row has seen no key: m_old = -inf).
+    // (always the case when a row sees its first key: m_old = -inf, mx finite).
+    // A row that does not move keeps alpha = 1 exactly -- also a row that has
+    // seen no key yet and sees none in this tile either (m_old = mx = -inf,
+    // where exp2(m_old - m_old) would be NaN) while another row of the wave
+    // moves.
     const bool move = mx > m_old + kTau;
     if (__ballot(move) != 0) {
       const float m_new = move ? mx : m_old;
-      const float alpha = __builtin_amdgcn_exp2f(m_old - m_new);  // 0 when m_old = -inf; 1 if unchanged
+      const float alpha = move ? __builtin_amdgcn_exp2f(m_old - m_new) : 1.f;  // 0 when m_old = -inf
       acc.m2[qb] = m_new;
       acc.lp[qb] *= alpha;
 #pragma unroll

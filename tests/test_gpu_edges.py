@@ -1,0 +1,136 @@
+"""GPU parity at the edges of the C ABI, against the CPU fp64 oracle: the
+largest visit count one call accepts, empty and one-key blocks, MHA decode
+(G = 1) and wide groups (G = 16), strided views out of fused QKV buffers, an
+explicit logit scale, and every split mode.  Every case prints its name,
+shape and seed before it touches the GPU."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from exact_blockwise_long_amd import blockattn as ba
+from exact_blockwise_long_amd import synth
+from oracle import attention as ora
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+MAX_VISITS = 32   # BLOCKATTN_MAX_VISITS
+
+
+def announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ba.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def run_and_check(q, k, v, lens, order, *, Hkv, q_pos0, causal, split_mode, scale=0.0, qd=None, kd=None, vd=None,
+                  what=""):
+    """fwd_block over blocks cut from k, v in the given lengths (positions in
+    block order), then finalize; compared with the oracle's attention."""
+    T, Hq, D = q.shape
+    qd = H.to_device(q) if qd is None else qd
+    kd = H.to_device(k) if kd is None else kd
+    vd = H.to_device(v) if vd is None else vd
+    blocks, off = [], 0
+    for n in lens:
+        blocks.append((kd[off:off + n], vd[off:off + n], off))
+        off += n
+    st = ba.new_state(T * Hq, D)
+    ba.fwd_block(qd, blocks, order, st, reset=True, n_kv_heads=Hkv, q_pos0=q_pos0, causal=causal,
+                 split_mode=split_mode, scale=scale)
+    out, lse = ba.finalize(st)
+    torch.cuda.synchronize()
+    s = scale if scale > 0 else 1.0 / np.sqrt(D)
+    a_ref, _, _, lse_ref = ora.attend(q.f64(), k.f64(), v.f64(), s, q_pos0 + np.arange(T), None, causal)
+    stats = H.assert_bf16_out(H.host(out).reshape(T, Hq, D), a_ref, what)
+    H.assert_close(H.host(lse).reshape(T, Hq), lse_ref, H.BF16_LSE, what + " lse")
+    print(f"    {what}: max/mean abs err {stats[0]:.2e}/{stats[1]:.2e}", flush=True)
+    return out, lse
+
+
+@pytest.mark.parametrize("split_mode", [0, 1, 2])
+def test_max_visits_in_one_call(split_mode):
+    """32 blocks in one call, in a shuffled order: empty, one-key, ragged and
+    multi-tile blocks; causal with the queries in the middle of the keys, so
+    later blocks are partly or wholly in the future."""
+    seed, T, Hq, Hkv, D = 81, 40, 8, 2, 128
+    lens = [[1, 0, 63, 64, 65, 7, 128, 200][i % 8] for i in range(MAX_VISITS)]
+    order = synth.rng(seed + 1).permutation(MAX_VISITS).tolist()
+    L = sum(lens)
+    q_pos0 = L // 2
+    announce(f"max visits: {MAX_VISITS} blocks, {L} keys, T={T} q_pos0={q_pos0} split_mode={split_mode} seed {seed}")
+    g = synth.rng(seed)
+    q = synth.normal(g, (T, Hq, D), 0.5, "bf16")
+    k = synth.normal(g, (L, Hkv, D), 0.5, "bf16")
+    v = synth.normal(g, (L, Hkv, D), 0.5, "bf16")
+    run_and_check(q, k, v, lens, order, Hkv=Hkv, q_pos0=q_pos0, causal=True, split_mode=split_mode,
+                  what=f"{MAX_VISITS} visits mode {split_mode}")
+
+
+@pytest.mark.parametrize("Hq,Hkv,T,causal", [(8, 8, 1, False), (8, 8, 1, True), (16, 1, 33, True),
+                                             (16, 1, 33, False)])
+def test_group_sizes_and_decode(Hq, Hkv, T, causal):
+    """MHA (G = 1) with a single query token, and a 16-wide group."""
+    seed, D, lens = 82, 128, [300, 1, 129]
+    announce(f"groups: Hq={Hq} Hkv={Hkv} T={T} causal={causal} lens={lens} seed {seed}")
+    g = synth.rng(seed)
+    L = sum(lens)
+    q = synth.normal(g, (T, Hq, D), 0.5, "bf16")
+    k = synth.normal(g, (L, Hkv, D), 0.5, "bf16")
+    v = synth.normal(g, (L, Hkv, D), 0.5, "bf16")
+    for mode in (0, 1, 2):
+        run_and_check(q, k, v, lens, [2, 0, 1], Hkv=Hkv, q_pos0=L - T, causal=causal, split_mode=mode,
+                      what=f"G={Hq // Hkv} T={T} mode {mode}")
+
+
+def test_strided_views_and_explicit_scale():
+    """Q, K and V as views into fused buffers ([T, 3, Hq, D] and [L, 2, Hkv, D]:
+    token strides of 3*Hq*D and 2*Hkv*D elements), with an explicit logit
+    scale; the backward with dO a view of the same strides."""
+    seed, T, Hq, Hkv, D, lens, scale = 83, 70, 8, 2, 64, [100, 37], 0.07
+    announce(f"strided views: q from [T,3,Hq,D], k/v from [L,2,Hkv,D], D={D} scale={scale} seed {seed}")
+    g = synth.rng(seed)
+    L = sum(lens)
+    qkv = synth.normal(g, (T, 3, Hq, D), 0.5, "bf16")
+    kv = synth.normal(g, (L, 2, Hkv, D), 0.5, "bf16")
+    q = synth.Tensor(np.ascontiguousarray(qkv.storage[:, 0]), "bf16")
+    k = synth.Tensor(np.ascontiguousarray(kv.storage[:, 0]), "bf16")
+    v = synth.Tensor(np.ascontiguousarray(kv.storage[:, 1]), "bf16")
+    qkvd, kvd = H.to_device(qkv), H.to_device(kv)
+    qd, kd, vd = qkvd[:, 0], kvd[:, 0], kvd[:, 1]
+    assert qd.stride(0) == 3 * Hq * D and kd.stride(0) == 2 * Hkv * D
+    for causal in (False, True):
+        for mode in (1, 2):
+            run_and_check(q, k, v, lens, [1, 0], Hkv=Hkv, q_pos0=L - T, causal=causal, split_mode=mode, scale=scale,
+                          qd=qd, kd=kd, vd=vd, what=f"strided causal={causal} mode {mode}")
+    # backward through the same views: dO is the third slot of the fused buffer
+    dod = qkvd[:, 2]
+    do = synth.Tensor(np.ascontiguousarray(qkv.storage[:, 2]), "bf16")
+    blocks = [(kd[:lens[0]], vd[:lens[0]], 0), (kd[lens[0]:], vd[lens[0]:], lens[0])]
+    st = ba.new_state(T * Hq, D)
+    ba.fwd_block(qd, blocks, [1, 0], st, reset=True, n_kv_heads=Hkv, q_pos0=L - T, causal=True, scale=scale)
+    out, lse = ba.finalize(st)
+    delta = ba.bwd_delta(out, dod.reshape(T * Hq, D) if dod.is_contiguous() else dod.contiguous().reshape(T * Hq, D))
+    dq = torch.zeros(T * Hq, D, dtype=torch.float32, device="cuda")
+    dkv = [(torch.zeros(n, Hkv, D, dtype=torch.float32, device="cuda"),
+            torch.zeros(n, Hkv, D, dtype=torch.float32, device="cuda")) for n in lens]
+    ba.bwd_block(qd, dod, lse, delta, blocks, [1, 0], dq, dkv, n_kv_heads=Hkv, q_pos0=L - T, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    rq, rk, rv = ora.attention_grads(q.f64(), k.f64(), v.f64(), do.f64(), scale, L - T + np.arange(T), None, True)
+    for got, ref, name in ((H.host(dq).reshape(T, Hq, D), rq, "dQ"),
+                           (np.concatenate([H.host(a) for a, _ in dkv]), rk, "dK"),
+                           (np.concatenate([H.host(b) for _, b in dkv]), rv, "dV")):
+        err = np.abs(got - ref)
+        mx, mn = err.max() / np.abs(ref).max(), err.mean() / np.abs(ref).mean()
+        print(f"    strided backward {name}: {mx:.2e} / {mn:.2e}", flush=True)
+        assert mx <= 2e-2 and mn <= 5e-3, f"strided backward {name}"

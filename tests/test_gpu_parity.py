@@ -209,6 +209,21 @@ def test_bf16_causal_future_keys_ignored():
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("split_mode", [1, 2])
+@pytest.mark.parametrize("D", [64, 128])
+def test_bf16_row_without_keys_in_first_tile(split_mode, D):
+    """The first visited block is wholly in the future for the first rows of a
+    row tile and visible to the tile's later rows: the first rows' reference
+    max stays -inf through a tile in which other rows of the wave move theirs
+    (regression: their rescale factor was exp2(-inf - -inf) = NaN)."""
+    seed, T, Hq, Hkv, lens, order, q_pos0 = 84, 70, 8, 2, [100, 37], [1, 0], 67
+    announce(f"bf16 first tile masked for some rows: D={D} lens={lens} order={order} q_pos0={q_pos0} "
+             f"split_mode={split_mode} seed {seed}")
+    q, k, v = make_case(seed, T, Hq, Hkv, D, lens)
+    st = run_fwd(q, k, v, lens, order, Hkv=Hkv, q_pos0=q_pos0, causal=True, split_mode=split_mode)
+    check_state_vs_oracle(st, q, k, v, q_pos0, True, what=f"first tile masked D{D} mode{split_mode}")
+
+
 def test_empty_and_degenerate():
     announce("degenerate: q_len 0, no visits with reset, all keys in the future")
     q, k, v = make_case(41, 40, 8, 2, 128, [64])
