@@ -162,3 +162,23 @@ def test_random_fanout(seed):
         o2, l2 = ba.fanout_prefix_prefill_paged(qd, kd, vd, ppd, spd, P, S)
     torch.cuda.synchronize()
     assert torch.equal(out, o2) and torch.equal(lse, l2), f"paged (page_len {PL}) differs from contiguous"
+
+
+@pytest.mark.parametrize("seed", range(4000, 4016))
+def test_random_shards_then_merge(seed):
+    """One partial state per block (shard_states), the n-way merge, finalize:
+    equal to attention over all the blocks' keys."""
+    c = draw(seed)
+    announce(f"random shards seed {seed}: {c}")
+    T, Hq, Hkv, D, lens = c["T"], c["Hq"], c["Hkv"], c["D"], c["lens"]
+    q, k, v = make_case(seed, T, Hq, Hkv, D, lens)
+    qd, kd, vd = H.to_device(q), H.to_device(k), H.to_device(v)
+    blocks, off = [], 0
+    for n in lens:
+        blocks.append((kd[off:off + n], vd[off:off + n], off))
+        off += n
+    states = [ba.new_state(T * Hq, D) for _ in lens]
+    ba.shard_states(qd, blocks, states, n_kv_heads=Hkv, q_pos0=c["q_pos0"], causal=c["causal"])
+    merged = ba.new_state(T * Hq, D)
+    ba.merge_states(states, merged)
+    check_state_vs_oracle(merged, q, k, v, c["q_pos0"], c["causal"], what=f"random shards seed {seed}")
