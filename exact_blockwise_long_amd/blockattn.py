@@ -82,7 +82,7 @@ EXPORTS = [
     "blockattn_fwd_block", "blockattn_fwd_workspace_bytes", "blockattn_shard_states",
     "blockattn_shard_workspace_bytes", "blockattn_merge_states", "blockattn_finalize",
     "fanout_prefix_decode", "fanout_workspace_bytes", "fanout_prefix_prefill",
-    "fanout_prefill_workspace_bytes", "fanout_prefix_decode_paged", "fanout_prefix_prefill_paged", "blockattn_bwd_delta", "blockattn_bwd_block", "blockattn_status_str",
+    "fanout_prefill_workspace_bytes", "fanout_prefix_decode_paged", "fanout_prefix_prefill_paged", "blockattn_workspace_bytes", "blockattn_bwd_delta", "blockattn_bwd_block", "blockattn_status_str",
     "blockattn_last_error", "blockattn_abi_version",
 ]
 
@@ -135,6 +135,8 @@ def load():
     lib.fanout_prefix_prefill.restype = i32
     lib.fanout_prefill_workspace_bytes.argtypes = [P(FanoutPrefill)]
     lib.fanout_prefill_workspace_bytes.restype = sz
+    lib.blockattn_workspace_bytes.argtypes = [P(Problem), P(Fanout)]
+    lib.blockattn_workspace_bytes.restype = sz
     lib.fanout_prefix_decode_paged.argtypes = [P(Fanout), P(KVPages), vp, vp, vp, vp, vp, vp, sz, vp]
     lib.fanout_prefix_decode_paged.restype = i32
     lib.fanout_prefix_prefill_paged.argtypes = [P(FanoutPrefill), P(KVPages), vp, vp, vp, vp, vp, vp, sz, vp]

@@ -794,6 +794,20 @@ ba_status prefill_shape(const ba_fanout_prefill* f, FanoutShape* s) {
 
 extern "C" {
 
+size_t blockattn_workspace_bytes(const ba_problem* p, const ba_fanout* f) {
+  size_t need = 0;
+  if (p && check_problem(p, (const void*)256) == BA_OK && p->q_len > 0 && fwd_uses_split(p)) {
+    // The split planner's chunks of a call: sum over visited blocks of
+    // ceil(keys / chunk_len) <= total / chunk_len + n_visit, with chunk_len >=
+    // total / want, so at most want + BLOCKATTN_MAX_VISITS slots.
+    const int tiles = row_tiles(p);
+    const int64_t want = std::max<int64_t>(1, (kTargetWorkgroups + tiles - 1) / (tiles > 0 ? tiles : 1));
+    need = partial_bytes(want + BLOCKATTN_MAX_VISITS, (int64_t)p->q_len * p->n_q_heads, p->head_dim);
+  }
+  if (f && check_fanout(f) == BA_OK && f->n_branches > 0) need = std::max(need, fanout_bytes(decode_shape(f)));
+  return need;
+}
+
 size_t fanout_workspace_bytes(const ba_fanout* f) {
   if (check_fanout(f) != BA_OK || f->n_branches == 0) return 0;
   return fanout_bytes(decode_shape(f));

@@ -293,3 +293,32 @@ def test_fanout_paged_validation(lib):
     # a prefix of 4M tokens is fine when paged (each page is its own 32-bit range)
     assert call(desc=ba.Fanout(4, 64, 8, 128, 1 << 22, 100, 0.0)) == 5
     assert call(desc=ba.Fanout(4, 64, 8, 128, 1000, 0, 0.0), suffix_pages=None) == 5
+
+
+def test_workspace_bound_covers_every_call(lib):
+    """blockattn_workspace_bytes(p, NULL) bounds blockattn_fwd_workspace_bytes
+    over random block sets and visit orders of the problem; (NULL, f) is the
+    fan-out decode's requirement.  Host-side sizing only."""
+    import numpy as np
+    g = np.random.Generator(np.random.PCG64(5))
+    for trial in range(200):
+        Hkv = int(g.choice([1, 2, 8]))
+        Hq = Hkv * int(g.choice([1, 4, 8]))
+        T = int(g.choice([1, 7, 64, 300, 2000]))
+        mode = int(g.choice([0, 2]))
+        p = _problem(n_q_heads=Hq, n_kv_heads=Hkv, q_len=T, q_stride_token=Hq * 128, split_mode=mode,
+                     causal=int(g.integers(0, 2)), q_pos0=int(g.integers(0, 5000)))
+        n = int(g.integers(1, 33))
+        blocks = (ba.KVBlock * n)()
+        pos = 0
+        for i in range(n):
+            ln = int(g.integers(0, 40000))
+            blocks[i] = ba.KVBlock(FAKE, FAKE, ln, pos, Hkv * 128, 128, Hkv * 128, 128)
+            pos += ln
+        bound = lib.blockattn_workspace_bytes(ctypes.byref(p), None)
+        order = (ctypes.c_int32 * n)(*g.permutation(n).tolist())
+        exact = lib.blockattn_fwd_workspace_bytes(ctypes.byref(p), blocks, n, order, n)
+        assert exact <= bound, (trial, exact, bound)
+    f = ba.Fanout(16, 64, 8, 128, 65536, 512, 0.0)
+    assert lib.blockattn_workspace_bytes(None, ctypes.byref(f)) == lib.fanout_workspace_bytes(ctypes.byref(f))
+    assert lib.blockattn_workspace_bytes(None, None) == 0
