@@ -280,7 +280,7 @@ __device__ inline Seg chunk_seg(const Seg* seg, int n_seg, const int32_t* chunk_
 
 // Partial state of one row tile over the keys of n_seg segments (get_seg(i)
 // returns segment i), written to a workspace slot.
-template <int D, class GetSeg>
+template <int D, int kAux, class GetSeg>
 __device__ inline void partial_job_segs(const QSide& qs, int f0, int f1, int g, int n_seg, GetSeg get_seg,
                                         float* ws_m, float* ws_l, float* ws_o, int64_t row_base, lds_char* lds) {
   const RowCtx rc = make_rowctx(qs, f0, f1, g);
@@ -292,7 +292,7 @@ __device__ inline void partial_job_segs(const QSide& qs, int f0, int f1, int g, 
   load_q<D>(lr, lane, qf);
   Acc<D> acc;
   init_acc<D>(acc);
-  run_segments<D>(
+  run_segments<D, kAux>(
       qs, rc, n_seg, get_seg,
       [&](const lds_char* stage, bool need_mask, int n_valid, int krel) {
         tile_compute<D>(stage, lane, qf, acc, qs.c, need_mask, qs.causal != 0, n_valid, krel, lr.qrel);
@@ -301,10 +301,10 @@ __device__ inline void partial_job_segs(const QSide& qs, int f0, int f1, int g, 
   store_acc<D>(acc, lane_rows(qs, rc, wave, lane), lane, ws_m, ws_l, ws_o, row_base);
 }
 
-template <int D>
+template <int D, int kAux>
 __device__ inline void partial_job(const QSide& qs, int f0, int f1, int g, const Seg& sg, float* ws_m,
                                    float* ws_l, float* ws_o, int64_t row_base, lds_char* lds) {
-  partial_job_segs<D>(qs, f0, f1, g, 1, [&](int) -> const Seg& { return sg; }, ws_m, ws_l, ws_o, row_base, lds);
+  partial_job_segs<D, kAux>(qs, f0, f1, g, 1, [&](int) -> const Seg& { return sg; }, ws_m, ws_l, ws_o, row_base, lds);
 }
 
 // The page ids of one job's key range [k0, k1) of a paged sequence whose
@@ -358,7 +358,7 @@ __device__ inline Seg paged_seg(const FanoutArgs& a, const PageIds& pi, int k0, 
   return sg;
 }
 
-template <int D>
+template <int D, int kAux>
 __global__ __launch_bounds__(kThreads, 2) void split_kernel(SplitArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[2 * Cfg<D>::STAGEB];
   const int Hkv = a.qs.Hkv;
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_kernel(SplitArgs a) {
   const int f0 = tile * kTileRows;
   const int f1 = min(f0 + kTileRows, total);
   const Seg cs = chunk_seg(a.seg, a.n_seg, a.chunk_begin, a.chunk_len, chunk);
-  partial_job<D>(a.qs, f0, f1, g, cs, a.ws_m, a.ws_l, a.ws_o, (int64_t)chunk * a.R, (lds_char*)lds);
+  partial_job<D, kAux>(a.qs, f0, f1, g, cs, a.ws_m, a.ws_l, a.ws_o, (int64_t)chunk * a.R, (lds_char*)lds);
 }
 
 // Shared-prefix fan-out (decode, or prefill of the private suffixes), one
@@ -379,7 +379,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_kernel(SplitArgs a) {
 // of the shared prefix, written to slot `chunk`; the remaining jobs are
 // (branch group or branch row tile, KV head) -- each branch's rows against its
 // private suffix under the causal rule, written to slot `suffix_slot`.
-template <int D>
+template <int D, int kAux>
 __global__ __launch_bounds__(kThreads, 2) void fanout_kernel(FanoutArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[2 * Cfg<D>::STAGEB];
   const int Hkv = a.qs.Hkv;
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(kThreads, 2) void fanout_kernel(FanoutArgs a) {
     const int k_end = min(k_off + a.chunk_len, a.prefix.n);
     if (a.prefix_pages) {
       const PageIds pi = load_page_ids(a.prefix_pages, k_off, k_end, a.page_len);
-      partial_job_segs<D>(
+      partial_job_segs<D, kAux>(
           a.qs, f0, f1, g, paged_segments(k_off, k_end, a.page_len),
           [&](int i) { return paged_seg<D>(a, pi, k_off, k_end, i, 0); }, a.ws_m, a.ws_l, a.ws_o,
           (int64_t)chunk * a.R, (lds_char*)lds);
@@ -409,7 +409,7 @@ __global__ __launch_bounds__(kThreads, 2) void fanout_kernel(FanoutArgs a) {
     sg.v = (const uint16_t*)sg.v + (int64_t)k_off * sg.vs_t;
     sg.pos0 = k_off;
     sg.n = k_end - k_off;
-    partial_job<D>(a.qs, f0, f1, g, sg, a.ws_m, a.ws_l, a.ws_o, (int64_t)chunk * a.R, (lds_char*)lds);
+    partial_job<D, kAux>(a.qs, f0, f1, g, sg, a.ws_m, a.ws_l, a.ws_o, (int64_t)chunk * a.R, (lds_char*)lds);
     return;
   }
   const int j = id - n_prefix_jobs;
@@ -438,7 +438,7 @@ __global__ __launch_bounds__(kThreads, 2) void fanout_kernel(FanoutArgs a) {
     const int f1 = min(f0 + kTileRows, (b + 1) * TG);
     if (a.suffix_pages) {
       const PageIds pi = load_page_ids(a.suffix_pages + (int64_t)b * a.suffix_pages_per_branch, 0, a.S, a.page_len);
-      partial_job_segs<D>(
+      partial_job_segs<D, kAux>(
           qs, f0, f1, g, paged_segments(0, a.S, a.page_len), [&](int i) { return paged_seg<D>(a, pi, 0, a.S, i, 0); },
           a.ws_m, a.ws_l, a.ws_o, (int64_t)a.suffix_slot * a.R, (lds_char*)lds);
       continue;
@@ -453,7 +453,7 @@ __global__ __launch_bounds__(kThreads, 2) void fanout_kernel(FanoutArgs a) {
     sg.pos0 = 0;
     sg.n = a.S;
     sg.pad_ = 0;
-    partial_job<D>(qs, f0, f1, g, sg, a.ws_m, a.ws_l, a.ws_o, (int64_t)a.suffix_slot * a.R, (lds_char*)lds);
+    partial_job<D, kAux>(qs, f0, f1, g, sg, a.ws_m, a.ws_l, a.ws_o, (int64_t)a.suffix_slot * a.R, (lds_char*)lds);
   }
 }
 
@@ -470,21 +470,41 @@ hipError_t launch_walk_bf16(const WalkArgs& a, int D, hipStream_t s) {
 }
 
 hipError_t launch_split_bf16(const SplitArgs& a, int n_chunks, int D, hipStream_t s) {
-  const int tiles = (a.qs.q_len * a.qs.G + kTileRows - 1) / kTileRows;
+  const int per_head = (a.qs.q_len * a.qs.G + kTileRows - 1) / kTileRows;
+  const int tiles = per_head;
   dim3 grid(tiles * a.qs.Hkv, n_chunks);
-  if (D == 128)
-    hipLaunchKernelGGL((split_kernel<128>), grid, dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((split_kernel<64>), grid, dim3(kThreads), 0, s, a);
+  // One row tile per KV head: every K/V byte is read by one workgroup.
+  const bool stream = per_head == 1;
+  if (D == 128) {
+    if (stream)
+      hipLaunchKernelGGL((split_kernel<128, kCacheStream>), grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((split_kernel<128, kCacheReuse>), grid, dim3(kThreads), 0, s, a);
+  } else {
+    if (stream)
+      hipLaunchKernelGGL((split_kernel<64, kCacheStream>), grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((split_kernel<64, kCacheReuse>), grid, dim3(kThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_fanout_bf16(const FanoutArgs& a, int n_jobs, int D, hipStream_t s) {
   dim3 grid(n_jobs);
-  if (D == 128)
-    hipLaunchKernelGGL((fanout_kernel<128>), grid, dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((fanout_kernel<64>), grid, dim3(kThreads), 0, s, a);
+  // All of a KV head's rows in one row tile (the decode): each prefix chunk
+  // and each suffix is read by one workgroup.
+  const bool stream = a.row_tiles == 1 && a.srt == 1;
+  if (D == 128) {
+    if (stream)
+      hipLaunchKernelGGL((fanout_kernel<128, kCacheStream>), grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((fanout_kernel<128, kCacheReuse>), grid, dim3(kThreads), 0, s, a);
+  } else {
+    if (stream)
+      hipLaunchKernelGGL((fanout_kernel<64, kCacheStream>), grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((fanout_kernel<64, kCacheReuse>), grid, dim3(kThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

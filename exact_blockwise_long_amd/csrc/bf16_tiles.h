@@ -89,13 +89,25 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 // Two floats to a packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32).
 __device__ inline bf16x2 pack_bf16x2(float a, float b) { return __builtin_convertvector(f32x2{a, b}, bf16x2); }
 
+// Cache policy of the K/V tile loads.  kCacheReuse is the default: other
+// workgroups read the same tiles (a KV head's keys serve every row tile of its
+// query rows) and find them in L2.  kCacheStream marks the loads non-temporal
+// (nt): for a launch whose K/V bytes are each read by a single workgroup, as
+// in the one-row-tile fan-out decode and shard sweeps, they then do not evict
+// lines that are reused.  Measured: the 64K fan-out decode 77 -> 71 us and the
+// 1M shard sweep 132 -> 126 us with kCacheStream; the prefill walk, whose
+// tiles are re-read, loses 10 % with it.
+constexpr int kCacheReuse = 0;
+constexpr int kCacheStream = 2;
+
 // One 16-byte-per-lane buffer load straight into LDS (buffer_load_dwordx4 ...
 // lds): lane i's bytes land at dst + 16 * i.  The host compilation pass never
 // runs device code but rejects this builtin in some template contexts, so the
 // call is compiled for the device only.
+template <int kAux = kCacheReuse>
 __device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t dst, uint32_t voff, uint32_t soff) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(size_t)dst, 16, voff, soff, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(size_t)dst, 16, voff, soff, 0, kAux);
 #endif
 }
 
@@ -164,7 +176,7 @@ __device__ inline LaneOffs<D> lane_offsets(const KVSrc& src, int wave, int lane)
 // Keys past the end of the range read as zeros (buffer range check); their
 // scores are masked, so their P is exactly 0.
 // `stage` is the LDS byte address of the stage.
-template <int D>
+template <int D, int kAux = kCacheReuse>
 __device__ inline void issue_tile(const KVSrc& src, const LaneOffs<D>& offs, int k0, uint32_t stage, int wave) {
   using C = Cfg<D>;
   const uint32_t soff_k = (uint32_t)k0 * src.kst;
@@ -172,8 +184,8 @@ __device__ inline void issue_tile(const KVSrc& src, const LaneOffs<D>& offs, int
 #pragma unroll
   for (int j = 0; j < C::LPW; ++j) {
     const uint32_t rbase = (uint32_t)((wave * C::LPW + j) * C::RPI);
-    lds_dma16(src.k, stage + rbase * C::ROWB, offs.k[j], soff_k);
-    lds_dma16(src.v, stage + C::TILEB + rbase * C::ROWB, offs.v[j], soff_v);
+    lds_dma16<kAux>(src.k, stage + rbase * C::ROWB, offs.k[j], soff_k);
+    lds_dma16<kAux>(src.v, stage + C::TILEB + rbase * C::ROWB, offs.v[j], soff_v);
   }
 }
 
@@ -227,7 +239,7 @@ __device__ inline void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: 
 // keys at or past n_valid are invalid and, for causal problems, key kk sits
 // at position krel + kk relative to the tile's first query.  It runs only in
 // waves that own rows.
-template <int D, class GetSeg, class TileFn>
+template <int D, int kAux = kCacheReuse, class GetSeg, class TileFn>
 __device__ inline void run_segments(const QSide& qs, const RowCtx& rc, int n_seg, GetSeg get_seg, TileFn tile,
                                     lds_char* lds, bool wave_active) {
   using C = Cfg<D>;
@@ -257,7 +269,7 @@ __device__ inline void run_segments(const QSide& qs, const RowCtx& rc, int n_seg
 
   const uint32_t lds_addr = (uint32_t)(size_t)lds;
   auto issue_next = [&](int stage_off) {
-    issue_tile<D>(isrc, ilo, ik, lds_addr + (uint32_t)stage_off, wave);
+    issue_tile<D, kAux>(isrc, ilo, ik, lds_addr + (uint32_t)stage_off, wave);
     ik += kTileKeys;
     if (ik >= is_n) {
       is = next_nonempty(is + 1, is_n);
