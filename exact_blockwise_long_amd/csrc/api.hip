@@ -36,8 +36,10 @@ ba_status hip_status(hipError_t e, const char* what) {
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Workgroups a split launch aims for: 4 per compute unit of a 256-CU part.
-constexpr int kTargetWorkgroups = 1024;
+// Workgroups a split launch aims for: two per compute unit of a 256-CU part,
+// one round (fastest for the bandwidth-bound shard sweep: 109 us against
+// 126 us at 1024 and 132 us at 256).
+constexpr int kTargetWorkgroups = 512;
 // Below this many (row tile x KV head) workgroups the keys are split.
 constexpr int kWalkMinWorkgroups = 512;
 constexpr int kMaxChunks = 8192;

@@ -310,7 +310,7 @@ ba_status fanout_prefix_prefill_paged(const ba_fanout_prefill* f, const ba_kv_pa
 
 /* Workspace enough for every blockattn_fwd_block call on problem p whatever
  * its blocks and visit order (a bound: the split planner makes at most
- * ceil(1024 / (row tiles x KV heads)) + BLOCKATTN_MAX_VISITS key chunks), and
+ * ceil(512 / (row tiles x KV heads)) + BLOCKATTN_MAX_VISITS key chunks), and
  * for fanout_prefix_decode with descriptor f; either may be NULL.  Lets a
  * caller size one workspace up front (blockattn_shard_states, which always
  * splits, has its own query above).  0 when nothing needs one or an argument
