@@ -10,8 +10,10 @@ is algorithmic TFLOP/s (4 * D * Hq * visible (query, key) pairs per step).
 
 The line also carries the roofline of the dominant kernel (measured live with
 HIP events on the stream it runs on), the CPU oracle timed on a bounded
-sample of the same workload, and secondary measurements of the other
-workloads (ring share, fan-out decode, sharded merge, scaled merge).
+sample of the same workload, secondary measurements of the other
+workloads (ring share, fan-out decode and prefill, sharded merge, scaled
+merge, backward, causal shard layouts), and a library bf16 GEMM timed the same
+way as the board's sustained matrix-core rate under its power limit.
 Prints exactly one JSON line (on stdout); progress goes to stderr.
 """
 
@@ -529,6 +531,32 @@ def copy_calibration(torch, steps):
             "bytes_written_per_copy": n * 4, "copies": steps}
 
 
+def gemm_reference(torch, steps, n=8192):
+    """A library bf16 GEMM (torch.matmul, served by hipBLASLt) of n^3, timed
+    like the headline step: the dense matrix-core rate this board sustains
+    under its power limit, beside which the attention kernels' fraction of
+    the nominal 2.5 PFLOP/s is read.  Not part of any step."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    reps = max(steps, 40)
+    for _ in range(reps):  # bring the clock to its loaded state first
+        torch.matmul(a, b, out=c)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tf = 2.0 * n ** 3 / ms / 1e9
+    log(f"library GEMM {n}^3 bf16: {ms:.3f} ms, {tf:.0f} TFLOP/s")
+    return {"workload": f"torch.matmul bf16 {n}x{n}x{n} (hipBLASLt), back to back", "ms": round(ms, 4),
+            "TFLOP/s": round(tf, 1), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
 def cpu_baseline(w, q, k, v, budget_s):
     """The oracle, as it stands, on a bounded sample of query tokens of the headline workload."""
     from threadpoolctl import threadpool_info
@@ -564,7 +592,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="all",
                     choices=["all", "causal_prefill", "ring_share", "fanout", "shard_merge", "merge_scaled",
-                             "layouts", "fanout_prefill", "fanout_paged", "backward", "copy_calibration"])
+                             "layouts", "fanout_prefill", "fanout_paged", "backward", "copy_calibration",
+                             "gemm_reference"])
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -605,6 +634,8 @@ def main():
         secondary["backward"] = bench_backward(torch, ba, H, wl.CAUSAL_PREFILL, args.steps, args.warmup)
     if only == "copy_calibration":
         secondary["copy_calibration"] = copy_calibration(torch, args.steps)
+    if only == "gemm_reference":
+        secondary["gemm_reference"] = gemm_reference(torch, args.steps)
     if only not in ("all", "causal_prefill"):
         print(json.dumps({"metric": METRIC, "partial": only, "secondary": secondary}), flush=True)
         return
@@ -653,6 +684,9 @@ def main():
         secondary["backward"] = bench_backward(torch, ba, H, w, args.steps, args.warmup)
         secondary["ring_share"] = bench_ring_share(torch, ba, H, wl.RING_SHARE, 2, 1)
         secondary["causal_ring_layouts"] = bench_layouts(torch, ba, H, wl.CAUSAL_RING_LAYOUTS, 2)
+        ref = gemm_reference(torch, args.steps)
+        ref["walk_kernel_vs_gemm"] = round(achieved / ref["TFLOP/s"], 4)
+        secondary["gemm_reference"] = ref
     if secondary:
         line["secondary"] = secondary
     if not args.no_cpu:
