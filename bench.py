@@ -84,8 +84,9 @@ class Timer:
         return float(np.median([a.elapsed_time(b) for a, b in self.pairs]))
 
 
-def bench_prefill(torch, ba, H, w, steps, warmup):
-    """Headline: fwd_block over all visits in one call + finalize."""
+def bench_prefill(torch, ba, H, w, steps, warmup, fused=True):
+    """Headline: every visit in one call, then finalisation -- fused into the
+    same call (blockattn_fwd_block_finalize), or as fwd_block + finalize."""
     log(f"inputs: {w.name}")
     q, k, v = w.make_inputs()
     qd, kd, vd = H.to_device(q), H.to_device(k), H.to_device(v)
@@ -97,11 +98,16 @@ def bench_prefill(torch, ba, H, w, steps, warmup):
 
     def step(timer=None):
         e0 = timer.start() if timer else None
-        ba.fwd_block(qd, blocks, w.order, st, reset=True, n_kv_heads=w.n_kv_heads, q_pos0=w.q_pos0,
-                     causal=w.causal)
+        if fused:
+            ba.fwd_block_finalize(qd, blocks, w.order, st, reset=True, n_kv_heads=w.n_kv_heads, q_pos0=w.q_pos0,
+                                  causal=w.causal, out=out, lse=lse)
+        else:
+            ba.fwd_block(qd, blocks, w.order, st, reset=True, n_kv_heads=w.n_kv_heads, q_pos0=w.q_pos0,
+                         causal=w.causal)
         if timer:
             timer.stop(e0)
-        ba.finalize(st, out=out, lse=lse)
+        if not fused:
+            ba.finalize(st, out=out, lse=lse)
 
     for _ in range(warmup):
         step()
@@ -115,7 +121,8 @@ def bench_prefill(torch, ba, H, w, steps, warmup):
     ms_step = (t1 - t0) * 1e3 / steps
     flops = w.flops()
     kernel_ms = timer.mean_ms()
-    log(f"prefill: {ms_step:.3f} ms/step, walk kernel {kernel_ms:.3f} ms, {flops / ms_step / 1e9:.1f} TFLOP/s")
+    log(f"prefill{' (fused finalisation)' if fused else ''}: {ms_step:.3f} ms/step, walk kernel {kernel_ms:.3f} ms, "
+        f"{flops / ms_step / 1e9:.1f} TFLOP/s")
     return dict(q=q, k=k, v=v, ms_step=ms_step, kernel_ms=kernel_ms, flops=flops, step=step)
 
 
@@ -230,7 +237,8 @@ def sample_clock(torch, step, seconds):
 
 
 def bench_ring_share(torch, ba, H, w, steps, warmup):
-    """One fwd_block call per ring visit (state carried in HBM) + finalize."""
+    """One call per ring visit, state carried in HBM between calls; the last
+    visit's call also finalises (blockattn_fwd_block_finalize)."""
     log(f"inputs: {w.name}")
     q, k, v = w.make_inputs()
     qd, kd, vd = H.to_device(q), H.to_device(k), H.to_device(v)
@@ -242,10 +250,13 @@ def bench_ring_share(torch, ba, H, w, steps, warmup):
     lse = torch.empty(w.rows, dtype=torch.float32, device="cuda")
 
     def step():
+        last = len(w.order) - 1
         for i, j in enumerate(w.order):
-            ba.fwd_block(qd, blocks, [j], st, reset=(i == 0), n_kv_heads=w.n_kv_heads, q_pos0=w.q_pos0,
-                         causal=w.causal)
-        ba.finalize(st, out=out, lse=lse)
+            kw = dict(reset=(i == 0), n_kv_heads=w.n_kv_heads, q_pos0=w.q_pos0, causal=w.causal)
+            if i < last:
+                ba.fwd_block(qd, blocks, [j], st, **kw)
+            else:
+                ba.fwd_block_finalize(qd, blocks, [j], st, out=out, lse=lse, **kw)
 
     for _ in range(warmup):
         step()
@@ -259,7 +270,7 @@ def bench_ring_share(torch, ba, H, w, steps, warmup):
     log(f"ring share: {ms:.2f} ms/step, {tf:.1f} TFLOP/s")
     return {"workload": w.name, "ms_per_step": round(ms, 3), "TFLOP/s": round(tf, 1),
             "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "visits": len(w.order),
-            "calls": "one fwd_block per visit, state carried in HBM"}
+            "calls": "one call per visit, state carried in HBM; the last call finalises"}
 
 
 class Flusher:

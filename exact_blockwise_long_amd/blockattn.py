@@ -79,11 +79,12 @@ class KVPages(ctypes.Structure):
 
 
 EXPORTS = [
-    "blockattn_fwd_block", "blockattn_fwd_workspace_bytes", "blockattn_shard_states",
-    "blockattn_shard_workspace_bytes", "blockattn_merge_states", "blockattn_finalize",
-    "fanout_prefix_decode", "fanout_workspace_bytes", "fanout_prefix_prefill",
-    "fanout_prefill_workspace_bytes", "fanout_prefix_decode_paged", "fanout_prefix_prefill_paged", "blockattn_workspace_bytes", "blockattn_bwd_delta", "blockattn_bwd_block", "blockattn_status_str",
-    "blockattn_last_error", "blockattn_abi_version",
+    "blockattn_fwd_block", "blockattn_fwd_block_finalize", "blockattn_fwd_workspace_bytes",
+    "blockattn_shard_states", "blockattn_shard_workspace_bytes", "blockattn_merge_states", "blockattn_finalize",
+    "fanout_prefix_decode", "fanout_workspace_bytes", "fanout_prefix_prefill", "fanout_prefill_workspace_bytes",
+    "fanout_prefix_decode_paged", "fanout_prefix_prefill_paged", "blockattn_workspace_bytes",
+    "blockattn_bwd_delta", "blockattn_bwd_block", "blockattn_status_str", "blockattn_last_error",
+    "blockattn_abi_version",
 ]
 
 _lib = None
@@ -112,6 +113,9 @@ def load():
     vp, sz, i32, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
     lib.blockattn_fwd_block.argtypes = [P(Problem), vp, P(KVBlock), i32, P(i32), i32, State, i32, vp, sz, vp]
     lib.blockattn_fwd_block.restype = i32
+    lib.blockattn_fwd_block_finalize.argtypes = [P(Problem), vp, P(KVBlock), i32, P(i32), i32, State, i32, vp, i32,
+                                                 i64, vp, vp, sz, vp]
+    lib.blockattn_fwd_block_finalize.restype = i32
     lib.blockattn_fwd_workspace_bytes.argtypes = [P(Problem), P(KVBlock), i32, P(i32), i32]
     lib.blockattn_fwd_workspace_bytes.restype = sz
     lib.blockattn_shard_states.argtypes = [P(Problem), vp, P(KVBlock), i32, P(State), vp, sz, vp]
@@ -255,6 +259,45 @@ def fwd_block(q: torch.Tensor, blocks: Sequence[Tuple[torch.Tensor, torch.Tensor
                                    _state(state), 1 if reset else 0, _ptr(workspace), ws_bytes,
                                    _stream(stream)), "blockattn_fwd_block")
     return state
+
+
+def fwd_block_finalize(q: torch.Tensor, blocks: Sequence[Tuple[torch.Tensor, torch.Tensor, int]],
+                       order: Optional[Sequence[int]], state, reset: bool, *, n_kv_heads: int, q_pos0: int = 0,
+                       causal: bool = False, scale: float = 0.0, split_mode: int = 0,
+                       out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None, want_lse: bool = True,
+                       lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None):
+    """blockattn_fwd_block_finalize: the visits of fwd_block, then the finalised
+    (A [rows, D], lse [rows] or None) in one call; ``state`` is read when not
+    ``reset`` and left unspecified."""
+    lib = load()
+    p = make_problem(q, n_kv_heads, q_pos0, causal, scale, split_mode)
+    T, Hq, D = q.shape
+    rows = T * Hq
+    _check_blocks(blocks, n_kv_heads, D, q.dtype)
+    _check_state(state, rows, D)
+    if out is None:
+        out = torch.empty(rows, D, dtype=out_dtype, device=q.device)
+    elif out.dim() != 2 or out.shape[0] != rows or out.shape[1] != D or out.stride(1) != 1 or \
+            out.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"out must be bf16 or fp32 [{rows}, {D}] with contiguous rows")
+    if lse is None and want_lse:
+        lse = torch.empty(rows, dtype=torch.float32, device=q.device)
+    elif lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != rows):
+        raise ValueError(f"lse must be contiguous fp32 with {rows} entries")
+    arr = make_blocks(blocks)
+    n_visit = len(order) if order is not None else len(blocks)
+    order_arr = (ctypes.c_int32 * max(1, n_visit))(*(order or []))
+    order_ptr = order_arr if order is not None else None
+    need = lib.blockattn_fwd_workspace_bytes(ctypes.byref(p), arr, len(blocks), order_ptr, n_visit)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    code = BA_BF16 if out.dtype == torch.bfloat16 else BA_F32
+    _check(lib.blockattn_fwd_block_finalize(ctypes.byref(p), _ptr(q), arr, len(blocks), order_ptr, n_visit,
+                                            _state(state), 1 if reset else 0, _ptr(out), code, out.stride(0),
+                                            _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)),
+           "blockattn_fwd_block_finalize")
+    return out, lse
 
 
 def fwd_workspace_bytes(q, blocks, order, *, n_kv_heads, q_pos0=0, causal=False, split_mode=0) -> int:

@@ -238,6 +238,143 @@ ba_status prepare_fwd(const ba_problem* p, const void* q, const ba_kv_block* blo
   return BA_OK;
 }
 
+// Where a forward call that finalises writes: A rows of out_row_stride
+// elements (bf16 or fp32) and, optionally, the rows' log-sum-exp.
+struct FinOut {
+  void* out = nullptr;
+  int32_t dtype = BA_BF16;
+  int64_t stride = 0;
+  float* lse = nullptr;
+};
+
+// The same checks as blockattn_finalize applies to its output.
+ba_status check_fin(const FinOut& f, int head_dim) {
+  if (!f.out) return fail(BA_ERR_NULL, "out is NULL");
+  if (f.dtype != BA_F32 && f.dtype != BA_BF16) return fail(BA_ERR_UNSUPPORTED, "out_dtype %d", f.dtype);
+  if (f.stride < head_dim) return fail(BA_ERR_SHAPE, "out_row_stride %lld < head_dim", (long long)f.stride);
+  if (f.stride % 4 != 0) return fail(BA_ERR_SHAPE, "out_row_stride must be a multiple of 4");
+  if (((uintptr_t)f.out % (f.dtype == BA_BF16 ? 8 : 16)) != 0) return fail(BA_ERR_SHAPE, "out misaligned");
+  return BA_OK;
+}
+
+ba_status finalize_run(ba_state s, int64_t rows, int head_dim, const FinOut& f, hipStream_t stream) {
+  ba::FinalizeArgs a;
+  a.m = s.m;
+  a.l = s.l;
+  a.o = s.o;
+  a.R = rows;
+  a.out = f.out;
+  a.out_bf16 = f.dtype == BA_BF16;
+  a.out_stride = f.stride;
+  a.lse = f.lse;
+  return hip_status(ba::launch_finalize(a, head_dim, stream), "finalize launch");
+}
+
+// The visits of one forward call: update the state, or (fin set) end with the
+// finalised output instead.  Everything is validated before the first launch.
+ba_status fwd_run(const ba_problem* p, const void* q, const ba_kv_block* blocks, int32_t n_blocks,
+                  const int32_t* order, int32_t n_visit, ba_state state, int32_t reset_state, const FinOut* fin,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Visits v;
+  SplitPlan sp;
+  bool split = false;
+  ba_status st = prepare_fwd(p, q, blocks, n_blocks, order, n_visit, v, sp, split);
+  if (st) return st;
+  if (p->q_len == 0) return ok();
+  st = check_state(state, "state");
+  if (st) return st;
+  if (fin) {
+    st = check_fin(*fin, p->head_dim);
+    if (st) return st;
+  }
+  const int D = p->head_dim;
+  const int64_t R = (int64_t)p->q_len * p->n_q_heads;
+  const size_t need = split ? partial_bytes(sp.n_chunks, R, D) : 0;
+  if (split && sp.n_chunks > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(BA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+    if (((uintptr_t)workspace % 16) != 0) return fail(BA_ERR_WORKSPACE, "workspace not 16-byte aligned");
+  }
+
+  if (!split) {
+    ba::WalkArgs a;
+    memset(&a, 0, sizeof(a));
+    a.qs = make_qside(p, q);
+    a.m = state.m;
+    a.l = state.l;
+    a.o = state.o;
+    a.reset = reset_state ? 1 : 0;
+    a.n_seg = 0;
+    for (int j : v.idx) {
+      // blocks no query of the block can see (causal future, or empty) are skipped
+      if (usable_keys(p, blocks[j]) == 0) continue;
+      a.seg[a.n_seg++] = make_seg(blocks[j]);
+    }
+    if (fin && p->dtype != BA_BF16) {
+      // The fp32 walk keeps the state; finalisation follows as its own launch.
+      if (a.reset || a.n_seg > 0) {
+        hipError_t e = ba::launch_walk_f32(a, D, stream);
+        if (e != hipSuccess) return hip_status(e, "fwd_block walk launch");
+      }
+      return finalize_run(state, R, D, *fin, stream);
+    }
+    if (fin) {
+      a.fin_out = fin->out;
+      a.fin_bf16 = fin->dtype == BA_BF16 ? 1 : 0;
+      a.fin_stride = fin->stride;
+      a.fin_lse = fin->lse;
+    } else if (!a.reset && a.n_seg == 0) {
+      return ok();
+    }
+    hipError_t e = (p->dtype == BA_BF16) ? ba::launch_walk_bf16(a, D, stream) : ba::launch_walk_f32(a, D, stream);
+    return hip_status(e, "fwd_block walk launch");
+  }
+
+  float *wm = nullptr, *wl = nullptr, *wo = nullptr;
+  if (sp.n_chunks > 0) {
+    partial_ptrs(workspace, sp.n_chunks, R, &wm, &wl, &wo);
+    ba::SplitArgs a;
+    memset(&a, 0, sizeof(a));
+    a.qs = make_qside(p, q);
+    a.ws_m = wm;
+    a.ws_l = wl;
+    a.ws_o = wo;
+    a.R = R;
+    a.chunk_len = sp.chunk_len;
+    a.n_seg = (int)v.idx.size();
+    for (int i = 0; i < a.n_seg; ++i) {
+      a.seg[i] = make_seg(blocks[v.idx[i]]);
+      a.chunk_begin[i] = sp.begin[i];
+    }
+    a.chunk_begin[a.n_seg] = sp.begin[a.n_seg];
+    hipError_t e = ba::launch_split_bf16(a, sp.n_chunks, D, stream);
+    if (e != hipSuccess) return hip_status(e, "fwd_block split launch");
+  }
+  if (!fin && !reset_state && sp.n_chunks == 0) return ok();
+  ba::MergeGroupArgs mg;
+  memset(&mg, 0, sizeof(mg));
+  mg.pm = wm;
+  mg.pl = wl;
+  mg.po = wo;
+  mg.R = R;
+  mg.n_groups = 1;
+  mg.has_init = reset_state ? 0 : 1;
+  mg.part_begin[0] = 0;
+  mg.part_begin[1] = sp.n_chunks;
+  mg.out_m[0] = state.m;
+  mg.out_l[0] = state.l;
+  mg.out_o[0] = state.o;
+  if (fin) {
+    if (fin->dtype == BA_BF16)
+      mg.fin_out = (uint16_t*)fin->out;
+    else
+      mg.fin_out_f32 = (float*)fin->out;
+    mg.fin_stride = fin->stride;
+    mg.fin_lse = fin->lse;
+  }
+  return hip_status(ba::launch_merge_groups(mg, D, stream), "fwd_block merge launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -273,75 +410,21 @@ size_t blockattn_fwd_workspace_bytes(const ba_problem* p, const ba_kv_block* blo
 ba_status blockattn_fwd_block(const ba_problem* p, const void* q, const ba_kv_block* blocks, int32_t n_blocks,
                               const int32_t* order, int32_t n_visit, ba_state state, int32_t reset_state,
                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  Visits v;
-  SplitPlan sp;
-  bool split = false;
-  ba_status st = prepare_fwd(p, q, blocks, n_blocks, order, n_visit, v, sp, split);
-  if (st) return st;
-  if (p->q_len == 0) return ok();
-  st = check_state(state, "state");
-  if (st) return st;
-  const int D = p->head_dim;
-  const int64_t R = (int64_t)p->q_len * p->n_q_heads;
+  return fwd_run(p, q, blocks, n_blocks, order, n_visit, state, reset_state, nullptr, workspace, workspace_bytes,
+                 stream);
+}
 
-  if (!split) {
-    ba::WalkArgs a;
-    memset(&a, 0, sizeof(a));
-    a.qs = make_qside(p, q);
-    a.m = state.m;
-    a.l = state.l;
-    a.o = state.o;
-    a.reset = reset_state ? 1 : 0;
-    a.n_seg = 0;
-    for (int j : v.idx) {
-      // blocks no query of the block can see (causal future, or empty) are skipped
-      if (usable_keys(p, blocks[j]) == 0) continue;
-      a.seg[a.n_seg++] = make_seg(blocks[j]);
-    }
-    if (!a.reset && a.n_seg == 0) return ok();
-    hipError_t e = (p->dtype == BA_BF16) ? ba::launch_walk_bf16(a, D, stream) : ba::launch_walk_f32(a, D, stream);
-    return hip_status(e, "fwd_block walk launch");
-  }
-
-  const size_t need = partial_bytes(sp.n_chunks, R, D);
-  if (sp.n_chunks > 0 && (!workspace || workspace_bytes < need))
-    return fail(BA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
-  if (sp.n_chunks > 0 && ((uintptr_t)workspace % 16) != 0) return fail(BA_ERR_WORKSPACE, "workspace not 16-byte aligned");
-  float *wm = nullptr, *wl = nullptr, *wo = nullptr;
-  if (sp.n_chunks > 0) {
-    partial_ptrs(workspace, sp.n_chunks, R, &wm, &wl, &wo);
-    ba::SplitArgs a;
-    memset(&a, 0, sizeof(a));
-    a.qs = make_qside(p, q);
-    a.ws_m = wm;
-    a.ws_l = wl;
-    a.ws_o = wo;
-    a.R = R;
-    a.chunk_len = sp.chunk_len;
-    a.n_seg = (int)v.idx.size();
-    for (int i = 0; i < a.n_seg; ++i) {
-      a.seg[i] = make_seg(blocks[v.idx[i]]);
-      a.chunk_begin[i] = sp.begin[i];
-    }
-    a.chunk_begin[a.n_seg] = sp.begin[a.n_seg];
-    hipError_t e = ba::launch_split_bf16(a, sp.n_chunks, D, stream);
-    if (e != hipSuccess) return hip_status(e, "fwd_block split launch");
-  }
-  if (!reset_state && sp.n_chunks == 0) return ok();
-  ba::MergeGroupArgs mg;
-  memset(&mg, 0, sizeof(mg));
-  mg.pm = wm;
-  mg.pl = wl;
-  mg.po = wo;
-  mg.R = R;
-  mg.n_groups = 1;
-  mg.has_init = reset_state ? 0 : 1;
-  mg.part_begin[0] = 0;
-  mg.part_begin[1] = sp.n_chunks;
-  mg.out_m[0] = state.m;
-  mg.out_l[0] = state.l;
-  mg.out_o[0] = state.o;
-  return hip_status(ba::launch_merge_groups(mg, D, stream), "fwd_block merge launch");
+ba_status blockattn_fwd_block_finalize(const ba_problem* p, const void* q, const ba_kv_block* blocks,
+                                       int32_t n_blocks, const int32_t* order, int32_t n_visit, ba_state state,
+                                       int32_t reset_state, void* out, int32_t out_dtype, int64_t out_row_stride,
+                                       float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  FinOut fin;
+  fin.out = out;
+  fin.dtype = out_dtype;
+  fin.stride = out_row_stride;
+  fin.lse = lse;
+  return fwd_run(p, q, blocks, n_blocks, order, n_visit, state, reset_state, &fin, workspace, workspace_bytes,
+                 stream);
 }
 
 ba_status blockattn_bwd_delta(int64_t rows, int32_t head_dim, const void* out, int32_t out_dtype,

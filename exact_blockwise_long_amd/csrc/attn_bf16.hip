@@ -230,6 +230,36 @@ __device__ inline void store_acc(Acc<D>& acc, const LaneRows& lr, int lane, floa
   }
 }
 
+// Finalise instead of writing the state ("RingAttention and Context
+// Parallelism", sections 2 and 7): A = O / l and LSE = m + ln l of valid rows.
+// O and the lane partial sums of l are both relative to the reference max m2
+// (base 2), so A = O / sum(lp) and LSE = m2 ln 2 + ln sum(lp); a row that saw
+// no key (sum 0) gets A = 0 and LSE = -inf.
+template <int D>
+__device__ inline void store_final(const Acc<D>& acc, const LaneRows& lr, int lane, void* out, bool out_bf16,
+                                   int64_t stride, float* lse) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  const int lg = lane >> 4;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float lsum = wave_sum_cols(acc.lp[qb]);
+    if (!lr.valid[qb]) continue;
+    const int64_t r = lr.srow[qb];
+    const bool empty = !(lsum > 0.f);
+    const float inv = empty ? 0.f : 1.f / lsum;
+#pragma unroll
+    for (int db = 0; db < Cfg<D>::DB; ++db) {
+      const f32x4 v = acc.o[db][qb] * inv;
+      const int64_t at = r * stride + 16 * db + 4 * lg;
+      if (out_bf16)
+        *(bf16x4*)((__bf16*)out + at) = __builtin_convertvector(v, bf16x4);
+      else
+        *(f32x4*)((float*)out + at) = v;
+    }
+    if (lse && lg == 0) lse[r] = empty ? -INFINITY : acc.m2[qb] * kLn2 + logf(lsum);
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void walk_kernel(WalkArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[2 * Cfg<D>::STAGEB];
@@ -261,7 +291,10 @@ __global__ __launch_bounds__(kThreads, 2) void walk_kernel(WalkArgs a) {
         tile_compute<D>(stage, lane, qf, acc, qs.c, need_mask, qs.causal != 0, n_valid, krel, lr.qrel);
       },
       (lds_char*)lds, wave_active);
-  store_acc<D>(acc, lane_rows(a.qs, rc, wave, lane), lane, a.m, a.l, a.o, 0);
+  if (a.fin_out)
+    store_final<D>(acc, lane_rows(a.qs, rc, wave, lane), lane, a.fin_out, a.fin_bf16 != 0, a.fin_stride, a.fin_lse);
+  else
+    store_acc<D>(acc, lane_rows(a.qs, rc, wave, lane), lane, a.m, a.l, a.o, 0);
 }
 
 // Chunk `chunk` of the segment table as a segment of its own.

@@ -48,6 +48,13 @@ struct WalkArgs {
   int32_t reset;
   int32_t n_seg;
   Seg seg[kMaxSeg];
+  // With fin_out set the walk ends by finalising instead of writing the state:
+  // out[r * fin_stride + d] = O / l (bf16 when fin_bf16, else fp32) and, if
+  // fin_lse is set, fin_lse[r] = m + ln l; empty rows give 0 and -inf.
+  void* fin_out;
+  int32_t fin_bf16;
+  int64_t fin_stride;
+  float* fin_lse;
 };
 
 // Split: workgroup (row tile, KV head) x chunk; chunk c of the segment table
@@ -117,8 +124,10 @@ struct MergeGroupArgs {
   float* out_m[kMaxSeg];
   float* out_l[kMaxSeg];
   float* out_o[kMaxSeg];
-  uint16_t* fin_out;  // bf16 [R, D] when not null (finalise instead of out_*)
-  float* fin_lse;     // optional with fin_out
+  uint16_t* fin_out;      // bf16 rows when not null (finalise instead of out_*)
+  float* fin_out_f32;     // or fp32 rows when not null
+  int64_t fin_stride;     // elements between output rows (0: D)
+  float* fin_lse;         // optional with fin_out / fin_out_f32
 };
 
 struct MergePtrArgs {

@@ -177,8 +177,8 @@ __global__ __launch_bounds__(kThreads) void merge_groups_kernel(MergeGroupArgs a
   }
   fold(run, P, r, q4, p0 + sub, p1, splits);
   if (!combine<D>(run, splits, slice, q4, sm) || !valid) return;
-  if (a.fin_out) {
-    write_final(run, r, q4, a.fin_out, nullptr, D, a.fin_lse);
+  if (a.fin_out || a.fin_out_f32) {
+    write_final(run, r, q4, a.fin_out, a.fin_out_f32, a.fin_stride ? a.fin_stride : D, a.fin_lse);
     return;
   }
   *(f32x4*)(a.out_o[gi] + r * D + 4 * q4) = run.o;

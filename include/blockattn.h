@@ -158,6 +158,31 @@ ba_status blockattn_fwd_block(const ba_problem* p, const void* q,
                               void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
 
+/* The last visits of a query block and its finalisation in one call ([RAC]
+ * s.2 and s.7): the result is that of blockattn_fwd_block with the same
+ * arguments followed by blockattn_finalize(state, q_len * n_q_heads,
+ * head_dim, out, out_dtype, out_row_stride, lse) -- out [q_len * n_q_heads
+ * rows, state-row order t * n_q_heads + h] of A = O / l in out_dtype (BA_BF16,
+ * rounded to nearest even, or BA_F32), lse (may be NULL) of m + ln l, and 0 /
+ * -inf for rows that saw no key -- up to rounding: the bf16 walk writes A and
+ * LSE from its registers instead of storing the state and reading it back.
+ * With reset_state == 0 the caller's state is read first, as by
+ * blockattn_fwd_block.  Afterwards the contents of state are unspecified (it
+ * may or may not hold the updated state).  Same workspace as
+ * blockattn_fwd_block (blockattn_fwd_workspace_bytes).  out and lse are
+ * written by the device; the caller owns them.  Errors: as
+ * blockattn_fwd_block, plus those of blockattn_finalize for out (BA_ERR_NULL,
+ * BA_ERR_UNSUPPORTED out_dtype, BA_ERR_SHAPE out_row_stride < head_dim or not a
+ * multiple of 4, out not 8-byte (bf16) or 16-byte (fp32) aligned), all checked
+ * before anything is launched. */
+ba_status blockattn_fwd_block_finalize(const ba_problem* p, const void* q,
+                                       const ba_kv_block* blocks, int32_t n_blocks,
+                                       const int32_t* order, int32_t n_visit,
+                                       ba_state state, int32_t reset_state,
+                                       void* out, int32_t out_dtype, int64_t out_row_stride,
+                                       float* lse, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+
 /* Bytes of workspace blockattn_fwd_block needs for these arguments (0 when
  * none).  Returns 0 as well for arguments blockattn_fwd_block would reject. */
 size_t blockattn_fwd_workspace_bytes(const ba_problem* p, const ba_kv_block* blocks,

@@ -44,7 +44,8 @@ def assert_close(got, ref, atol, what="", rel=False):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     same_inf = np.isinf(got) & np.isinf(ref) & (np.sign(got) == np.sign(ref))
-    d = np.where(same_inf, 0.0, np.abs(got - ref))
+    with np.errstate(invalid="ignore"):  # inf - inf where both are the same infinity; masked out
+        d = np.where(same_inf, 0.0, np.abs(got - ref))
     if rel:
         d = d / np.maximum(np.abs(ref), 1e-30)
         d = np.where(same_inf | ((ref == 0) & (got == 0)), 0.0, d)

@@ -153,6 +153,29 @@ def test_finalize_validation(lib):
     assert lib.blockattn_finalize(_state(), 0, 128, FAKE, ba.BA_BF16, 128, None, None) == 0
 
 
+def test_fwd_block_finalize_validation(lib):
+    """The fused forward-and-finalise call checks the problem, the state and
+    the output before any launch; every call here fails one of those checks."""
+    def call(p=None, out=FAKE, dtype=ba.BA_BF16, stride=128, state=None, ws=None, ws_bytes=0):
+        p = p if p is not None else _problem()
+        order = (ctypes.c_int32 * 2)(1, 0)
+        return lib.blockattn_fwd_block_finalize(ctypes.byref(p), FAKE, _blocks(2), 2, order, 2, state or _state(), 1,
+                                                out, dtype, stride, None, ws, ws_bytes, None)
+    assert call(p=_problem(head_dim=96)) == 2
+    assert call(p=_problem(n_kv_heads=3)) == 2
+    assert call(state=ba.State(FAKE, None, FAKE)) == 1
+    assert call(out=None) == 1
+    assert call(dtype=9) == 3
+    assert call(stride=64) == 2
+    assert call(stride=130) == 2
+    assert call(out=FAKE + 4) == 2                        # bf16 rows need 8-byte alignment
+    assert call(out=FAKE + 8, dtype=ba.BA_F32) == 2       # fp32 rows need 16
+    # 16 query tokens split over keys: the workspace is checked before any launch
+    assert call() == 5
+    assert call(ws=FAKE, ws_bytes=16) == 5
+    assert call(p=_problem(q_len=0)) == 0                 # nothing to do: no launch
+
+
 def test_fanout_validation(lib):
     def call(f, ws=None, ws_bytes=0, **ptrs):
         a = dict(q=FAKE, pk=FAKE, pv=FAKE, sk=FAKE, sv=FAKE, out=FAKE)

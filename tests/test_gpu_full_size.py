@@ -73,27 +73,37 @@ def check_sampled(w, q, k, v, out, lse, tokens):
           flush=True)
 
 
-def test_causal_prefill_full_size():
+@pytest.mark.parametrize("fused", [True, False], ids=["fused_finalize", "fwd_block_then_finalize"])
+def test_causal_prefill_full_size(fused):
+    """The benchmark's step (every visit and the finalisation in one call), and
+    the same visits through fwd_block followed by finalize."""
     w = wl.CAUSAL_PREFILL
-    announce(w.name)
+    announce(f"{w.name} fused={fused}")
     q, k, v, qd, blocks = blockwise_device(w)
     st = ba.new_state(w.rows, w.head_dim)
-    ba.fwd_block(qd, blocks, w.order, st, reset=True, n_kv_heads=w.n_kv_heads, q_pos0=w.q_pos0,
-                 causal=w.causal)
-    out, lse = ba.finalize(st)
+    kw = dict(reset=True, n_kv_heads=w.n_kv_heads, q_pos0=w.q_pos0, causal=w.causal)
+    if fused:
+        out, lse = ba.fwd_block_finalize(qd, blocks, w.order, st, **kw)
+    else:
+        ba.fwd_block(qd, blocks, w.order, st, **kw)
+        out, lse = ba.finalize(st)
     torch.cuda.synchronize()
     check_sampled(w, q, k, v, out, lse, sample_tokens(w.q_len, w.block_len, 2, 21))
 
 
 def test_ring_share_full_size_one_call_per_visit():
+    """As the benchmark runs it: one call per visit, the last one finalising."""
     w = wl.RING_SHARE
     announce(w.name)
     q, k, v, qd, blocks = blockwise_device(w)
     st = ba.new_state(w.rows, w.head_dim)
+    last = len(w.order) - 1
     for i, j in enumerate(w.order):
-        ba.fwd_block(qd, blocks, [j], st, reset=(i == 0), n_kv_heads=w.n_kv_heads, q_pos0=w.q_pos0,
-                     causal=w.causal)
-    out, lse = ba.finalize(st)
+        kw = dict(reset=(i == 0), n_kv_heads=w.n_kv_heads, q_pos0=w.q_pos0, causal=w.causal)
+        if i < last:
+            ba.fwd_block(qd, blocks, [j], st, **kw)
+        else:
+            out, lse = ba.fwd_block_finalize(qd, blocks, [j], st, **kw)
     torch.cuda.synchronize()
     del blocks, qd
     check_sampled(w, q, k, v, out, lse, sample_tokens(w.q_len, w.block_len, 3, 9))
