@@ -672,7 +672,7 @@ def main():
                    "block_len": w.block_len, "order": w.order, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "causal": w.causal,
                    "algorithmic_flops_per_step": w.flops()},
-        "roofline": {"kernel": "walk_kernel<128> (bf16 fwd_block, one launch per step)", "bound": "mfma",
+        "roofline": {"kernel": "walk_kernel<128> (bf16 fwd_block_finalize, one launch per step)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_record("walk_kernel_causal_prefill"),
