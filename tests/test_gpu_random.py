@@ -1,8 +1,8 @@
 """Seeded random configurations against the CPU fp64 oracle: block counts,
 lengths (empty and one-key blocks included), visit orders, query positions
 (rows before every key, rows past every key), causal or not, group sizes,
-head dims and split modes, for the forward walk, the backward and the
-fan-out.  Each configuration is drawn from its own seed, printed before it
+head dims and split modes, for the forward walk (also ending in the fused
+forward-and-finalise call), the backward and the fan-out.  Each configuration is drawn from its own seed, printed before it
 touches the GPU, and small enough for the oracle to finish in a second."""
 
 from __future__ import annotations
@@ -182,3 +182,37 @@ def test_random_shards_then_merge(seed):
     merged = ba.new_state(T * Hq, D)
     ba.merge_states(states, merged)
     check_state_vs_oracle(merged, q, k, v, c["q_pos0"], c["causal"], what=f"random shards seed {seed}")
+
+
+@pytest.mark.parametrize("seed", range(5000, 5032))
+def test_random_fused_finalize(seed):
+    """The visits of a random configuration ending in blockattn_fwd_block_finalize:
+    all in one call, or (per_visit) one fwd_block call per visit with the last
+    visit's call finalising; output in bf16 or fp32."""
+    c = draw(seed)
+    out_dtype = torch.float32 if seed % 3 == 0 else torch.bfloat16
+    announce(f"random fused finalize seed {seed}: {c} out {out_dtype}")
+    T, Hq, Hkv, D = c["T"], c["Hq"], c["Hkv"], c["D"]
+    q, k, v = make_case(seed, T, Hq, Hkv, D, c["lens"])
+    qd, kd, vd = H.to_device(q), H.to_device(k), H.to_device(v)
+    blocks, off = [], 0
+    for n in c["lens"]:
+        blocks.append((kd[off:off + n], vd[off:off + n], off))
+        off += n
+    kw = dict(n_kv_heads=Hkv, q_pos0=c["q_pos0"], causal=c["causal"], split_mode=c["split_mode"])
+    st = ba.new_state(T * Hq, D)
+    order = c["order"]
+    if c["per_visit"]:
+        for i, j in enumerate(order[:-1]):
+            ba.fwd_block(qd, blocks, [j], st, reset=(i == 0), **kw)
+        out, lse = ba.fwd_block_finalize(qd, blocks, order[-1:], st, reset=(len(order) == 1), out_dtype=out_dtype,
+                                         **kw)
+    else:
+        out, lse = ba.fwd_block_finalize(qd, blocks, order, st, reset=True, out_dtype=out_dtype, **kw)
+    torch.cuda.synchronize()
+    a_ref, _, _, lse_ref = ora.attend(q.f64(), k.f64(), v.f64(), 1.0 / np.sqrt(D), c["q_pos0"] + np.arange(T),
+                                      None, c["causal"])
+    got = H.host(out).reshape(T, Hq, D)
+    stats = H.assert_bf16_out(got, a_ref, f"random fused seed {seed}")
+    H.assert_close(H.host(lse).reshape(T, Hq), lse_ref, H.BF16_LSE, f"random fused seed {seed} lse")
+    print(f"    max/mean abs err {stats[0]:.2e}/{stats[1]:.2e}", flush=True)
