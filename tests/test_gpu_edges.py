@@ -1,7 +1,7 @@
 """GPU parity at the edges of the C ABI, against the CPU fp64 oracle: the
 largest visit count one call accepts, empty and one-key blocks, MHA decode
-(G = 1) and wide groups (G = 16), strided views out of fused QKV buffers, an
-explicit logit scale, and every split mode.  Every case prints its name,
+(G = 1) and wide groups (G = 16), strided views out of fused QKV buffers,
+head-major layouts, an explicit logit scale, and every split mode.  Every case prints its name,
 shape and seed before it touches the GPU."""
 
 from __future__ import annotations
@@ -134,3 +134,49 @@ def test_strided_views_and_explicit_scale():
         mx, mn = err.max() / np.abs(ref).max(), err.mean() / np.abs(ref).mean()
         print(f"    strided backward {name}: {mx:.2e} / {mn:.2e}", flush=True)
         assert mx <= 2e-2 and mn <= 5e-3, f"strided backward {name}"
+
+
+def test_head_major_layouts():
+    """Q stored as [Hq, T, D] and K, V as [Hkv, L, D], passed as [T, Hq, D] and
+    [L, Hkv, D] views (token stride D, head stride T*D or L*D): both forward
+    paths, the fused forward-and-finalise call, and the backward with dO in
+    the same layout as Q."""
+    seed, T, Hq, Hkv, D, lens, q_pos0 = 84, 150, 8, 2, 128, [130, 64], 60
+    announce(f"head-major layouts T={T} Hq={Hq} Hkv={Hkv} D={D} lens={lens} q_pos0={q_pos0} seed {seed}")
+    g = synth.rng(seed)
+    L = sum(lens)
+    q = synth.normal(g, (T, Hq, D), 0.5, "bf16")
+    k = synth.normal(g, (L, Hkv, D), 0.5, "bf16")
+    v = synth.normal(g, (L, Hkv, D), 0.5, "bf16")
+    do = synth.normal(g, (T, Hq, D), 0.5, "bf16")
+
+    def head_major(t):
+        return H.to_device(t).permute(1, 0, 2).contiguous().permute(1, 0, 2)
+
+    qd, kd, vd, dod = head_major(q), head_major(k), head_major(v), head_major(do)
+    assert qd.stride() == (D, T * D, 1) and kd.stride() == (D, L * D, 1)
+    for mode in (1, 2):
+        run_and_check(q, k, v, lens, [1, 0], Hkv=Hkv, q_pos0=q_pos0, causal=True, split_mode=mode, qd=qd, kd=kd,
+                      vd=vd, what=f"head-major mode {mode}")
+    blocks = [(kd[:lens[0]], vd[:lens[0]], 0), (kd[lens[0]:], vd[lens[0]:], lens[0])]
+    st = ba.new_state(T * Hq, D)
+    out, lse = ba.fwd_block_finalize(qd, blocks, [1, 0], st, reset=True, n_kv_heads=Hkv, q_pos0=q_pos0, causal=True)
+    torch.cuda.synchronize()
+    a_ref, _, _, lse_ref = ora.attend(q.f64(), k.f64(), v.f64(), 1.0 / np.sqrt(D), q_pos0 + np.arange(T), None, True)
+    H.assert_bf16_out(H.host(out).reshape(T, Hq, D), a_ref, "head-major fused")
+    H.assert_close(H.host(lse).reshape(T, Hq), lse_ref, H.BF16_LSE, "head-major fused lse")
+    delta = ba.bwd_delta(out, dod.contiguous().reshape(T * Hq, D))
+    dq = torch.zeros(T * Hq, D, dtype=torch.float32, device="cuda")
+    dkv = [(torch.zeros(n, Hkv, D, dtype=torch.float32, device="cuda"),
+            torch.zeros(n, Hkv, D, dtype=torch.float32, device="cuda")) for n in lens]
+    ba.bwd_block(qd, dod, lse, delta, blocks, [1, 0], dq, dkv, n_kv_heads=Hkv, q_pos0=q_pos0, causal=True)
+    torch.cuda.synchronize()
+    rq, rk, rv = ora.attention_grads(q.f64(), k.f64(), v.f64(), do.f64(), 1.0 / np.sqrt(D), q_pos0 + np.arange(T),
+                                     None, True)
+    for got, ref, name in ((H.host(dq).reshape(T, Hq, D), rq, "dQ"),
+                           (np.concatenate([H.host(a) for a, _ in dkv]), rk, "dK"),
+                           (np.concatenate([H.host(b) for _, b in dkv]), rv, "dV")):
+        err = np.abs(got - ref)
+        mx, mn = err.max() / np.abs(ref).max(), err.mean() / np.abs(ref).mean()
+        print(f"    head-major backward {name}: {mx:.2e} / {mn:.2e}", flush=True)
+        assert mx <= 2e-2 and mn <= 5e-3, f"head-major backward {name}"
