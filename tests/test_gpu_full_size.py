@@ -171,6 +171,14 @@ def test_shard_merge_full_size_all_rows():
     H.assert_close(H.host(merged[0]).reshape(m_ref.shape), m_ref, H.BF16_M * max(1.0, logits_span / 4), "shard m")
     print(f"    all {w.rows} rows, max |m| {logits_span:.1f}: max/mean abs err {stats[0]:.2e}/{stats[1]:.2e}",
           flush=True)
+    # The same 1,048,576 keys as ONE block of one call (the split planner cuts
+    # it into key chunks), finalised in the same call.
+    st = ba.new_state(w.rows, w.head_dim)
+    out1, lse1 = ba.fwd_block_finalize(qd, [(kd, vd, 0)], [0], st, reset=True, n_kv_heads=1)
+    torch.cuda.synchronize()
+    stats = H.assert_bf16_out(H.host(out1).reshape(a_ref.shape), a_ref, w.name + " one block")
+    H.assert_close(H.host(lse1).reshape(lse_ref.shape), lse_ref, H.BF16_LSE, "one-block lse")
+    print(f"    one 1M-key block, fused finalisation: max/mean abs err {stats[0]:.2e}/{stats[1]:.2e}", flush=True)
 
 
 def test_fanout_prefill_full_size_all_rows():
