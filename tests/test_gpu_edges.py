@@ -1,7 +1,8 @@
 """GPU parity at the edges of the C ABI, against the CPU fp64 oracle: the
 largest visit count one call accepts, empty and one-key blocks, MHA decode
 (G = 1) and wide groups (G = 16), strided views out of fused QKV buffers,
-head-major layouts, an explicit logit scale, and every split mode.  Every case prints its name,
+head-major layouts, an explicit logit scale, every split mode, and two
+calls running at once on two streams.  Every case prints its name,
 shape and seed before it touches the GPU."""
 
 from __future__ import annotations
@@ -180,3 +181,54 @@ def test_head_major_layouts():
         mx, mn = err.max() / np.abs(ref).max(), err.mean() / np.abs(ref).mean()
         print(f"    head-major backward {name}: {mx:.2e} / {mn:.2e}", flush=True)
         assert mx <= 2e-2 and mn <= 5e-3, f"head-major backward {name}"
+
+
+def test_two_streams_at_once():
+    """Work goes on the caller's stream and the library keeps no state of its
+    own: a split forward-and-finalise call and a fan-out decode issued three
+    times each on two side streams (default priority) run concurrently and both
+    match the oracle."""
+    seed = 85
+    announce(f"two streams at once: fwd_block_finalize (split) and fanout_prefix_decode, seed {seed}")
+    g = synth.rng(seed)
+    T, Hq, Hkv, D, lens, q_pos0 = 300, 8, 2, 128, [200, 77, 129, 64], 350
+    q = synth.normal(g, (T, Hq, D), 0.5, "bf16")
+    k = synth.normal(g, (sum(lens), Hkv, D), 0.5, "bf16")
+    v = synth.normal(g, (sum(lens), Hkv, D), 0.5, "bf16")
+    nb, P, S = 4, 1000, 37
+    fq = synth.normal(g, (nb, Hq, D), 0.5, "bf16")
+    pk = synth.normal(g, (P, Hkv, D), 0.5, "bf16")
+    pv = synth.normal(g, (P, Hkv, D), 0.5, "bf16")
+    sk = synth.normal(g, (nb, S, Hkv, D), 0.5, "bf16")
+    sv = synth.normal(g, (nb, S, Hkv, D), 0.5, "bf16")
+    qd, kd, vd = H.to_device(q), H.to_device(k), H.to_device(v)
+    blocks, off = [], 0
+    for n in lens:
+        blocks.append((kd[off:off + n], vd[off:off + n], off))
+        off += n
+    fdev = [H.to_device(t) for t in (fq, pk, pv, sk, sv)]
+    # every buffer is allocated before the side streams start
+    kw = dict(n_kv_heads=Hkv, q_pos0=q_pos0, causal=True, split_mode=2)
+    st = ba.new_state(T * Hq, D)
+    out_a = torch.empty(T * Hq, D, dtype=torch.bfloat16, device="cuda")
+    lse_a = torch.empty(T * Hq, dtype=torch.float32, device="cuda")
+    ws_a = torch.empty(max(1, ba.fwd_workspace_bytes(qd, blocks, [2, 0, 3, 1], **kw)), dtype=torch.uint8,
+                       device="cuda")
+    out_b = torch.empty(nb, Hq, D, dtype=torch.bfloat16, device="cuda")
+    lse_b = torch.empty(nb, Hq, dtype=torch.float32, device="cuda")
+    ws_b = torch.empty(ba.fanout_workspace_bytes(nb, Hq, Hkv, D, P, S), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            ba.fwd_block_finalize(qd, blocks, [2, 0, 3, 1], st, reset=True, out=out_a, lse=lse_a, workspace=ws_a,
+                                  **kw)
+        with torch.cuda.stream(s2):
+            ba.fanout_prefix_decode(*fdev, workspace=ws_b, out=out_b, lse=lse_b)
+    torch.cuda.synchronize()
+    a_ref, _, _, lse_ref = ora.attend(q.f64(), k.f64(), v.f64(), 1.0 / np.sqrt(D), q_pos0 + np.arange(T), None, True)
+    H.assert_bf16_out(H.host(out_a).reshape(T, Hq, D), a_ref, "stream 1 forward")
+    H.assert_close(H.host(lse_a).reshape(T, Hq), lse_ref, H.BF16_LSE, "stream 1 lse")
+    b_ref, lse_b_ref = ora.fanout_decode(fq.f64(), pk.f64(), pv.f64(), sk.f64(), sv.f64(), 1.0 / np.sqrt(D))
+    H.assert_bf16_out(H.host(out_b), b_ref, "stream 2 fan-out")
+    H.assert_close(H.host(lse_b), lse_b_ref, H.BF16_LSE, "stream 2 lse")
