@@ -8,15 +8,18 @@
 // section 3 (m = -inf, l = 0, O = 0), with the causal rule of its section 5.
 //
 // Mapping onto CDNA4:
-//  * A workgroup is 4 waves and owns 128 "flat rows" (query token x member of
-//    one GQA group) that all read the same KV head, so one K/V tile in LDS
-//    serves every query head of the group ("AHBM Agentic Runtime
-//    Architecture" s.1.3: rows batched against shared KV).
+//  * A workgroup owns a tile of "flat rows" (query token x member of one GQA
+//    group) that all read the same KV head, so one K/V tile in LDS serves
+//    every query head of the group ("AHBM Agentic Runtime Architecture"
+//    s.1.3: rows batched against shared KV).  The split and fan-out kernels
+//    use 4 waves and 128 rows (two workgroups per compute unit); the walk
+//    uses 8 waves and 256 rows (one per compute unit), so each K/V byte
+//    staged from L2 into LDS serves twice the rows.
 //  * K/V tiles of 64 keys go HBM -> LDS with buffer_load_dwordx4 ... lds (no
 //    register staging), double-buffered: the next tile's loads are in flight
-//    while the current one is multiplied (two LDS stages of 32 KiB fit two
-//    workgroups per compute unit; a deeper third stage measured slower).  16-byte chunks of every LDS row are
-//    XOR-swizzled by row so both operand reads below are bank-conflict free.
+//    while the current one is multiplied (two LDS stages of 32 KiB per
+//    workgroup).  16-byte chunks of every LDS row are XOR-swizzled by row so
+//    both operand reads below are bank-conflict free.
 //  * Each wave owns 32 rows.  Scores are formed transposed, S^T = K Q^T, with
 //    v_mfma_f32_16x16x32_bf16: K (ds_read_b128 from LDS) is the A operand and
 //    Q (kept in registers for the whole kernel) the B operand.  The S^T
@@ -260,19 +263,26 @@ __device__ inline void store_final(const Acc<D>& acc, const LaneRows& lr, int la
   }
 }
 
+// The walk's workgroup: 8 waves of 32 rows.  Against 4 waves of 32 rows at
+// two workgroups per compute unit (the same waves per SIMD and registers per
+// wave), it moves half the K/V bytes from L2 into LDS per multiply; on the
+// power-limited board that made the 32K causal prefill 5 % faster.
+constexpr int kWalkWaves = 8;
+constexpr int kWalkRows = 32 * kWalkWaves;
+
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void walk_kernel(WalkArgs a) {
+__global__ __launch_bounds__(64 * kWalkWaves, 1) void walk_kernel(WalkArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[2 * Cfg<D>::STAGEB];
   const int Hkv = a.qs.Hkv;
-  const int g = blockIdx.x % Hkv;          // consecutive workgroups land on different XCDs;
-  const int n_tiles = (a.qs.q_len * a.qs.G + kTileRows - 1) / kTileRows;
-  const int tile = n_tiles - 1 - (int)(blockIdx.x / Hkv);  // causal: longest rows first
+  const int g = blockIdx.x % Hkv;
+  const int n_tiles = (a.qs.q_len * a.qs.G + kWalkRows - 1) / kWalkRows;
+  const int tile = n_tiles - 1 - (int)(blockIdx.x / Hkv);
   const int total = a.qs.q_len * a.qs.G;
-  const int f0 = tile * kTileRows;
-  const int f1 = min(f0 + kTileRows, total);
+  const int f0 = tile * kWalkRows;
+  const int f1 = min(f0 + kWalkRows, total);
   const RowCtx rc = make_rowctx(a.qs, f0, f1, g);
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const LaneRows lr = lane_rows(a.qs, rc, wave, lane);
   const bool wave_active = f0 + wave * 32 < f1;
 
@@ -285,7 +295,7 @@ __global__ __launch_bounds__(kThreads, 2) void walk_kernel(WalkArgs a) {
     load_acc<D>(acc, lr, lane, a.m, a.l, a.o);
 
   const QSide& qs = a.qs;
-  run_segments<D>(
+  run_segments<D, kCacheReuse, kWalkWaves>(
       qs, rc, a.n_seg, [&](int i) -> const Seg& { return a.seg[i]; },
       [&](const lds_char* stage, bool need_mask, int n_valid, int krel) {
         tile_compute<D>(stage, lane, qf, acc, qs.c, need_mask, qs.causal != 0, n_valid, krel, lr.qrel);
@@ -493,12 +503,12 @@ __global__ __launch_bounds__(kThreads, 2) void fanout_kernel(FanoutArgs a) {
 }  // namespace
 
 hipError_t launch_walk_bf16(const WalkArgs& a, int D, hipStream_t s) {
-  const int tiles = (a.qs.q_len * a.qs.G + kTileRows - 1) / kTileRows;
+  const int tiles = (a.qs.q_len * a.qs.G + kWalkRows - 1) / kWalkRows;
   dim3 grid(tiles * a.qs.Hkv);
   if (D == 128)
-    hipLaunchKernelGGL(walk_kernel<128>, grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(walk_kernel<128>, grid, dim3(64 * kWalkWaves), 0, s, a);
   else
-    hipLaunchKernelGGL(walk_kernel<64>, grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(walk_kernel<64>, grid, dim3(64 * kWalkWaves), 0, s, a);
   return hipGetLastError();
 }
 

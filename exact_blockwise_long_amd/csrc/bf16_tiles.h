@@ -24,14 +24,16 @@ constexpr int kThreads = 256;
 constexpr int kTileKeys = 64;
 constexpr float kTau = 8.0f;   // lazy-rescale headroom, log2 units
 
-template <int D>
+// Tile geometry for head_dim D and W waves per workgroup (the W waves share
+// the loads of every tile).
+template <int D, int W = 4>
 struct Cfg {
   static constexpr int ROWB = D * 2;                  // bytes per K or V row in LDS
   static constexpr int CPR = D / 8;                   // 16-byte chunks per row
   static constexpr int TILEB = kTileKeys * ROWB;      // bytes of one K (or V) tile
   static constexpr int STAGEB = 2 * TILEB;            // K tile then V tile
   static constexpr int RPI = 64 / CPR;                // rows per wave-wide 1 KiB load
-  static constexpr int LPW = kTileKeys / RPI / 4;     // loads per wave per tile (each of K and V)
+  static constexpr int LPW = kTileKeys / RPI / W;     // loads per wave per tile (each of K and V)
   static constexpr int DC = D / 32;                   // 32-wide d chunks (QK^T K-dim steps)
   static constexpr int DB = D / 16;                   // 16-wide d blocks of O^T
 };
@@ -151,16 +153,16 @@ __device__ inline KVSrc make_src(const Seg& s, int g) {
 // fetches the global chunk p ^ swizzle(r), which is where the operand reads
 // look for it.  They depend only on the key strides, so they are computed once
 // per segment.
-template <int D>
+template <int D, int W = 4>
 struct LaneOffs {
-  uint32_t k[Cfg<D>::LPW];
-  uint32_t v[Cfg<D>::LPW];
+  uint32_t k[Cfg<D, W>::LPW];
+  uint32_t v[Cfg<D, W>::LPW];
 };
 
-template <int D>
-__device__ inline LaneOffs<D> lane_offsets(const KVSrc& src, int wave, int lane) {
-  using C = Cfg<D>;
-  LaneOffs<D> o;
+template <int D, int W = 4>
+__device__ inline LaneOffs<D, W> lane_offsets(const KVSrc& src, int wave, int lane) {
+  using C = Cfg<D, W>;
+  LaneOffs<D, W> o;
   const int rsub = lane / C::CPR;
   const int p = lane % C::CPR;
 #pragma unroll
@@ -176,9 +178,9 @@ __device__ inline LaneOffs<D> lane_offsets(const KVSrc& src, int wave, int lane)
 // Keys past the end of the range read as zeros (buffer range check); their
 // scores are masked, so their P is exactly 0.
 // `stage` is the LDS byte address of the stage.
-template <int D, int kAux = kCacheReuse>
-__device__ inline void issue_tile(const KVSrc& src, const LaneOffs<D>& offs, int k0, uint32_t stage, int wave) {
-  using C = Cfg<D>;
+template <int D, int kAux = kCacheReuse, int W = 4>
+__device__ inline void issue_tile(const KVSrc& src, const LaneOffs<D, W>& offs, int k0, uint32_t stage, int wave) {
+  using C = Cfg<D, W>;
   const uint32_t soff_k = (uint32_t)k0 * src.kst;
   const uint32_t soff_v = (uint32_t)k0 * src.vst;
 #pragma unroll
@@ -239,7 +241,7 @@ __device__ inline void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: 
 // keys at or past n_valid are invalid and, for causal problems, key kk sits
 // at position krel + kk relative to the tile's first query.  It runs only in
 // waves that own rows.
-template <int D, int kAux = kCacheReuse, class GetSeg, class TileFn>
+template <int D, int kAux = kCacheReuse, int W = 4, class GetSeg, class TileFn>
 __device__ inline void run_segments(const QSide& qs, const RowCtx& rc, int n_seg, GetSeg get_seg, TileFn tile,
                                     lds_char* lds, bool wave_active) {
   using C = Cfg<D>;
@@ -262,21 +264,21 @@ __device__ inline void run_segments(const QSide& qs, const RowCtx& rc, int n_seg
   if (is >= n_seg) return;
   int ik = 0;
   KVSrc isrc = make_src<D>(get_seg(is), rc.g);
-  LaneOffs<D> ilo = lane_offsets<D>(isrc, wave, lane);
+  LaneOffs<D, W> ilo = lane_offsets<D, W>(isrc, wave, lane);
   // compute cursor
   int cs = is, ck = 0, cn = is_n;
   int64_t cpos0 = get_seg(cs).pos0;
 
   const uint32_t lds_addr = (uint32_t)(size_t)lds;
   auto issue_next = [&](int stage_off) {
-    issue_tile<D, kAux>(isrc, ilo, ik, lds_addr + (uint32_t)stage_off, wave);
+    issue_tile<D, kAux, W>(isrc, ilo, ik, lds_addr + (uint32_t)stage_off, wave);
     ik += kTileKeys;
     if (ik >= is_n) {
       is = next_nonempty(is + 1, is_n);
       ik = 0;
       if (is < n_seg) {
         isrc = make_src<D>(get_seg(is), rc.g);
-        ilo = lane_offsets<D>(isrc, wave, lane);
+        ilo = lane_offsets<D, W>(isrc, wave, lane);
       }
     }
   };
