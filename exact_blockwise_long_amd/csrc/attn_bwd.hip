@@ -11,7 +11,7 @@
 // (the chain rule of the attention definition of its section 1).
 //
 // Two kernels, no atomics, so results do not depend on scheduling:
-//  * dq_kernel walks key tiles for a tile of 128 query rows, exactly like the
+//  * dq_kernel walks key tiles for a tile of 256 query rows, exactly like the
 //    forward walk (the same LDS tile pipeline): S^T = K Q^T and dP^T = V dO^T
 //    with Q and dO in registers, then dQ^T += K^T dS^T with K^T read from the
 //    row-major K tile by ds_read_b64_tr_b16.
@@ -166,18 +166,23 @@ __device__ inline void dq_tile(const lds_char* stage, int lane, const bf16x8 (&q
   }
 }
 
+// dQ workgroups: 8 waves of 32 query rows, so each K/V tile staged in LDS
+// serves 256 rows (as in the forward walk).
+constexpr int kDqWaves = 8;
+constexpr int kDqRows = 32 * kDqWaves;
+
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(BwdArgs a) {
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(16))) char lds[2 * C::STAGEB];
   const QSide& qs = a.qs;
   const int Hkv = qs.Hkv;
   const int g = blockIdx.x % Hkv;
-  const int n_tiles = (qs.q_len * qs.G + kTileRows - 1) / kTileRows;
+  const int n_tiles = (qs.q_len * qs.G + kDqRows - 1) / kDqRows;
   const int tile = n_tiles - 1 - (int)(blockIdx.x / Hkv);  // causal: longest rows first
   const int total = qs.q_len * qs.G;
-  const int f0 = tile * kTileRows;
-  const int f1 = min(f0 + kTileRows, total);
+  const int f0 = tile * kDqRows;
+  const int f1 = min(f0 + kDqRows, total);
   const RowCtx rc = make_rowctx(qs, f0, f1, g);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -204,7 +209,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) dq[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  run_segments<D>(
+  run_segments<D, kCacheReuse, kDqWaves>(
       qs, rc, a.n_seg, [&](int i) -> const Seg& { return a.seg[i]; },
       [&](const lds_char* stage, bool need_mask, int n_valid, int krel) {
         dq_tile<D>(stage, lane, qf, gf, dq, l2, dl, qs.c, need_mask, qs.causal != 0, n_valid, krel, lr.qrel);
@@ -490,14 +495,14 @@ hipError_t launch_delta(const DeltaArgs& a, int D, hipStream_t s) {
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, int n_key_tiles, int D, hipStream_t s) {
-  const int tiles = (a.qs.q_len * a.qs.G + kTileRows - 1) / kTileRows;
+  const int tiles = (a.qs.q_len * a.qs.G + kDqRows - 1) / kDqRows;
   dim3 grid_q(tiles * a.qs.Hkv);
   dim3 grid_k(n_key_tiles * a.qs.Hkv);
   if (D == 128) {
-    hipLaunchKernelGGL(dq_kernel<128>, grid_q, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(dq_kernel<128>, grid_q, dim3(64 * kDqWaves), 0, s, a);
     if (n_key_tiles > 0) hipLaunchKernelGGL(dkdv_kernel<128>, grid_k, dim3(kThreads), 0, s, a);
   } else {
-    hipLaunchKernelGGL(dq_kernel<64>, grid_q, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(dq_kernel<64>, grid_q, dim3(64 * kDqWaves), 0, s, a);
     if (n_key_tiles > 0) hipLaunchKernelGGL(dkdv_kernel<64>, grid_k, dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
