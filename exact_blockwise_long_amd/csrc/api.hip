@@ -676,10 +676,11 @@ ba_status check_fanout(const ba_fanout* f) {
 }
 
 struct FanoutPlan {
-  int row_tiles = 0;   // 128-row tiles of one KV head's rows (n_branches * T * G)
+  bool wide = false;   // 8-wave workgroups, 256-row tiles
+  int row_tiles = 0;   // row tiles of one KV head's rows (n_branches * T * G)
   int chunk_len = 0;
   int n_chunks = 0;    // prefix chunks
-  int srt = 1;         // 128-row tiles of one branch's rows (T * G)
+  int srt = 1;         // row tiles of one branch's rows (T * G)
   int bpj = 1;         // branches per suffix job (when a branch's rows fit one tile)
   int suffix_jobs = 0;
   int slots = 0;       // workspace partial slots
@@ -696,16 +697,16 @@ struct FanoutPlan {
 // walks bpj branches' private suffixes of one KV head one after another (or
 // one row tile of one branch when a branch has more than one); a prefix job
 // walks one chunk of the shared prefix for one row tile of a KV head.
-FanoutPlan plan_fanout(const FanoutShape& f) {
+FanoutPlan plan_fanout_tiles(const FanoutShape& f, int tile_rows, int target) {
   FanoutPlan fp;
   const int G = f.Hq / f.Hkv;
   const int64_t rows = (int64_t)f.nb * f.T * G;
-  fp.row_tiles = (int)((rows + ba::kTileRows - 1) / ba::kTileRows);
-  fp.srt = (int)(((int64_t)f.T * G + ba::kTileRows - 1) / ba::kTileRows);
+  fp.row_tiles = (int)((rows + tile_rows - 1) / tile_rows);
+  fp.srt = (int)(((int64_t)f.T * G + tile_rows - 1) / tile_rows);
   const int xs = fp.row_tiles * f.Hkv;
   const int64_t keys_total =
       (int64_t)f.Hkv * ((int64_t)f.P * fp.row_tiles + (int64_t)f.nb * fp.srt * f.S);
-  const int64_t per_job = keys_total / ba::kFanoutTargetWorkgroups > 1 ? keys_total / ba::kFanoutTargetWorkgroups : 1;
+  const int64_t per_job = keys_total / target > 1 ? keys_total / target : 1;
   if (f.S > 0) {
     if (fp.srt == 1) {
       int64_t bpj = (per_job + f.S / 2) / f.S;
@@ -723,7 +724,7 @@ FanoutPlan plan_fanout(const FanoutShape& f) {
     // leave; only comparable ones take prefix jobs' places in the launch.
     const int64_t suffix_job_keys = fp.srt == 1 ? (int64_t)fp.bpj * f.S : (int64_t)f.S;
     const bool suffix_small = f.S > 0 && 2 * suffix_job_keys < per_job;
-    int64_t want = (ba::kFanoutTargetWorkgroups - (suffix_small ? 0 : fp.suffix_jobs)) / xs;
+    int64_t want = (target - (suffix_small ? 0 : fp.suffix_jobs)) / xs;
     if (want < 1) want = 1;
     int64_t cl = (f.P + want - 1) / want;
     cl = (cl + 63) / 64 * 64;
@@ -734,6 +735,19 @@ FanoutPlan plan_fanout(const FanoutShape& f) {
   fp.slots = fp.n_chunks;
   if (f.S > 0) fp.suffix_slot = fp.slots++;
   fp.n_jobs = xs * fp.n_chunks + fp.suffix_jobs;
+  return fp;
+}
+
+// More than one 128-row tile per KV head (a prefill, or a decode of many
+// branches per group) makes the launch matrix-core bound: it then runs 8-wave
+// workgroups of 256-row tiles, one per compute unit, sized to half as many
+// jobs, so each K/V tile staged in LDS serves twice the rows (as in the walk).
+FanoutPlan plan_fanout(const FanoutShape& f) {
+  FanoutPlan fp = plan_fanout_tiles(f, ba::kTileRows, ba::kFanoutTargetWorkgroups);
+  if (BA_FANOUT_WIDE && fp.row_tiles >= 2) {
+    fp = plan_fanout_tiles(f, ba::kWideTileRows, ba::kFanoutTargetWorkgroups / 2);
+    fp.wide = true;
+  }
   return fp;
 }
 
@@ -816,6 +830,7 @@ ba_status fanout_run(const FanoutShape& f, const void* q, const void* prefix_k, 
   a.suffix_slot = fp.suffix_slot;
   a.srt = fp.srt;
   a.bpj = fp.bpj;
+  a.wide = fp.wide ? 1 : 0;
   if (pages) {
     // The kernel takes the paged path for a job kind when its table is set.
     a.sk = nullptr;

@@ -323,7 +323,7 @@ __device__ inline Seg chunk_seg(const Seg* seg, int n_seg, const int32_t* chunk_
 
 // Partial state of one row tile over the keys of n_seg segments (get_seg(i)
 // returns segment i), written to a workspace slot.
-template <int D, int kAux, class GetSeg>
+template <int D, int kAux, int W = 4, class GetSeg>
 __device__ inline void partial_job_segs(const QSide& qs, int f0, int f1, int g, int n_seg, GetSeg get_seg,
                                         float* ws_m, float* ws_l, float* ws_o, int64_t row_base, lds_char* lds) {
   const RowCtx rc = make_rowctx(qs, f0, f1, g);
@@ -335,7 +335,7 @@ __device__ inline void partial_job_segs(const QSide& qs, int f0, int f1, int g, 
   load_q<D>(lr, lane, qf);
   Acc<D> acc;
   init_acc<D>(acc);
-  run_segments<D, kAux>(
+  run_segments<D, kAux, W>(
       qs, rc, n_seg, get_seg,
       [&](const lds_char* stage, bool need_mask, int n_valid, int krel) {
         tile_compute<D>(stage, lane, qf, acc, qs.c, need_mask, qs.causal != 0, n_valid, krel, lr.qrel);
@@ -344,10 +344,11 @@ __device__ inline void partial_job_segs(const QSide& qs, int f0, int f1, int g, 
   store_acc<D>(acc, lane_rows(qs, rc, wave, lane), lane, ws_m, ws_l, ws_o, row_base);
 }
 
-template <int D, int kAux>
+template <int D, int kAux, int W = 4>
 __device__ inline void partial_job(const QSide& qs, int f0, int f1, int g, const Seg& sg, float* ws_m,
                                    float* ws_l, float* ws_o, int64_t row_base, lds_char* lds) {
-  partial_job_segs<D, kAux>(qs, f0, f1, g, 1, [&](int) -> const Seg& { return sg; }, ws_m, ws_l, ws_o, row_base, lds);
+  partial_job_segs<D, kAux, W>(qs, f0, f1, g, 1, [&](int) -> const Seg& { return sg; }, ws_m, ws_l, ws_o, row_base,
+                               lds);
 }
 
 // The page ids of one job's key range [k0, k1) of a paged sequence whose
@@ -422,8 +423,14 @@ __global__ __launch_bounds__(kThreads, 2) void split_kernel(SplitArgs a) {
 // of the shared prefix, written to slot `chunk`; the remaining jobs are
 // (branch group or branch row tile, KV head) -- each branch's rows against its
 // private suffix under the causal rule, written to slot `suffix_slot`.
-template <int D, int kAux>
-__global__ __launch_bounds__(kThreads, 2) void fanout_kernel(FanoutArgs a) {
+//
+// kWide: 8-wave workgroups of 256-row tiles, one per compute unit, as in the
+// walk (for launches with more than one 128-row tile per KV head, which the
+// matrix cores bound); otherwise 4 waves and 128-row tiles.
+template <int D, int kAux, bool kWide>
+__global__ __launch_bounds__(kWide ? 2 * kThreads : kThreads, kWide ? 1 : 2) void fanout_kernel(FanoutArgs a) {
+  constexpr int W = kWide ? 8 : 4;
+  constexpr int TR = 32 * W;   // rows of a row tile
   __shared__ __attribute__((aligned(16))) char lds[2 * Cfg<D>::STAGEB];
   const int Hkv = a.qs.Hkv;
   const int G = a.qs.G;
@@ -435,13 +442,13 @@ __global__ __launch_bounds__(kThreads, 2) void fanout_kernel(FanoutArgs a) {
     const int x = id % xs;
     const int chunk = id / xs;
     const int g = x % Hkv;
-    const int f0 = (x / Hkv) * kTileRows;
-    const int f1 = min(f0 + kTileRows, total);
+    const int f0 = (x / Hkv) * TR;
+    const int f1 = min(f0 + TR, total);
     const int k_off = chunk * a.chunk_len;
     const int k_end = min(k_off + a.chunk_len, a.prefix.n);
     if (a.prefix_pages) {
       const PageIds pi = load_page_ids(a.prefix_pages, k_off, k_end, a.page_len);
-      partial_job_segs<D, kAux>(
+      partial_job_segs<D, kAux, W>(
           a.qs, f0, f1, g, paged_segments(k_off, k_end, a.page_len),
           [&](int i) { return paged_seg<D>(a, pi, k_off, k_end, i, 0); }, a.ws_m, a.ws_l, a.ws_o,
           (int64_t)chunk * a.R, (lds_char*)lds);
@@ -452,7 +459,7 @@ __global__ __launch_bounds__(kThreads, 2) void fanout_kernel(FanoutArgs a) {
     sg.v = (const uint16_t*)sg.v + (int64_t)k_off * sg.vs_t;
     sg.pos0 = k_off;
     sg.n = k_end - k_off;
-    partial_job<D, kAux>(a.qs, f0, f1, g, sg, a.ws_m, a.ws_l, a.ws_o, (int64_t)chunk * a.R, (lds_char*)lds);
+    partial_job<D, kAux, W>(a.qs, f0, f1, g, sg, a.ws_m, a.ws_l, a.ws_o, (int64_t)chunk * a.R, (lds_char*)lds);
     return;
   }
   const int j = id - n_prefix_jobs;
@@ -477,11 +484,11 @@ __global__ __launch_bounds__(kThreads, 2) void fanout_kernel(FanoutArgs a) {
     QSide qs = a.qs;
     qs.causal = 1;
     qs.q_pos0 = (int64_t)(a.S - a.T) - (int64_t)b * a.T;
-    const int f0 = b * TG + rt * kTileRows;
-    const int f1 = min(f0 + kTileRows, (b + 1) * TG);
+    const int f0 = b * TG + rt * TR;
+    const int f1 = min(f0 + TR, (b + 1) * TG);
     if (a.suffix_pages) {
       const PageIds pi = load_page_ids(a.suffix_pages + (int64_t)b * a.suffix_pages_per_branch, 0, a.S, a.page_len);
-      partial_job_segs<D, kAux>(
+      partial_job_segs<D, kAux, W>(
           qs, f0, f1, g, paged_segments(0, a.S, a.page_len), [&](int i) { return paged_seg<D>(a, pi, 0, a.S, i, 0); },
           a.ws_m, a.ws_l, a.ws_o, (int64_t)a.suffix_slot * a.R, (lds_char*)lds);
       continue;
@@ -496,7 +503,8 @@ __global__ __launch_bounds__(kThreads, 2) void fanout_kernel(FanoutArgs a) {
     sg.pos0 = 0;
     sg.n = a.S;
     sg.pad_ = 0;
-    partial_job<D, kAux>(qs, f0, f1, g, sg, a.ws_m, a.ws_l, a.ws_o, (int64_t)a.suffix_slot * a.R, (lds_char*)lds);
+    partial_job<D, kAux, W>(qs, f0, f1, g, sg, a.ws_m, a.ws_l, a.ws_o, (int64_t)a.suffix_slot * a.R,
+                            (lds_char*)lds);
   }
 }
 
@@ -532,21 +540,30 @@ hipError_t launch_split_bf16(const SplitArgs& a, int n_chunks, int D, hipStream_
   return hipGetLastError();
 }
 
-hipError_t launch_fanout_bf16(const FanoutArgs& a, int n_jobs, int D, hipStream_t s) {
-  dim3 grid(n_jobs);
+template <int D, bool kWide>
+void launch_fanout_w(const FanoutArgs& a, dim3 grid, hipStream_t s) {
   // All of a KV head's rows in one row tile (the decode): each prefix chunk
   // and each suffix is read by one workgroup.
   const bool stream = a.row_tiles == 1 && a.srt == 1;
+  const dim3 block(kWide ? 2 * kThreads : kThreads);
+  if (stream)
+    hipLaunchKernelGGL((fanout_kernel<D, kCacheStream, kWide>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((fanout_kernel<D, kCacheReuse, kWide>), grid, block, 0, s, a);
+}
+
+hipError_t launch_fanout_bf16(const FanoutArgs& a, int n_jobs, int D, hipStream_t s) {
+  dim3 grid(n_jobs);
   if (D == 128) {
-    if (stream)
-      hipLaunchKernelGGL((fanout_kernel<128, kCacheStream>), grid, dim3(kThreads), 0, s, a);
+    if (a.wide)
+      launch_fanout_w<128, true>(a, grid, s);
     else
-      hipLaunchKernelGGL((fanout_kernel<128, kCacheReuse>), grid, dim3(kThreads), 0, s, a);
+      launch_fanout_w<128, false>(a, grid, s);
   } else {
-    if (stream)
-      hipLaunchKernelGGL((fanout_kernel<64, kCacheStream>), grid, dim3(kThreads), 0, s, a);
+    if (a.wide)
+      launch_fanout_w<64, true>(a, grid, s);
     else
-      hipLaunchKernelGGL((fanout_kernel<64, kCacheReuse>), grid, dim3(kThreads), 0, s, a);
+      launch_fanout_w<64, false>(a, grid, s);
   }
   return hipGetLastError();
 }

@@ -97,6 +97,7 @@ struct FanoutArgs {
   int32_t suffix_slot;
   int32_t srt;       // 128-row tiles of one branch's rows
   int32_t bpj;       // branches per suffix job (srt == 1)
+  int32_t wide;      // 1: 8-wave workgroups and 256-row tiles (row_tiles, srt in those)
   // Paged K/V (prefix_pages != nullptr): prefix.k / prefix.v are the pools,
   // page p of a table starts page_len * Hkv * D elements after the pool base.
   const int32_t* prefix_pages;
@@ -187,8 +188,12 @@ struct DeltaArgs {
 
 // Rows per workgroup tile of the bf16 attention kernels.
 constexpr int kTileRows = 128;
+constexpr int kWideTileRows = 256;   // row tile of the 8-wave fan-out workgroups
 
 // Workgroups the fan-out planner aims for (prefix-chunk jobs plus suffix jobs).
+#ifndef BA_FANOUT_WIDE
+#define BA_FANOUT_WIDE 1
+#endif
 #ifndef BA_FANOUT_TARGET_WG
 #define BA_FANOUT_TARGET_WG 512
 #endif
