@@ -165,18 +165,42 @@ int row_tiles(const ba_problem* p) {
   return (int)((flat + ba::kTileRows - 1) / ba::kTileRows) * p->n_kv_heads;
 }
 
+// Row tiling of a split launch.  More than one 128-row tile per KV head makes
+// it matrix-core bound: it then runs 8-wave workgroups of 256-row tiles, one
+// per compute unit, aiming for half as many workgroups (as the walk and the
+// fan-out do).  One tile per KV head stays on 4-wave workgroups.
+struct SplitGeom {
+  bool wide = false;
+  int tiles = 0;    // row tiles x KV heads
+  int target = 0;   // workgroups the planner aims for
+};
+
+SplitGeom split_geom(const ba_problem* p) {
+  SplitGeom sg;
+  const int64_t flat = (int64_t)p->q_len * (p->n_q_heads / p->n_kv_heads);
+  const int64_t narrow = (flat + ba::kTileRows - 1) / ba::kTileRows;
+  sg.wide = BA_SPLIT_WIDE && narrow >= 2;
+  const int64_t per_head = sg.wide ? (flat + ba::kWideTileRows - 1) / ba::kWideTileRows : narrow;
+  sg.tiles = (int)per_head * p->n_kv_heads;
+  sg.target = sg.wide ? kTargetWorkgroups / 2 : kTargetWorkgroups;
+  return sg;
+}
+
 // Split plan: chunk length and per-visit chunk offsets.
 struct SplitPlan {
+  bool wide = false;
   int chunk_len = 0;
   int n_chunks = 0;
   std::vector<int> begin;  // size n_seg + 1
 };
 
-SplitPlan plan_split(const std::vector<int64_t>& keys, int tiles) {
+SplitPlan plan_split(const std::vector<int64_t>& keys, const SplitGeom& geom) {
   SplitPlan sp;
+  sp.wide = geom.wide;
+  const int tiles = geom.tiles;
   int64_t total = 0;
   for (int64_t k : keys) total += k;
-  int64_t want = (kTargetWorkgroups + tiles - 1) / (tiles > 0 ? tiles : 1);
+  int64_t want = (geom.target + tiles - 1) / (tiles > 0 ? tiles : 1);
   if (want < 1) want = 1;
   int64_t cl = (total + want - 1) / want;
   cl = (cl + 63) / 64 * 64;
@@ -233,7 +257,7 @@ ba_status prepare_fwd(const ba_problem* p, const void* q, const ba_kv_block* blo
   if (split) {
     std::vector<int64_t> keys;
     for (int j : v.idx) keys.push_back(usable_keys(p, blocks[j]));
-    sp = plan_split(keys, row_tiles(p));
+    sp = plan_split(keys, split_geom(p));
   }
   return BA_OK;
 }
@@ -341,6 +365,7 @@ ba_status fwd_run(const ba_problem* p, const void* q, const ba_kv_block* blocks,
     a.ws_o = wo;
     a.R = R;
     a.chunk_len = sp.chunk_len;
+    a.wide = sp.wide ? 1 : 0;
     a.n_seg = (int)v.idx.size();
     for (int i = 0; i < a.n_seg; ++i) {
       a.seg[i] = make_seg(blocks[v.idx[i]]);
@@ -522,7 +547,7 @@ size_t blockattn_shard_workspace_bytes(const ba_problem* p, const ba_kv_block* b
     if (check_block(blocks[i], i, p->dtype, p->head_dim) != BA_OK) return 0;
     keys.push_back(usable_keys(p, blocks[i]));
   }
-  SplitPlan sp = plan_split(keys, row_tiles(p));
+  SplitPlan sp = plan_split(keys, split_geom(p));
   return partial_bytes(sp.n_chunks, (int64_t)p->q_len * p->n_q_heads, p->head_dim);
 }
 
@@ -546,7 +571,7 @@ ba_status blockattn_shard_states(const ba_problem* p, const void* q, const ba_kv
   if (p->q_len == 0) return ok();
   const int D = p->head_dim;
   const int64_t R = (int64_t)p->q_len * p->n_q_heads;
-  SplitPlan sp = plan_split(keys, row_tiles(p));
+  SplitPlan sp = plan_split(keys, split_geom(p));
   const size_t need = partial_bytes(sp.n_chunks, R, D);
   float *wm = nullptr, *wl = nullptr, *wo = nullptr;
   if (sp.n_chunks > 0) {
@@ -562,6 +587,7 @@ ba_status blockattn_shard_states(const ba_problem* p, const void* q, const ba_kv
     a.ws_o = wo;
     a.R = R;
     a.chunk_len = sp.chunk_len;
+    a.wide = sp.wide ? 1 : 0;
     a.n_seg = n_blocks;
     for (int i = 0; i < n_blocks; ++i) {
       a.seg[i] = make_seg(blocks[i]);
@@ -900,8 +926,9 @@ size_t blockattn_workspace_bytes(const ba_problem* p, const ba_fanout* f) {
     // The split planner's chunks of a call: sum over visited blocks of
     // ceil(keys / chunk_len) <= total / chunk_len + n_visit, with chunk_len >=
     // total / want, so at most want + BLOCKATTN_MAX_VISITS slots.
-    const int tiles = row_tiles(p);
-    const int64_t want = std::max<int64_t>(1, (kTargetWorkgroups + tiles - 1) / (tiles > 0 ? tiles : 1));
+    const SplitGeom geom = split_geom(p);
+    const int tiles = geom.tiles;
+    const int64_t want = std::max<int64_t>(1, (geom.target + tiles - 1) / (tiles > 0 ? tiles : 1));
     need = partial_bytes(want + BLOCKATTN_MAX_VISITS, (int64_t)p->q_len * p->n_q_heads, p->head_dim);
   }
   if (f && check_fanout(f) == BA_OK && f->n_branches > 0) need = std::max(need, fanout_bytes(decode_shape(f)));

@@ -402,18 +402,22 @@ __device__ inline Seg paged_seg(const FanoutArgs& a, const PageIds& pi, int k0, 
   return sg;
 }
 
-template <int D, int kAux>
-__global__ __launch_bounds__(kThreads, 2) void split_kernel(SplitArgs a) {
+// kWide: 8-wave workgroups of 256-row tiles (more than one 128-row tile per
+// KV head), otherwise 4 waves and 128-row tiles.
+template <int D, int kAux, bool kWide>
+__global__ __launch_bounds__(kWide ? 2 * kThreads : kThreads, kWide ? 1 : 2) void split_kernel(SplitArgs a) {
+  constexpr int W = kWide ? 8 : 4;
+  constexpr int TR = 32 * W;
   __shared__ __attribute__((aligned(16))) char lds[2 * Cfg<D>::STAGEB];
   const int Hkv = a.qs.Hkv;
   const int g = blockIdx.x % Hkv;
   const int tile = blockIdx.x / Hkv;
   const int chunk = blockIdx.y;
   const int total = a.qs.q_len * a.qs.G;
-  const int f0 = tile * kTileRows;
-  const int f1 = min(f0 + kTileRows, total);
+  const int f0 = tile * TR;
+  const int f1 = min(f0 + TR, total);
   const Seg cs = chunk_seg(a.seg, a.n_seg, a.chunk_begin, a.chunk_len, chunk);
-  partial_job<D, kAux>(a.qs, f0, f1, g, cs, a.ws_m, a.ws_l, a.ws_o, (int64_t)chunk * a.R, (lds_char*)lds);
+  partial_job<D, kAux, W>(a.qs, f0, f1, g, cs, a.ws_m, a.ws_l, a.ws_o, (int64_t)chunk * a.R, (lds_char*)lds);
 }
 
 // Shared-prefix fan-out (decode, or prefill of the private suffixes), one
@@ -520,23 +524,26 @@ hipError_t launch_walk_bf16(const WalkArgs& a, int D, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D>
+void launch_split_d(const SplitArgs& a, dim3 grid, bool stream, hipStream_t s) {
+  if (a.wide)
+    hipLaunchKernelGGL((split_kernel<D, kCacheReuse, true>), grid, dim3(2 * kThreads), 0, s, a);
+  else if (stream)
+    hipLaunchKernelGGL((split_kernel<D, kCacheStream, false>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((split_kernel<D, kCacheReuse, false>), grid, dim3(kThreads), 0, s, a);
+}
+
 hipError_t launch_split_bf16(const SplitArgs& a, int n_chunks, int D, hipStream_t s) {
-  const int per_head = (a.qs.q_len * a.qs.G + kTileRows - 1) / kTileRows;
-  const int tiles = per_head;
-  dim3 grid(tiles * a.qs.Hkv, n_chunks);
+  const int tile_rows = a.wide ? kWideTileRows : kTileRows;
+  const int per_head = (a.qs.q_len * a.qs.G + tile_rows - 1) / tile_rows;
+  dim3 grid(per_head * a.qs.Hkv, n_chunks);
   // One row tile per KV head: every K/V byte is read by one workgroup.
   const bool stream = per_head == 1;
-  if (D == 128) {
-    if (stream)
-      hipLaunchKernelGGL((split_kernel<128, kCacheStream>), grid, dim3(kThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((split_kernel<128, kCacheReuse>), grid, dim3(kThreads), 0, s, a);
-  } else {
-    if (stream)
-      hipLaunchKernelGGL((split_kernel<64, kCacheStream>), grid, dim3(kThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((split_kernel<64, kCacheReuse>), grid, dim3(kThreads), 0, s, a);
-  }
+  if (D == 128)
+    launch_split_d<128>(a, grid, stream, s);
+  else
+    launch_split_d<64>(a, grid, stream, s);
   return hipGetLastError();
 }
 

@@ -70,6 +70,7 @@ struct SplitArgs {
   int64_t R;
   int32_t chunk_len;
   int32_t n_seg;
+  int32_t wide;      // 1: 8-wave workgroups and 256-row tiles
   int32_t chunk_begin[kMaxSeg + 1];
   Seg seg[kMaxSeg];
 };
@@ -191,6 +192,9 @@ constexpr int kTileRows = 128;
 constexpr int kWideTileRows = 256;   // row tile of the 8-wave fan-out workgroups
 
 // Workgroups the fan-out planner aims for (prefix-chunk jobs plus suffix jobs).
+#ifndef BA_SPLIT_WIDE
+#define BA_SPLIT_WIDE 1
+#endif
 #ifndef BA_FANOUT_WIDE
 #define BA_FANOUT_WIDE 1
 #endif
