@@ -24,16 +24,16 @@ constexpr int kThreads = 256;
 constexpr int kTileKeys = 64;
 constexpr float kTau = 8.0f;   // lazy-rescale headroom, log2 units
 
-// Tile geometry for head_dim D and W waves per workgroup (the W waves share
-// the loads of every tile).
-template <int D, int W = 4>
+// Tile geometry for head_dim D, W waves per workgroup (the W waves share the
+// loads of every tile) and TK keys per tile.
+template <int D, int W = 4, int TK = kTileKeys>
 struct Cfg {
   static constexpr int ROWB = D * 2;                  // bytes per K or V row in LDS
   static constexpr int CPR = D / 8;                   // 16-byte chunks per row
-  static constexpr int TILEB = kTileKeys * ROWB;      // bytes of one K (or V) tile
+  static constexpr int TILEB = TK * ROWB;             // bytes of one K (or V) tile
   static constexpr int STAGEB = 2 * TILEB;            // K tile then V tile
   static constexpr int RPI = 64 / CPR;                // rows per wave-wide 1 KiB load
-  static constexpr int LPW = kTileKeys / RPI / W;     // loads per wave per tile (each of K and V)
+  static constexpr int LPW = TK / RPI / W;            // loads per wave per tile (each of K and V)
   static constexpr int DC = D / 32;                   // 32-wide d chunks (QK^T K-dim steps)
   static constexpr int DB = D / 16;                   // 16-wide d blocks of O^T
 };
@@ -153,16 +153,16 @@ __device__ inline KVSrc make_src(const Seg& s, int g) {
 // fetches the global chunk p ^ swizzle(r), which is where the operand reads
 // look for it.  They depend only on the key strides, so they are computed once
 // per segment.
-template <int D, int W = 4>
+template <int D, int W = 4, int TK = kTileKeys>
 struct LaneOffs {
-  uint32_t k[Cfg<D, W>::LPW];
-  uint32_t v[Cfg<D, W>::LPW];
+  uint32_t k[Cfg<D, W, TK>::LPW];
+  uint32_t v[Cfg<D, W, TK>::LPW];
 };
 
-template <int D, int W = 4>
-__device__ inline LaneOffs<D, W> lane_offsets(const KVSrc& src, int wave, int lane) {
-  using C = Cfg<D, W>;
-  LaneOffs<D, W> o;
+template <int D, int W = 4, int TK = kTileKeys>
+__device__ inline LaneOffs<D, W, TK> lane_offsets(const KVSrc& src, int wave, int lane) {
+  using C = Cfg<D, W, TK>;
+  LaneOffs<D, W, TK> o;
   const int rsub = lane / C::CPR;
   const int p = lane % C::CPR;
 #pragma unroll
@@ -178,9 +178,9 @@ __device__ inline LaneOffs<D, W> lane_offsets(const KVSrc& src, int wave, int la
 // Keys past the end of the range read as zeros (buffer range check); their
 // scores are masked, so their P is exactly 0.
 // `stage` is the LDS byte address of the stage.
-template <int D, int kAux = kCacheReuse, int W = 4>
-__device__ inline void issue_tile(const KVSrc& src, const LaneOffs<D, W>& offs, int k0, uint32_t stage, int wave) {
-  using C = Cfg<D, W>;
+template <int D, int kAux = kCacheReuse, int W = 4, int TK = kTileKeys>
+__device__ inline void issue_tile(const KVSrc& src, const LaneOffs<D, W, TK>& offs, int k0, uint32_t stage, int wave) {
+  using C = Cfg<D, W, TK>;
   const uint32_t soff_k = (uint32_t)k0 * src.kst;
   const uint32_t soff_v = (uint32_t)k0 * src.vst;
 #pragma unroll
@@ -241,10 +241,10 @@ __device__ inline void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: 
 // keys at or past n_valid are invalid and, for causal problems, key kk sits
 // at position krel + kk relative to the tile's first query.  It runs only in
 // waves that own rows.
-template <int D, int kAux = kCacheReuse, int W = 4, class GetSeg, class TileFn>
+template <int D, int kAux = kCacheReuse, int W = 4, int TK = kTileKeys, class GetSeg, class TileFn>
 __device__ inline void run_segments(const QSide& qs, const RowCtx& rc, int n_seg, GetSeg get_seg, TileFn tile,
                                     lds_char* lds, bool wave_active) {
-  using C = Cfg<D>;
+  using C = Cfg<D, W, TK>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -264,21 +264,21 @@ __device__ inline void run_segments(const QSide& qs, const RowCtx& rc, int n_seg
   if (is >= n_seg) return;
   int ik = 0;
   KVSrc isrc = make_src<D>(get_seg(is), rc.g);
-  LaneOffs<D, W> ilo = lane_offsets<D, W>(isrc, wave, lane);
+  LaneOffs<D, W, TK> ilo = lane_offsets<D, W, TK>(isrc, wave, lane);
   // compute cursor
   int cs = is, ck = 0, cn = is_n;
   int64_t cpos0 = get_seg(cs).pos0;
 
   const uint32_t lds_addr = (uint32_t)(size_t)lds;
   auto issue_next = [&](int stage_off) {
-    issue_tile<D, kAux, W>(isrc, ilo, ik, lds_addr + (uint32_t)stage_off, wave);
-    ik += kTileKeys;
+    issue_tile<D, kAux, W, TK>(isrc, ilo, ik, lds_addr + (uint32_t)stage_off, wave);
+    ik += TK;
     if (ik >= is_n) {
       is = next_nonempty(is + 1, is_n);
       ik = 0;
       if (is < n_seg) {
         isrc = make_src<D>(get_seg(is), rc.g);
-        ilo = lane_offsets<D, W>(isrc, wave, lane);
+        ilo = lane_offsets<D, W, TK>(isrc, wave, lane);
       }
     }
   };
@@ -289,16 +289,16 @@ __device__ inline void run_segments(const QSide& qs, const RowCtx& rc, int n_seg
     __syncthreads();
     if (is < n_seg) issue_next(nxt_off);
     if (wave_active) {
-      const int n_valid = min(kTileKeys, cn - ck);
+      const int n_valid = min(TK, cn - ck);
       const int64_t kpos0 = cpos0 + ck;
-      const bool need_mask = (n_valid < kTileKeys) || (qs.causal && kpos0 + kTileKeys - 1 > rc.qpos_min);
+      const bool need_mask = (n_valid < TK) || (qs.causal && kpos0 + TK - 1 > rc.qpos_min);
       // Visited keys satisfy kpos0 <= qpos_max, so the offset fits easily in 32 bits
       // whenever a mask is needed; far-past tiles are clamped (never masked).
       const int64_t krel64 = kpos0 - rc.qpos_min;
       const int krel = (int)max((int64_t)-(1 << 30), min((int64_t)(1 << 30), krel64));
       tile(lds + cur_off, need_mask, n_valid, krel);
     }
-    ck += kTileKeys;
+    ck += TK;
     if (ck >= cn) {
       cs = next_nonempty(cs + 1, cn);
       ck = 0;
