@@ -174,7 +174,7 @@ __device__ inline LaneOffs<D, W, TK> lane_offsets(const KVSrc& src, int wave, in
   return o;
 }
 
-// Issue the HBM -> LDS loads of the 64-key tile starting at key k0 of `src`.
+// Issue the HBM -> LDS loads of the TK-key tile starting at key k0 of `src`.
 // Keys past the end of the range read as zeros (buffer range check); their
 // scores are masked, so their P is exactly 0.
 // `stage` is the LDS byte address of the stage.

@@ -81,14 +81,15 @@ struct SplitArgs {
 // Prefix job (row tile, KV head g, chunk c): flat rows of the tile against
 // prefix keys [c * chunk_len, ...), no mask, written to workspace slot c.
 // Suffix job for KV head g: with srt == 1, each branch b of a group of bpj
-// consecutive branches; otherwise one 128-row tile rt of one branch b -- the
+// consecutive branches; otherwise one row tile rt of one branch b -- the
 // branch's flat rows [b*T*G, (b+1)*T*G) (tile rt of them) against its own
 // suffix (suffix k/v are [n_branches, S, Hkv, D]), causal with new token i at
-// suffix position S - T + i, written to slot suffix_slot.
+// suffix position S - T + i, written to slot suffix_slot.  Row tiles are 128
+// rows, or 256 with wide.
 struct FanoutArgs {
   QSide qs;          // q_len = n_branches, non-causal
   Seg prefix;        // the whole shared prefix
-  int32_t row_tiles;
+  int32_t row_tiles; // row tiles of one KV head's rows
   int32_t chunk_len;
   int32_t n_chunks;
   const void* sk;
@@ -96,7 +97,7 @@ struct FanoutArgs {
   int32_t S;
   int32_t T;         // new tokens per branch
   int32_t suffix_slot;
-  int32_t srt;       // 128-row tiles of one branch's rows
+  int32_t srt;       // row tiles of one branch's rows
   int32_t bpj;       // branches per suffix job (srt == 1)
   int32_t wide;      // 1: 8-wave workgroups and 256-row tiles (row_tiles, srt in those)
   // Paged K/V (prefix_pages != nullptr): prefix.k / prefix.v are the pools,
