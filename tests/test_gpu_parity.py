@@ -346,11 +346,14 @@ def test_fanout_small(nb, Hq, Hkv, D, P, S):
 # ---------------------------------------------------------------- fan-out prefill
 
 # (nb, T, Hq, Hkv, D, P, S): several new tokens per branch, causal in the suffix.
-# 2 x 20 x 8 rows: 160 rows per KV head, two row tiles per branch; T = S: no
-# older private tokens; P = 0: no prefix; the last case groups branches per job.
+# 2 x 20 x 8 rows: 160 rows per branch and KV head (one 256-row tile of the
+# wide launch, whose tiles span branches for the prefix); T = S: no
+# older private tokens; P = 0: no prefix; the fifth case groups branches per
+# job; the last is one branch (one 256-row tile per KV head, each K/V byte read
+# by one workgroup).
 @pytest.mark.parametrize("nb,T,Hq,Hkv,D,P,S", [(3, 5, 8, 2, 128, 1000, 37), (2, 20, 64, 8, 128, 700, 90),
                                                (4, 7, 8, 2, 64, 300, 7), (3, 9, 8, 2, 128, 0, 70),
-                                               (42, 2, 4, 4, 64, 2000, 3)])
+                                               (42, 2, 4, 4, 64, 2000, 3), (1, 20, 64, 8, 128, 700, 90)])
 def test_fanout_prefill(nb, T, Hq, Hkv, D, P, S):
     announce(f"fanout prefill nb={nb} T={T} Hq={Hq} Hkv={Hkv} D={D} P={P} S={S} seed 72")
     g = synth.rng(72)
