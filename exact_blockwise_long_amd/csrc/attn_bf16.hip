@@ -332,7 +332,7 @@ __device__ inline Seg chunk_seg(const Seg* seg, int n_seg, const int32_t* chunk_
 
 // Partial state of one row tile over the keys of n_seg segments (get_seg(i)
 // returns segment i), written to a workspace slot.
-template <int D, int kAux, int W = 4, class GetSeg>
+template <int D, int kAux, int W = 4, int TK = kTileKeys, class GetSeg>
 __device__ inline void partial_job_segs(const QSide& qs, int f0, int f1, int g, int n_seg, GetSeg get_seg,
                                         float* ws_m, float* ws_l, float* ws_o, int64_t row_base, lds_char* lds) {
   const RowCtx rc = make_rowctx(qs, f0, f1, g);
@@ -344,19 +344,19 @@ __device__ inline void partial_job_segs(const QSide& qs, int f0, int f1, int g, 
   load_q<D>(lr, lane, qf);
   Acc<D> acc;
   init_acc<D>(acc);
-  run_segments<D, kAux, W>(
+  run_segments<D, kAux, W, TK>(
       qs, rc, n_seg, get_seg,
       [&](const lds_char* stage, bool need_mask, int n_valid, int krel) {
-        tile_compute<D>(stage, lane, qf, acc, qs.c, need_mask, qs.causal != 0, n_valid, krel, lr.qrel);
+        tile_compute<D, TK>(stage, lane, qf, acc, qs.c, need_mask, qs.causal != 0, n_valid, krel, lr.qrel);
       },
       lds, wave_active);
   store_acc<D>(acc, lane_rows(qs, rc, wave, lane), lane, ws_m, ws_l, ws_o, row_base);
 }
 
-template <int D, int kAux, int W = 4>
+template <int D, int kAux, int W = 4, int TK = kTileKeys>
 __device__ inline void partial_job(const QSide& qs, int f0, int f1, int g, const Seg& sg, float* ws_m,
                                    float* ws_l, float* ws_o, int64_t row_base, lds_char* lds) {
-  partial_job_segs<D, kAux, W>(qs, f0, f1, g, 1, [&](int) -> const Seg& { return sg; }, ws_m, ws_l, ws_o, row_base,
+  partial_job_segs<D, kAux, W, TK>(qs, f0, f1, g, 1, [&](int) -> const Seg& { return sg; }, ws_m, ws_l, ws_o, row_base,
                                lds);
 }
 
@@ -417,7 +417,8 @@ template <int D, int kAux, bool kWide>
 __global__ __launch_bounds__(kWide ? 2 * kThreads : kThreads, kWide ? 1 : 2) void split_kernel(SplitArgs a) {
   constexpr int W = kWide ? 8 : 4;
   constexpr int TR = 32 * W;
-  __shared__ __attribute__((aligned(16))) char lds[2 * Cfg<D>::STAGEB];
+  constexpr int TK = kWide ? 128 : kTileKeys;   // one workgroup per compute unit has the LDS for it
+  __shared__ __attribute__((aligned(16))) char lds[2 * Cfg<D, W, TK>::STAGEB];
   const int Hkv = a.qs.Hkv;
   const int g = blockIdx.x % Hkv;
   const int tile = blockIdx.x / Hkv;
@@ -426,7 +427,7 @@ __global__ __launch_bounds__(kWide ? 2 * kThreads : kThreads, kWide ? 1 : 2) voi
   const int f0 = tile * TR;
   const int f1 = min(f0 + TR, total);
   const Seg cs = chunk_seg(a.seg, a.n_seg, a.chunk_begin, a.chunk_len, chunk);
-  partial_job<D, kAux, W>(a.qs, f0, f1, g, cs, a.ws_m, a.ws_l, a.ws_o, (int64_t)chunk * a.R, (lds_char*)lds);
+  partial_job<D, kAux, W, TK>(a.qs, f0, f1, g, cs, a.ws_m, a.ws_l, a.ws_o, (int64_t)chunk * a.R, (lds_char*)lds);
 }
 
 // Shared-prefix fan-out (decode, or prefill of the private suffixes), one
@@ -444,6 +445,9 @@ template <int D, int kAux, bool kWide>
 __global__ __launch_bounds__(kWide ? 2 * kThreads : kThreads, kWide ? 1 : 2) void fanout_kernel(FanoutArgs a) {
   constexpr int W = kWide ? 8 : 4;
   constexpr int TR = 32 * W;   // rows of a row tile
+  // 64-key tiles throughout, so that a paged walk (whose page pieces can be
+  // 64 keys long) visits exactly the contiguous walk's tiles and gives its
+  // result bit for bit.
   __shared__ __attribute__((aligned(16))) char lds[2 * Cfg<D>::STAGEB];
   const int Hkv = a.qs.Hkv;
   const int G = a.qs.G;
