@@ -190,15 +190,17 @@ struct DeltaArgs {
 
 // Rows per workgroup tile of the bf16 attention kernels.
 constexpr int kTileRows = 128;
-constexpr int kWideTileRows = 256;   // row tile of the 8-wave fan-out workgroups
+constexpr int kWideTileRows = 256;   // row tile of the 8-wave split and fan-out workgroups
 
-// Workgroups the fan-out planner aims for (prefix-chunk jobs plus suffix jobs).
+// 8-wave workgroups with 256-row tiles for the split and fan-out launches
+// (1 = on, when a KV head's rows fill two or more 128-row tiles).
 #ifndef BA_SPLIT_WIDE
 #define BA_SPLIT_WIDE 1
 #endif
 #ifndef BA_FANOUT_WIDE
 #define BA_FANOUT_WIDE 1
 #endif
+// Workgroups the fan-out planner aims for (prefix-chunk jobs plus suffix jobs).
 #ifndef BA_FANOUT_TARGET_WG
 #define BA_FANOUT_TARGET_WG 512
 #endif

@@ -335,7 +335,9 @@ ba_status fanout_prefix_prefill_paged(const ba_fanout_prefill* f, const ba_kv_pa
 
 /* Workspace enough for every blockattn_fwd_block call on problem p whatever
  * its blocks and visit order (a bound: the split planner makes at most
- * ceil(512 / (row tiles x KV heads)) + BLOCKATTN_MAX_VISITS key chunks), and
+ * ceil(W / (row tiles x KV heads)) + BLOCKATTN_MAX_VISITS key chunks, W being
+ * 512 workgroups of 128-row tiles, or 256 of 256-row tiles when a KV head's
+ * query rows fill two or more 128-row tiles), and
  * for fanout_prefix_decode with descriptor f; either may be NULL.  Lets a
  * caller size one workspace up front (blockattn_shard_states, which always
  * splits, has its own query above).  0 when nothing needs one or an argument
