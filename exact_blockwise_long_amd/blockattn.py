@@ -170,6 +170,40 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+# Debug canary: when set, every buffer this module allocates (workspaces,
+# states from new_state, outputs) is filled with 0xFF bytes -- NaN as fp32 and
+# as bf16 -- before the call, so a kernel that reads a slot before writing it,
+# or lets a key outside its range into a result, shows NaN instead of stale
+# values.
+_poison = False
+
+
+def set_poison(enabled: bool) -> bool:
+    """Turns the NaN canary on or off; returns the previous setting."""
+    global _poison
+    prev, _poison = _poison, bool(enabled)
+    return prev
+
+
+def _empty(shape, dtype, device, stream=None) -> torch.Tensor:
+    """Uninitialised device memory for a call enqueued on ``stream``.
+
+    The allocation is made on that stream, so the caching allocator hands the
+    memory to other work only in that stream's order: a buffer dropped on return
+    (an auto-sized workspace) is not reused while the call still runs.
+    """
+    if stream is None or stream == torch.cuda.current_stream(device):
+        t = torch.empty(shape, dtype=dtype, device=device)
+        if _poison:
+            t.view(torch.uint8).fill_(0xFF)
+        return t
+    with torch.cuda.stream(stream):
+        t = torch.empty(shape, dtype=dtype, device=device)
+        if _poison:
+            t.view(torch.uint8).fill_(0xFF)
+    return t
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return BA_BF16
@@ -205,11 +239,11 @@ def _check_blocks(blocks, n_kv_heads: int, head_dim: int, dtype):
                                  f"{tuple(t.shape)} {t.dtype}")
 
 
-def new_state(rows: int, head_dim: int, device="cuda") -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+def new_state(rows: int, head_dim: int, device="cuda", stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Uninitialised fp32 state buffers (m [rows], l [rows], o [rows, D])."""
-    return (torch.empty(rows, dtype=torch.float32, device=device),
-            torch.empty(rows, dtype=torch.float32, device=device),
-            torch.empty(rows, head_dim, dtype=torch.float32, device=device))
+    return (_empty(rows, torch.float32, device, stream),
+            _empty(rows, torch.float32, device, stream),
+            _empty((rows, head_dim), torch.float32, device, stream))
 
 
 def _state(st) -> State:
@@ -253,7 +287,7 @@ def fwd_block(q: torch.Tensor, blocks: Sequence[Tuple[torch.Tensor, torch.Tensor
     order_ptr = order_arr if order is not None else None
     need = lib.blockattn_fwd_workspace_bytes(ctypes.byref(p), arr, len(blocks), order_ptr, n_visit)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _empty(need, torch.uint8, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.blockattn_fwd_block(ctypes.byref(p), _ptr(q), arr, len(blocks), order_ptr, n_visit,
                                    _state(state), 1 if reset else 0, _ptr(workspace), ws_bytes,
@@ -276,12 +310,12 @@ def fwd_block_finalize(q: torch.Tensor, blocks: Sequence[Tuple[torch.Tensor, tor
     _check_blocks(blocks, n_kv_heads, D, q.dtype)
     _check_state(state, rows, D)
     if out is None:
-        out = torch.empty(rows, D, dtype=out_dtype, device=q.device)
+        out = _empty((rows, D), out_dtype, q.device, stream)
     elif out.dim() != 2 or out.shape[0] != rows or out.shape[1] != D or out.stride(1) != 1 or \
             out.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError(f"out must be bf16 or fp32 [{rows}, {D}] with contiguous rows")
     if lse is None and want_lse:
-        lse = torch.empty(rows, dtype=torch.float32, device=q.device)
+        lse = _empty(rows, torch.float32, q.device, stream)
     elif lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != rows):
         raise ValueError(f"lse must be contiguous fp32 with {rows} entries")
     arr = make_blocks(blocks)
@@ -290,7 +324,7 @@ def fwd_block_finalize(q: torch.Tensor, blocks: Sequence[Tuple[torch.Tensor, tor
     order_ptr = order_arr if order is not None else None
     need = lib.blockattn_fwd_workspace_bytes(ctypes.byref(p), arr, len(blocks), order_ptr, n_visit)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _empty(need, torch.uint8, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     code = BA_BF16 if out.dtype == torch.bfloat16 else BA_F32
     _check(lib.blockattn_fwd_block_finalize(ctypes.byref(p), _ptr(q), arr, len(blocks), order_ptr, n_visit,
@@ -326,7 +360,7 @@ def shard_states(q: torch.Tensor, blocks, states_out, *, n_kv_heads: int, q_pos0
     sts = (State * max(1, len(blocks)))(*[_state(s) for s in states_out])
     need = lib.blockattn_shard_workspace_bytes(ctypes.byref(p), arr, len(blocks))
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _empty(need, torch.uint8, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.blockattn_shard_states(ctypes.byref(p), _ptr(q), arr, len(blocks), sts, _ptr(workspace),
                                       ws_bytes, _stream(stream)), "blockattn_shard_states")
@@ -354,12 +388,12 @@ def finalize(state, out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None
     rows, D = o.shape
     _check_state(state, rows, D)
     if out is None:
-        out = torch.empty(rows, D, dtype=out_dtype, device=o.device)
+        out = _empty((rows, D), out_dtype, o.device, stream)
     elif out.dim() != 2 or out.shape[0] != rows or out.shape[1] != D or out.stride(1) != 1 or \
             out.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError(f"out must be bf16 or fp32 [{rows}, {D}] with contiguous rows")
     if lse is None and want_lse:
-        lse = torch.empty(rows, dtype=torch.float32, device=o.device)
+        lse = _empty(rows, torch.float32, o.device, stream)
     elif lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != rows):
         raise ValueError(f"lse must be contiguous fp32 with {rows} entries")
     code = BA_BF16 if out.dtype == torch.bfloat16 else BA_F32
@@ -405,12 +439,12 @@ def fanout_prefix_decode(q, prefix_k, prefix_v, suffix_k, suffix_v, scale: float
     f = Fanout(nb, Hq, Hkv, D, P, S, scale)
     need = lib.fanout_workspace_bytes(ctypes.byref(f))
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _empty(need, torch.uint8, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if out is None:
-        out = torch.empty(nb, Hq, D, dtype=torch.bfloat16, device=q.device)
+        out = _empty((nb, Hq, D), torch.bfloat16, q.device, stream)
     if lse is None and want_lse:
-        lse = torch.empty(nb, Hq, dtype=torch.float32, device=q.device)
+        lse = _empty((nb, Hq), torch.float32, q.device, stream)
     _check(lib.fanout_prefix_decode(ctypes.byref(f), _ptr(q), _ptr(prefix_k), _ptr(prefix_v), _ptr(suffix_k),
                                     _ptr(suffix_v), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
                                     _stream(stream)), "fanout_prefix_decode")
@@ -441,12 +475,12 @@ def fanout_prefix_prefill(q, prefix_k, prefix_v, suffix_k, suffix_v, scale: floa
     f = FanoutPrefill(nb, T, Hq, Hkv, D, P, S, scale)
     need = lib.fanout_prefill_workspace_bytes(ctypes.byref(f))
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _empty(need, torch.uint8, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if out is None:
-        out = torch.empty(nb, T, Hq, D, dtype=torch.bfloat16, device=q.device)
+        out = _empty((nb, T, Hq, D), torch.bfloat16, q.device, stream)
     if lse is None and want_lse:
-        lse = torch.empty(nb, T, Hq, dtype=torch.float32, device=q.device)
+        lse = _empty((nb, T, Hq), torch.float32, q.device, stream)
     _check(lib.fanout_prefix_prefill(ctypes.byref(f), _ptr(q), _ptr(prefix_k), _ptr(prefix_v), _ptr(suffix_k),
                                      _ptr(suffix_v), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
                                      _stream(stream)), "fanout_prefix_prefill")
@@ -474,7 +508,7 @@ def bwd_delta(out: torch.Tensor, dout: torch.Tensor, delta: Optional[torch.Tenso
     if g2.shape != o2.shape:
         raise ValueError(f"dout {tuple(g2.shape)} must match out {tuple(o2.shape)} row for row")
     if delta is None:
-        delta = torch.empty(rows, dtype=torch.float32, device=out.device)
+        delta = _empty(rows, torch.float32, out.device, stream)
     elif delta.dtype != torch.float32 or not delta.is_contiguous() or delta.numel() != rows:
         raise ValueError(f"delta must be contiguous fp32 with {rows} entries")
     code = BA_BF16 if out.dtype == torch.bfloat16 else BA_F32
@@ -563,12 +597,12 @@ def fanout_prefix_decode_paged(q, k_pool, v_pool, prefix_pages, suffix_pages, pr
     f = Fanout(nb, Hq, Hkv, D, prefix_len, suffix_len, scale)
     need = lib.fanout_workspace_bytes(ctypes.byref(f))
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _empty(need, torch.uint8, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if out is None:
-        out = torch.empty(nb, Hq, D, dtype=torch.bfloat16, device=q.device)
+        out = _empty((nb, Hq, D), torch.bfloat16, q.device, stream)
     if lse is None and want_lse:
-        lse = torch.empty(nb, Hq, dtype=torch.float32, device=q.device)
+        lse = _empty((nb, Hq), torch.float32, q.device, stream)
     _check(lib.fanout_prefix_decode_paged(ctypes.byref(f), ctypes.byref(pages), _ptr(q), _ptr(k_pool), _ptr(v_pool),
                                           _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)),
            "fanout_prefix_decode_paged")
@@ -587,12 +621,12 @@ def fanout_prefix_prefill_paged(q, k_pool, v_pool, prefix_pages, suffix_pages, p
     f = FanoutPrefill(nb, T, Hq, Hkv, D, prefix_len, suffix_len, scale)
     need = lib.fanout_prefill_workspace_bytes(ctypes.byref(f))
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _empty(need, torch.uint8, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if out is None:
-        out = torch.empty(nb, T, Hq, D, dtype=torch.bfloat16, device=q.device)
+        out = _empty((nb, T, Hq, D), torch.bfloat16, q.device, stream)
     if lse is None and want_lse:
-        lse = torch.empty(nb, T, Hq, dtype=torch.float32, device=q.device)
+        lse = _empty((nb, T, Hq), torch.float32, q.device, stream)
     _check(lib.fanout_prefix_prefill_paged(ctypes.byref(f), ctypes.byref(pages), _ptr(q), _ptr(k_pool),
                                            _ptr(v_pool), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
                                            _stream(stream)), "fanout_prefix_prefill_paged")

@@ -85,6 +85,10 @@ ba_status check_block(const ba_kv_block& b, int i, int dtype, int head_dim) {
       return fail(BA_ERR_SHAPE, "block %d: k/v not 16-byte aligned", i);
     if (b.k_stride_token % 8 || b.k_stride_head % 8 || b.v_stride_token % 8 || b.v_stride_head % 8)
       return fail(BA_ERR_SHAPE, "block %d: bf16 strides must be multiples of 8 elements", i);
+    // The tile loads' range check ends a block after its last key only when
+    // one key's row does not run into the next key's.
+    if (b.k_stride_token < head_dim || b.v_stride_token < head_dim)
+      return fail(BA_ERR_SHAPE, "block %d: bf16 token strides must be >= head_dim", i);
     // The bf16 kernels read one KV head of a block through a buffer resource
     // with 32-bit byte offsets.
     if (head_extent_bf16(b.len, b.k_stride_token, head_dim) > (int64_t)UINT32_MAX ||

@@ -6,6 +6,7 @@
 #pragma once
 
 #include "internal.h"
+#include "tile_addr.h"
 
 namespace ba {
 namespace {
@@ -37,22 +38,6 @@ struct Cfg {
   static constexpr int DC = D / 32;                   // 32-wide d chunks (QK^T K-dim steps)
   static constexpr int DB = D / 16;                   // 16-wide d blocks of O^T
 };
-
-// Chunk swizzle of every LDS tile: global 16-byte chunk c of tile row r sits
-// at chunk c ^ swz(r).  Tiles are read two ways: 16-byte row reads (lane l
-// reads row l % 16 of a 16-row block, chunk 4*dc + l / 16) and transposing
-// 8-byte reads (lane l reads 8 bytes of row 4*(l / 16) + (l % 16) / 4 of a
-// 16-row block, chunk pair 2*db + {0, 1}).  LDS has 64 banks of 4 bytes;
-// measured with a one-wave probe on the bank-conflict counter, a 16-byte read
-// is served in four 16-lane passes, each pairing lanes 8a .. 8a + 7 of one
-// quarter-wave with eight lanes of the other half of an odd quarter-wave, and
-// a transposing read in two 32-lane passes.  For D = 128 (one row per bank
-// line) (r & 7) << 1 keeps both kinds conflict-free, while r & 15 doubles the
-// transposing reads' passes; for D = 64 (two rows per bank line) r & 7 does.
-template <int D>
-__device__ inline int swz(int row) {
-  return D == 128 ? ((row & 7) << 1) : (row & 7);
-}
 
 // Reductions over the 4 lanes that share lane % 16 (one query column).
 //
@@ -124,11 +109,12 @@ struct RowCtx {
   int64_t qpos_min, qpos_max;
 };
 
-// A key range as the kernels see it: buffer resources over K and V of one KV
-// head, the byte stride between keys, the absolute position of key 0 and the
-// number of keys.  Reads past the range return zeros (buffer range check).
+// A key range as the kernels see it: K and V of one KV head (the address of
+// key 0), the byte stride between keys, the absolute position of key 0 and
+// the number of keys.
 struct KVSrc {
-  __amdgpu_buffer_rsrc_t k, v;
+  const char* kb;
+  const char* vb;
   uint32_t kst, vst;       // bytes between consecutive keys
   int64_t pos0;
   int n;
@@ -137,22 +123,18 @@ struct KVSrc {
 template <int D>
 __device__ inline KVSrc make_src(const Seg& s, int g) {
   KVSrc r;
-  const char* kb = (const char*)s.k + (int64_t)g * s.ks_h * 2;
-  const char* vb = (const char*)s.v + (int64_t)g * s.vs_h * 2;
+  r.kb = (const char*)s.k + (int64_t)g * s.ks_h * 2;
+  r.vb = (const char*)s.v + (int64_t)g * s.vs_h * 2;
   r.kst = (uint32_t)(s.ks_t * 2);
   r.vst = (uint32_t)(s.vs_t * 2);
-  r.k = make_rsrc(kb, s.n > 0 ? (uint32_t)((s.n - 1) * (int64_t)r.kst + D * 2) : 0u);
-  r.v = make_rsrc(vb, s.n > 0 ? (uint32_t)((s.n - 1) * (int64_t)r.vst + D * 2) : 0u);
   r.pos0 = s.pos0;
   r.n = s.n;
   return r;
 }
 
-// Per-lane byte offsets, within a tile, of the 16-byte chunks this lane moves:
-// wave-wide load j carries RPI whole rows; lane (row r, chunk position p)
-// fetches the global chunk p ^ swizzle(r), which is where the operand reads
-// look for it.  They depend only on the key strides, so they are computed once
-// per segment.
+// Per-lane byte offsets, within a tile, of the 16-byte chunks this lane moves
+// (tile_lane_offset).  They depend only on the key strides, so they are
+// computed once per segment.
 template <int D, int W = 4, int TK = kTileKeys>
 struct LaneOffs {
   uint32_t k[Cfg<D, W, TK>::LPW];
@@ -163,31 +145,35 @@ template <int D, int W = 4, int TK = kTileKeys>
 __device__ inline LaneOffs<D, W, TK> lane_offsets(const KVSrc& src, int wave, int lane) {
   using C = Cfg<D, W, TK>;
   LaneOffs<D, W, TK> o;
-  const int rsub = lane / C::CPR;
-  const int p = lane % C::CPR;
 #pragma unroll
   for (int j = 0; j < C::LPW; ++j) {
-    const int row = (wave * C::LPW + j) * C::RPI + rsub;
-    o.k[j] = (uint32_t)row * src.kst + (uint32_t)((p ^ swz<D>(row)) * 16);
-    o.v[j] = (uint32_t)row * src.vst + (uint32_t)((p ^ swz<D>(row)) * 16);
+    o.k[j] = tile_lane_offset<D, W, TK>(src.kst, wave, lane, j);
+    o.v[j] = tile_lane_offset<D, W, TK>(src.vst, wave, lane, j);
   }
   return o;
 }
 
-// Issue the HBM -> LDS loads of the TK-key tile starting at key k0 of `src`.
-// Keys past the end of the range read as zeros (buffer range check); their
-// scores are masked, so their P is exactly 0.
-// `stage` is the LDS byte address of the stage.
+// Issue the HBM -> LDS loads of the TK-key tile starting at key k0 of `src`,
+// of which the first n_read keys (k0 < n_read <= src.n) may be read.  The
+// tile gets buffer resources of its own (tile_addr.h): based at key k0, they
+// end at the last byte of key n_read - 1, and the scalar offset is 0, so the
+// range check covers every lane's whole offset.  Rows at or past n_read load
+// zeros without touching memory; their scores are masked, so their P is
+// exactly 0 and 0 * V adds nothing.  `stage` is the LDS byte address of the
+// stage.
 template <int D, int kAux = kCacheReuse, int W = 4, int TK = kTileKeys>
-__device__ inline void issue_tile(const KVSrc& src, const LaneOffs<D, W, TK>& offs, int k0, uint32_t stage, int wave) {
+__device__ inline void issue_tile(const KVSrc& src, const LaneOffs<D, W, TK>& offs, int k0, int n_read,
+                                  uint32_t stage, int wave) {
   using C = Cfg<D, W, TK>;
-  const uint32_t soff_k = (uint32_t)k0 * src.kst;
-  const uint32_t soff_v = (uint32_t)k0 * src.vst;
+  const __amdgpu_buffer_rsrc_t rk =
+      make_rsrc(src.kb + (uint32_t)k0 * src.kst, tile_records<D>(n_read, k0, src.kst));
+  const __amdgpu_buffer_rsrc_t rv =
+      make_rsrc(src.vb + (uint32_t)k0 * src.vst, tile_records<D>(n_read, k0, src.vst));
 #pragma unroll
   for (int j = 0; j < C::LPW; ++j) {
     const uint32_t rbase = (uint32_t)((wave * C::LPW + j) * C::RPI);
-    lds_dma16<kAux>(src.k, stage + rbase * C::ROWB, offs.k[j], soff_k);
-    lds_dma16<kAux>(src.v, stage + C::TILEB + rbase * C::ROWB, offs.v[j], soff_v);
+    lds_dma16<kAux>(rk, stage + rbase * C::ROWB, offs.k[j], 0);
+    lds_dma16<kAux>(rv, stage + C::TILEB + rbase * C::ROWB, offs.v[j], 0);
   }
 }
 
@@ -271,7 +257,7 @@ __device__ inline void run_segments(const QSide& qs, const RowCtx& rc, int n_seg
 
   const uint32_t lds_addr = (uint32_t)(size_t)lds;
   auto issue_next = [&](int stage_off) {
-    issue_tile<D, kAux, W, TK>(isrc, ilo, ik, lds_addr + (uint32_t)stage_off, wave);
+    issue_tile<D, kAux, W, TK>(isrc, ilo, ik, is_n, lds_addr + (uint32_t)stage_off, wave);
     ik += TK;
     if (ik >= is_n) {
       is = next_nonempty(is + 1, is_n);

@@ -332,14 +332,26 @@ def paged_layout(g: np.random.Generator, n_branches: int, prefix_len: int, suffi
     return n_pool, prefix_pages, suffix_pages
 
 
+# bf16 bit patterns that poison every key row no correct read touches: NaN,
+# +inf, -inf and a negative NaN, cycled element by element.  A kernel that
+# lets such a row into a result (even multiplied by a zero weight) shows NaN.
+POISON_BF16 = np.array([0x7FC0, 0x7F80, 0xFF80, 0xFFC1], dtype=np.uint16)
+
+
+def poison_rows(shape) -> np.ndarray:
+    """A bf16 bit array of ``shape`` filled with the POISON_BF16 cycle."""
+    n = int(np.prod(shape))
+    return np.resize(POISON_BF16, n).reshape(shape)
+
+
 def scatter_pages(g: np.random.Generator, prefix: synth.Tensor, suffix: synth.Tensor, n_pool: int,
-                  prefix_pages: np.ndarray, suffix_pages: np.ndarray, page_len: int, scale: float = 0.5):
+                  prefix_pages: np.ndarray, suffix_pages: np.ndarray, page_len: int):
     """A bf16 page pool [n_pool, page_len, Hkv, D] holding ``prefix`` [P, Hkv, D]
     and each branch's ``suffix`` [nb, S, Hkv, D] at the given pages; every
-    other row (unused pages, the tails of partial pages) is N(0,1)*scale noise
-    that no correct read touches."""
+    other row (unused pages, the tails of partial pages) holds NaN and +-inf
+    (POISON_BF16), which no correct read touches.  ``g`` is not used."""
     tail = prefix.shape[1:] if prefix.shape[0] else suffix.shape[2:]
-    pool = synth.normal(g, (n_pool, page_len) + tuple(tail), scale, "bf16").storage.copy()
+    pool = poison_rows((n_pool, page_len) + tuple(tail))
 
     def put(x, pages):
         for i, pid in enumerate(pages):

@@ -145,9 +145,14 @@ typedef struct {
  * needs `workspace` of blockattn_fwd_workspace_bytes() bytes (device memory,
  * 256-byte aligned).  Otherwise workspace may be NULL.
  *
+ * Only keys [0, len) of a block are read: the bytes after a block's last key
+ * are never touched, whatever they hold, and a key no query row of a tile of
+ * the call can see under the causal rule is not read either.
+ *
  * Errors: BA_ERR_NULL (p, q, blocks with n_visit > 0, a block's k/v with
  * len > 0, or a state array); BA_ERR_SHAPE (bad head counts, head_dim, negative
- * lengths, non-positive strides, a bf16 block one of whose KV heads spans
+ * lengths, non-positive strides, a bf16 block whose token stride is below
+ * head_dim, a bf16 block one of whose KV heads spans
  * 4 GiB or more: the bf16 kernels address it with 32-bit offsets); BA_ERR_ORDER (duplicate/out-of-range order
  * entry, n_visit > BLOCKATTN_MAX_VISITS or > n_blocks); BA_ERR_UNSUPPORTED
  * (dtype); BA_ERR_WORKSPACE. */

@@ -213,10 +213,10 @@ def test_two_streams_at_once():
     out_a = torch.empty(T * Hq, D, dtype=torch.bfloat16, device="cuda")
     lse_a = torch.empty(T * Hq, dtype=torch.float32, device="cuda")
     ws_a = torch.empty(max(1, ba.fwd_workspace_bytes(qd, blocks, [2, 0, 3, 1], **kw)), dtype=torch.uint8,
-                       device="cuda")
+                       device="cuda").fill_(0xFF)
     out_b = torch.empty(nb, Hq, D, dtype=torch.bfloat16, device="cuda")
     lse_b = torch.empty(nb, Hq, dtype=torch.float32, device="cuda")
-    ws_b = torch.empty(ba.fanout_workspace_bytes(nb, Hq, Hkv, D, P, S), dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(ba.fanout_workspace_bytes(nb, Hq, Hkv, D, P, S), dtype=torch.uint8, device="cuda").fill_(0xFF)
     torch.cuda.synchronize()
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     for _ in range(3):

@@ -50,7 +50,7 @@ def test_ring_step_and_fanout_replayed_from_a_graph():
     qs_ = H.to_device(synth.normal(g, (40, Hq, D), 0.5, "bf16"))
     kw_s = dict(n_kv_heads=Hkv, q_pos0=2000, causal=True)
     ws_s = torch.empty(max(16, ba.fwd_workspace_bytes(qs_, blocks, order, **kw_s)), dtype=torch.uint8,
-                       device="cuda")
+                       device="cuda").fill_(0xFF)
     # ... and a fan-out decode.
     nb, P, S = 8, 3000, 100
     fq = H.to_device(synth.normal(g, (nb, Hq, D), 0.5, "bf16"))
@@ -58,7 +58,7 @@ def test_ring_step_and_fanout_replayed_from_a_graph():
     pv = H.to_device(synth.normal(g, (P, Hkv, D), 0.5, "bf16"))
     sk = H.to_device(synth.normal(g, (nb, S, Hkv, D), 0.5, "bf16"))
     sv = H.to_device(synth.normal(g, (nb, S, Hkv, D), 0.5, "bf16"))
-    ws_f = torch.empty(ba.fanout_workspace_bytes(nb, Hq, Hkv, D, P, S), dtype=torch.uint8, device="cuda")
+    ws_f = torch.empty(ba.fanout_workspace_bytes(nb, Hq, Hkv, D, P, S), dtype=torch.uint8, device="cuda").fill_(0xFF)
 
     st = ba.new_state(T * Hq, D)
     st_s = ba.new_state(40 * Hq, D)
