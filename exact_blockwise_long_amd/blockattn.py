@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(PKG, "libblockattn.so")
 BA_F32, BA_BF16 = 0, 1
 MAX_VISITS = 32
 MAX_MERGE_PARTS = 64
+STATIC_SCRATCH_BYTES = 64 << 20   # BLOCKATTN_STATIC_SCRATCH_BYTES
 
 STATUS = {0: "BA_OK", 1: "BA_ERR_NULL", 2: "BA_ERR_SHAPE", 3: "BA_ERR_UNSUPPORTED",
           4: "BA_ERR_ORDER", 5: "BA_ERR_WORKSPACE", 6: "BA_ERR_HIP"}
@@ -81,7 +82,8 @@ class KVPages(ctypes.Structure):
 EXPORTS = [
     "blockattn_fwd_block", "blockattn_fwd_block_finalize", "blockattn_fwd_workspace_bytes",
     "blockattn_shard_states", "blockattn_shard_workspace_bytes", "blockattn_merge_states", "blockattn_finalize",
-    "fanout_prefix_decode", "fanout_workspace_bytes", "fanout_prefix_prefill", "fanout_prefill_workspace_bytes",
+    "fanout_prefix_decode", "fanout_workspace_bytes", "fanout_prefix_decode_noalloc", "fanout_prefix_prefill",
+    "fanout_prefill_workspace_bytes",
     "fanout_prefix_decode_paged", "fanout_prefix_prefill_paged", "blockattn_workspace_bytes",
     "blockattn_bwd_delta", "blockattn_bwd_block", "blockattn_status_str", "blockattn_last_error",
     "blockattn_abi_version",
@@ -130,6 +132,8 @@ def load():
     lib.fanout_prefix_decode.restype = i32
     lib.fanout_workspace_bytes.argtypes = [P(Fanout)]
     lib.fanout_workspace_bytes.restype = sz
+    lib.fanout_prefix_decode_noalloc.argtypes = [P(Fanout), vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.fanout_prefix_decode_noalloc.restype = i32
     lib.blockattn_bwd_delta.argtypes = [i64, i32, vp, i32, i64, vp, i64, vp, vp]
     lib.blockattn_bwd_delta.restype = i32
     lib.blockattn_bwd_block.argtypes = [P(Problem), vp, vp, vp, vp, P(KVBlock), i32, P(i32), i32, vp,
@@ -448,6 +452,31 @@ def fanout_prefix_decode(q, prefix_k, prefix_v, suffix_k, suffix_v, scale: float
     _check(lib.fanout_prefix_decode(ctypes.byref(f), _ptr(q), _ptr(prefix_k), _ptr(prefix_v), _ptr(suffix_k),
                                     _ptr(suffix_v), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
                                     _stream(stream)), "fanout_prefix_decode")
+    return out, lse
+
+
+def fanout_prefix_decode_noalloc(q, prefix_k, prefix_v, suffix_k, suffix_v, out, lse=None, scale: float = 0.0,
+                                 stream=None):
+    """fanout_prefix_decode_noalloc: fanout_prefix_decode with the library's static
+    per-device scratch instead of a workspace.  ``out`` [nb, Hq, D] bf16 (and
+    ``lse`` [nb, Hq] fp32, optional) are the caller's; this wrapper allocates
+    nothing, so it can run under graph capture."""
+    lib = load()
+    nb, Hq, D = q.shape
+    Hkv = prefix_k.shape[1] if prefix_k is not None else suffix_k.shape[2]
+    P = prefix_k.shape[0] if prefix_k is not None else 0
+    S = suffix_k.shape[1] if suffix_k is not None else 0
+    for name, t in (("q", q), ("prefix_k", prefix_k), ("prefix_v", prefix_v), ("suffix_k", suffix_k),
+                    ("suffix_v", suffix_v)):
+        if t is not None and (not t.is_contiguous() or t.dtype != torch.bfloat16):
+            raise ValueError(f"{name} must be contiguous bf16")
+    if out is None:
+        raise ValueError("out is required (the allocation-free entry point allocates nothing)")
+    _check_fanout(q, prefix_k, prefix_v, suffix_k, suffix_v, out, lse, (nb, Hq), Hkv, D, P, S)
+    f = Fanout(nb, Hq, Hkv, D, P, S, scale)
+    _check(lib.fanout_prefix_decode_noalloc(ctypes.byref(f), _ptr(q), _ptr(prefix_k), _ptr(prefix_v),
+                                            _ptr(suffix_k), _ptr(suffix_v), _ptr(out), _ptr(lse), _stream(stream)),
+           "fanout_prefix_decode_noalloc")
     return out, lse
 
 

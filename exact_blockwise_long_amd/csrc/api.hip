@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "internal.h"
@@ -892,6 +893,35 @@ ba_status fanout_run(const FanoutShape& f, const void* q, const void* prefix_k, 
   return hip_status(ba::launch_merge_groups(mg, D, stream), "fanout merge launch");
 }
 
+// Scratch of the allocation-free fan-out decode: one array per device, part of
+// the library's code object, zero at load and held until the process ends.
+// In host code `scratch` only names the symbol; its device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kStaticScratchBytes = BLOCKATTN_STATIC_SCRATCH_BYTES;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The scratch address on the current device (looked up on its first use).
+ba_status static_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(BA_ERR_UNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(BA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return BA_OK;
+}
+
 FanoutShape decode_shape(const ba_fanout* f) {
   FanoutShape s;
   s.nb = f->n_branches;
@@ -951,6 +981,23 @@ ba_status fanout_prefix_decode(const ba_fanout* f, const void* q, const void* pr
   if (st) return st;
   return fanout_run(decode_shape(f), q, prefix_k, prefix_v, suffix_k, suffix_v, out, lse, workspace,
                     workspace_bytes, stream);
+}
+
+ba_status fanout_prefix_decode_noalloc(const ba_fanout* f, const void* q, const void* prefix_k,
+                                       const void* prefix_v, const void* suffix_k, const void* suffix_v,
+                                       void* out, float* lse, hipStream_t stream) {
+  ba_status st = check_fanout(f);
+  if (st) return st;
+  if (f->n_branches == 0) return ok();
+  const size_t need = fanout_bytes(decode_shape(f));
+  if (need > kStaticScratchBytes)
+    return fail(BA_ERR_WORKSPACE, "fan-out needs %zu bytes of scratch; the static scratch holds %zu", need,
+                kStaticScratchBytes);
+  void* ws = nullptr;
+  st = static_scratch(&ws);
+  if (st) return st;
+  return fanout_run(decode_shape(f), q, prefix_k, prefix_v, suffix_k, suffix_v, out, lse, ws, kStaticScratchBytes,
+                    stream);
 }
 
 size_t fanout_prefill_workspace_bytes(const ba_fanout_prefill* f) {

@@ -260,6 +260,27 @@ ba_status fanout_prefix_decode(const ba_fanout* f, const void* q,
 
 size_t fanout_workspace_bytes(const ba_fanout* f);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: the same
+ * fan-out decode as fanout_prefix_decode (same kernels, bit-identical
+ * results) with no workspace argument.  Its partial states go to a scratch
+ * array of BLOCKATTN_STATIC_SCRATCH_BYTES that the library holds on each
+ * device it runs on, from the first call on that device (the calling thread's
+ * current device, to which `stream` must belong) until the process ends.  The
+ * call allocates nothing.  Every call on one device shares that device's
+ * scratch, and it keeps the last call's contents: calls that overlap on one
+ * device (on different streams, or from different threads without ordering)
+ * race; calls on one stream are ordered and safe.  The caller owns q, the K/V
+ * and out/lse as for fanout_prefix_decode.  Errors: as fanout_prefix_decode,
+ * with BA_ERR_WORKSPACE when fanout_workspace_bytes(f) exceeds the scratch
+ * (checked before anything is enqueued), BA_ERR_HIP when the scratch's
+ * address cannot be obtained. */
+#define BLOCKATTN_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+ba_status fanout_prefix_decode_noalloc(const ba_fanout* f, const void* q,
+                                       const void* prefix_k, const void* prefix_v,
+                                       const void* suffix_k, const void* suffix_v,
+                                       void* out, float* lse, hipStream_t stream);
+
 /* Shared-prefix fan-out over several new tokens per branch: prefill of the
  * branches' private suffixes ([AHBM] s.2.5, s.3.1-3.2 and s.3.6: 8 sub-agents
  * x 20 new tokens give a combined query matrix of 160 rows per query head).

@@ -194,6 +194,21 @@ def test_fanout_validation(lib):
     assert call(ba.Fanout(0, 8, 2, 128, 100, 10, 0.0)) == 0   # no branches: no-op
 
 
+def test_fanout_noalloc_rejects_more_than_its_scratch(lib):
+    # decode shapes whose partial states exceed the static scratch: rejected on
+    # the host before the scratch is looked up or anything is enqueued
+    f = ba.Fanout(2048, 64, 8, 128, 65536, 512, 0.0)
+    assert lib.fanout_workspace_bytes(ctypes.byref(f)) > ba.STATIC_SCRATCH_BYTES
+    assert lib.fanout_prefix_decode_noalloc(ctypes.byref(f), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 5
+    assert b"static scratch" in lib.blockattn_last_error()
+    # the full-size 64K decode (16 branches) fits
+    f = ba.Fanout(16, 64, 8, 128, 65536, 512, 0.0)
+    assert 0 < lib.fanout_workspace_bytes(ctypes.byref(f)) <= ba.STATIC_SCRATCH_BYTES
+    # shape errors come first, as for fanout_prefix_decode
+    assert lib.fanout_prefix_decode_noalloc(ctypes.byref(ba.Fanout(4, 8, 3, 128, 100, 10, 0.0)), FAKE, FAKE, FAKE,
+                                            FAKE, FAKE, FAKE, None, None) == 2
+
+
 def test_fanout_prefill_validation(lib):
     def call(f, ws=None, ws_bytes=0, **ptrs):
         a = dict(q=FAKE, pk=FAKE, pv=FAKE, sk=FAKE, sv=FAKE, out=FAKE)
