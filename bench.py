@@ -2,18 +2,25 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--no-secondary]
 
-A step is one pass of the hot path over one batch of synthetic input: the
-headline workload is causal prefill of one 4096-token query block (GQA 64/8,
-head_dim 128, bf16) against 8 K/V blocks of 4096 visited in ring order
-7, 6, ..., 0 with fp32 (m, l, O) state, then finalisation to bf16.  ``value``
-is algorithmic TFLOP/s (4 * D * Hq * visible (query, key) pairs per step).
+A step is one pass of the hot path over one batch of synthetic input.  The
+headline workload is one GPU's share of a causal ring at long context: a
+16384-token query block (block 12 of 16 over a 262144-token sequence; GQA
+64/8, head_dim 128, bf16) walks the K/V blocks in ring order 12, 11, ..., 0
+with fp32 (m, l, O) state carried in HBM between calls -- one
+``blockattn_fwd_block`` call per ring visit, the last visit with visible keys
+finalising in the same call; blocks 13-15 lie in the causal future and make
+no call.  ``value`` is algorithmic TFLOP/s (4 * D * Hq * visible (query, key)
+pairs per step).
 
 The line also carries the roofline of the dominant kernel (measured live with
-HIP events on the stream it runs on), the CPU oracle timed on a bounded
-sample of the same workload, secondary measurements of the other
-workloads (ring share, fan-out decode and prefill, sharded merge, scaled
-merge, backward, causal shard layouts), and a library bf16 GEMM timed the same
-way as the board's sustained matrix-core rate under its power limit.
+HIP events around each launch, on the stream it runs on), its MFMA
+utilisation and HBM bytes from the committed rocprofv3 counter runs when they
+match the current kernel sources, the CPU oracle timed on a bounded sample
+of the same workload, every workload's input SHA-256 and its errors against
+the oracle, and secondary measurements of the other workloads (the 32K
+causal prefill, fan-out decode and prefill, sharded merge, scaled merge,
+backward, causal shard layouts) with a library bf16 GEMM timed the same way
+as the board's sustained matrix-core rate under its power limit.
 Prints exactly one JSON line (on stdout); progress goes to stderr.
 """
 
@@ -41,8 +48,9 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def traffic_record(kernel: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they match the current sources."""
+def counters_record(key: str):
+    """The committed rocprofv3 counter record of one kernel and workload
+    (profiles/traffic.json), or None when it was taken on other kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -51,13 +59,37 @@ def traffic_record(kernel: str):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    entry = rec.get(kernel)
+    entry = rec.get(key)
     if not entry:
         return None
     from exact_blockwise_long_amd import build
     if entry.get("source_sha256") != build.sources_digest():
         return None
-    return entry.get("hbm_bytes_per_launch")
+    return entry
+
+
+def traffic_record(key: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match the current sources."""
+    entry = counters_record(key)
+    return None if entry is None else entry.get("hbm_bytes_per_launch")
+
+
+class DevIO:
+    """Host synthetic tensors to device tensors (the binding's from_host)."""
+
+    def __init__(self, ba):
+        self.ba = ba
+
+    def to_device(self, t):
+        return self.ba.from_host(t.storage, t.dtype == "bf16")
+
+
+def input_sha256(tensors, names=("q", "k", "v")):
+    """SHA-256 of each input's storage bits (NumPy does not promise stream stability across versions)."""
+    return {n: t.sha256() for n, t in zip(names, tensors)}
+
+
+FANOUT_NAMES = ("q", "prefix_k", "prefix_v", "suffix_k", "suffix_v")
 
 
 class Timer:
@@ -77,18 +109,23 @@ class Timer:
         e1.record()
         self.pairs.append((e0, e1))
 
+    def all_ms(self):
+        return [a.elapsed_time(b) for a, b in self.pairs]
+
     def mean_ms(self):
-        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs]))
+        return float(np.mean(self.all_ms()))
 
     def median_ms(self):
         return float(np.median([a.elapsed_time(b) for a, b in self.pairs]))
 
 
 def bench_prefill(torch, ba, H, w, steps, warmup, fused=True):
-    """Headline: every visit in one call, then finalisation -- fused into the
-    same call (blockattn_fwd_block_finalize), or as fwd_block + finalize."""
+    """The 32K causal prefill: every visit of the query block in one call, then
+    finalisation -- fused into the same call (blockattn_fwd_block_finalize), or
+    as fwd_block + finalize."""
     log(f"inputs: {w.name}")
     q, k, v = w.make_inputs()
+    sha = input_sha256((q, k, v))
     qd, kd, vd = H.to_device(q), H.to_device(k), H.to_device(v)
     blocks = [(kd[b * w.block_len:(b + 1) * w.block_len], vd[b * w.block_len:(b + 1) * w.block_len],
                b * w.block_len) for b in range(w.n_blocks)]
@@ -121,9 +158,19 @@ def bench_prefill(torch, ba, H, w, steps, warmup, fused=True):
     ms_step = (t1 - t0) * 1e3 / steps
     flops = w.flops()
     kernel_ms = timer.mean_ms()
+    tf, ktf = flops / ms_step / 1e9, flops / kernel_ms / 1e9
     log(f"prefill{' (fused finalisation)' if fused else ''}: {ms_step:.3f} ms/step, walk kernel {kernel_ms:.3f} ms, "
-        f"{flops / ms_step / 1e9:.1f} TFLOP/s")
-    return dict(q=q, k=k, v=v, ms_step=ms_step, kernel_ms=kernel_ms, flops=flops, step=step)
+        f"{tf:.1f} TFLOP/s")
+    cnt = counters_record("walk_kernel_causal_prefill") or {}
+    res = {"workload": w.name, "ms_per_step": round(ms_step, 4), "TFLOP/s": round(tf, 1),
+           "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "algorithmic_flops_per_step": flops,
+           "calls": "one blockattn_fwd_block_finalize call per step (every visit, then the finalised output)",
+           "roofline": {"kernel": "walk_kernel<128>", "bound": "mfma", "achieved": round(ktf, 2),
+                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ktf / PEAK_BF16_TFLOPS, 4),
+                        "traffic": cnt.get("hbm_bytes_per_launch"), "mfma_util_pct": cnt.get("mfma_util_pct"),
+                        "kernel_ms_mean": round(kernel_ms, 4)},
+           "input_sha256": sha}
+    return dict(result=res, q=q, k=k, v=v, out=out, lse=lse, step=step, kernel_ms=kernel_ms, flops=flops)
 
 
 def bench_backward(torch, ba, H, w, steps, warmup):
@@ -237,40 +284,55 @@ def sample_clock(torch, step, seconds):
 
 
 def bench_ring_share(torch, ba, H, w, steps, warmup):
-    """One call per ring visit, state carried in HBM between calls; the last
-    visit's call also finalises (blockattn_fwd_block_finalize)."""
+    """One GPU's share of a causal ring (the headline).  One blockattn_fwd_block
+    call per ring visit, fp32 state carried in HBM between calls; the last
+    visit whose block has visible keys calls blockattn_fwd_block_finalize
+    instead and writes the output.  Visits of blocks wholly in the causal
+    future make no call (the rule lets no key of theirs in).  Every launch is
+    bracketed by HIP events on the stream it runs on."""
     log(f"inputs: {w.name}")
     q, k, v = w.make_inputs()
+    sha = input_sha256((q, k, v))
     qd, kd, vd = H.to_device(q), H.to_device(k), H.to_device(v)
-    del q, k, v
     blocks = [(kd[b * w.block_len:(b + 1) * w.block_len], vd[b * w.block_len:(b + 1) * w.block_len],
                b * w.block_len) for b in range(w.n_blocks)]
     st = ba.new_state(w.rows, w.head_dim)
     out = torch.empty(w.rows, w.head_dim, dtype=torch.bfloat16, device="cuda")
     lse = torch.empty(w.rows, dtype=torch.float32, device="cuda")
+    visible = w.visited_nonempty()
+    skipped = [b for b in w.order if b not in visible]
+    last = len(visible) - 1
+    kw = dict(n_kv_heads=w.n_kv_heads, q_pos0=w.q_pos0, causal=w.causal)
 
-    def step():
-        last = len(w.order) - 1
-        for i, j in enumerate(w.order):
-            kw = dict(reset=(i == 0), n_kv_heads=w.n_kv_heads, q_pos0=w.q_pos0, causal=w.causal)
+    def step(timer=None):
+        for i, j in enumerate(visible):
+            e0 = timer.start() if timer else None
             if i < last:
-                ba.fwd_block(qd, blocks, [j], st, **kw)
+                ba.fwd_block(qd, blocks, [j], st, reset=(i == 0), **kw)
             else:
-                ba.fwd_block_finalize(qd, blocks, [j], st, out=out, lse=lse, **kw)
+                ba.fwd_block_finalize(qd, blocks, [j], st, reset=(i == 0), out=out, lse=lse, **kw)
+            if timer:
+                timer.stop(e0)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    timer = Timer(torch)
     t0 = time.perf_counter()
     for _ in range(steps):
-        step()
+        step(timer)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
-    tf = w.flops() / ms / 1e9
-    log(f"ring share: {ms:.2f} ms/step, {tf:.1f} TFLOP/s")
-    return {"workload": w.name, "ms_per_step": round(ms, 3), "TFLOP/s": round(tf, 1),
-            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "visits": len(w.order),
-            "calls": "one call per visit, state carried in HBM; the last call finalises"}
+    launches = np.array(timer.all_ms()).reshape(steps, len(visible))
+    kernel_ms_step = float(launches.sum(axis=1).mean())
+    flops = w.flops()
+    tf = flops / ms / 1e9
+    ktf = flops / kernel_ms_step / 1e9
+    log(f"ring share: {ms:.2f} ms/step, {len(visible)} launches {kernel_ms_step:.2f} ms, {tf:.1f} TFLOP/s "
+        f"(kernels {ktf:.1f})")
+    return dict(q=q, k=k, v=v, out=out, lse=lse, step=step, ms_step=ms, kernel_ms_step=kernel_ms_step,
+                launch_ms_mean=float(launches.mean()), launch_ms_by_visit=launches.mean(axis=0).tolist(),
+                flops=flops, visible=visible, skipped=skipped, sha=sha)
 
 
 class Flusher:
@@ -314,10 +376,12 @@ def bench_fanout(torch, ba, H, w, steps, warmup):
     ms = timer.median_ms()
     gbs = w.bytes() / ms / 1e6
     log(f"fanout: {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
-    return {"workload": w.name, "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
-            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": w.bytes(),
-            "traffic_attention_kernel": traffic_record("fanout_kernel_fanout_decode"),
-            "timing": "median over steps, HIP events around the call, 1 GiB read between calls evicts the caches"}
+    res = {"workload": w.name, "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+           "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": w.bytes(),
+           "traffic_attention_kernel": traffic_record("fanout_kernel_fanout_decode"),
+           "timing": "median over steps, HIP events around the call, 1 GiB read between calls evicts the caches",
+           "input_sha256": input_sha256(ins, FANOUT_NAMES)}
+    return dict(result=res, ins=ins, out=out, lse=lse)
 
 
 def bench_fanout_paged(torch, ba, H, w, steps, warmup, page_len=256):
@@ -396,9 +460,10 @@ def bench_shard_merge(torch, ba, H, w, steps, warmup):
     gbs = w.sweep_bytes() / ms / 1e6
     merge_us = t_merge.median_ms() * 1e3
     log(f"shard merge: sweep {ms * 1e3:.1f} us ({gbs:.0f} GB/s), 32-way merge {merge_us:.1f} us")
-    return {"workload": w.name, "sweep_us": round(ms * 1e3, 2), "sweep_GB/s": round(gbs, 1),
-            "sweep_frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "merge_us": round(merge_us, 2),
-            "merge_bytes": w.merge_bytes()}
+    res = {"workload": w.name, "sweep_us": round(ms * 1e3, 2), "sweep_GB/s": round(gbs, 1),
+           "sweep_frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "merge_us": round(merge_us, 2),
+           "merge_bytes": w.merge_bytes(), "input_sha256": input_sha256((q, k, v))}
+    return dict(result=res, q=q, k=k, v=v, out=out, lse=lse)
 
 
 def bench_merge_scaled(torch, ba, steps, warmup, n_parts=32, rows=131072, D=128):
@@ -568,32 +633,150 @@ def gemm_reference(torch, steps, n=8192):
             "TFLOP/s": round(tf, 1), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
 
 
-def cpu_baseline(w, q, k, v, budget_s):
-    """The oracle, as it stands, on a bounded sample of query tokens of the headline workload."""
+def blas_threads():
     from threadpoolctl import threadpool_info
+    return int(max([t.get("num_threads", 1) for t in threadpool_info() if t.get("user_api") == "blas"] or [1]))
 
+
+def errors(got, ref):
+    d = np.abs(np.asarray(got, dtype=np.float64) - np.asarray(ref, dtype=np.float64))
+    return {"max_abs": float(d.max()), "mean_abs": float(d.mean())}
+
+
+def lse_errors(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    both_inf = np.isinf(got) & np.isinf(ref) & (np.sign(got) == np.sign(ref))
+    with np.errstate(invalid="ignore"):
+        d = np.where(both_inf, 0.0, np.abs(got - ref))
+    return float(d.max())
+
+
+def oracle_sampled(w, q, k, v, out, lse, fixed_tokens, budget_s, seed):
+    """The oracle (fp64 NumPy, as it stands) on sampled query tokens of a blockwise
+    workload, every query head of each: the tokens in ``fixed_tokens`` first,
+    then seeded random ones, 8 at a time, until ``budget_s`` seconds of oracle
+    time are spent.  Returns the oracle's rate (algorithmic FLOP of the sampled
+    rows over its time), the extrapolated time of the whole block, and the
+    GPU output's errors on the sampled rows."""
     from exact_blockwise_long_amd import synth
     from oracle import attention as ora
 
-    g = np.random.Generator(np.random.PCG64(1234))
-    order = g.permutation(w.q_len)
-    k64 = synth.Tensor(k.storage, k.dtype).f64()
-    v64 = synth.Tensor(v.storage, v.dtype).f64()
-    done, flops = 0, 0.0
+    T, Hq, D = w.q_len, w.n_q_heads, w.head_dim
     t0 = time.perf_counter()
-    batch = 8
-    while time.perf_counter() - t0 < budget_s and done < w.q_len:
-        toks = np.sort(order[done:done + batch])
+    n_keys = min(w.kv_len, w.q_pos0 + T) if w.causal else w.kv_len   # keys past the last query are never visible
+    k64 = synth.Tensor(k.storage[:n_keys], k.dtype).f64()
+    v64 = synth.Tensor(v.storage[:n_keys], v.dtype).f64()
+    prep_s = time.perf_counter() - t0
+    g = np.random.Generator(np.random.PCG64(seed))
+    rest = [t for t in g.permutation(T) if t not in set(fixed_tokens)]
+    queue = list(fixed_tokens) + rest
+    got = out.float().cpu().numpy().reshape(T, Hq, D)
+    got_lse = lse.cpu().numpy().reshape(T, Hq)
+    done, flops, err_max, err_sum, err_n, lse_max = 0, 0.0, 0.0, 0.0, 0, 0.0
+    t0 = time.perf_counter()
+    while done < len(queue) and (time.perf_counter() - t0 < budget_s or done < len(fixed_tokens)):
+        toks = np.sort(np.asarray(queue[done:done + 8]))
         q64 = synth.Tensor(q.storage[toks], q.dtype).f64()
-        ora.attend(q64, k64, v64, w.scale, w.q_pos0 + toks, None, w.causal)
-        vis = np.minimum(w.kv_len, np.maximum(0, w.q_pos0 + toks + 1)) if w.causal else np.full(len(toks), w.kv_len)
-        flops += 4.0 * w.head_dim * w.n_q_heads * float(vis.sum())
+        a, _, _, l_ref = ora.attend(q64, k64, v64, w.scale, w.q_pos0 + toks, None, w.causal)
+        vis = np.clip(w.q_pos0 + toks + 1, 0, n_keys) if w.causal else np.full(len(toks), n_keys)
+        flops += 4.0 * D * Hq * float(vis.sum())
+        d = np.abs(got[toks] - a)
+        err_max = max(err_max, float(d.max()))
+        err_sum += float(d.sum())
+        err_n += d.size
+        lse_max = max(lse_max, lse_errors(got_lse[toks], l_ref))
         done += len(toks)
     el = time.perf_counter() - t0
-    threads = max([t.get("num_threads", 1) for t in threadpool_info() if t.get("user_api") == "blas"] or [1])
-    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {w.q_len} query tokens (all {w.n_q_heads} heads, every visible key) of the "
-                      f"headline workload, fp64 NumPy, {el:.1f} s; host has {os.cpu_count()} logical CPUs"}
+    rate = flops / el
+    return {"tokens": done, "rows": done * Hq, "oracle_s": round(el, 2), "convert_s": round(prep_s, 2),
+            "oracle_flops": flops, "oracle_TFLOP/s": rate / 1e12,
+            "extrapolated_full_s": round(w.flops() / rate, 1),
+            "errors": {"max_abs": err_max, "mean_abs": err_sum / max(err_n, 1), "lse_max_abs": lse_max}}
+
+
+def cpu_baseline(w, check):
+    """The line's cpu_baseline: the oracle's rate on the headline workload's sample."""
+    return {"value": round(check["oracle_TFLOP/s"], 6), "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{check['tokens']} of {w.q_len} query tokens ({check['rows']} (token, head) rows: tokens 0 "
+                      f"and {w.q_len - 1}, row-tile and key-tile edges, then seeded random ones; every visible key) "
+                      f"of the headline workload, fp64 NumPy, {check['oracle_s']:.1f} s; the whole block would "
+                      f"take {check['extrapolated_full_s']:.0f} s at this rate (extrapolated); host has "
+                      f"{os.cpu_count()} logical CPUs"}
+
+
+def bench_tiny(torch, ba, H, w, steps, warmup, check):
+    """The tiny fp32 workload: one fwd_block call over its 4 blocks in order
+    1, 2, 3, 0, then finalize (fp32), timed with HIP events; and its errors
+    against the oracle on every row (output, m, l, LSE)."""
+    q, k, v = w.make_inputs()
+    qd, kd, vd = H.to_device(q), H.to_device(k), H.to_device(v)
+    L = w.block_len
+    blocks = [(kd[b * L:(b + 1) * L], vd[b * L:(b + 1) * L], b * L) for b in range(w.n_blocks)]
+    st = ba.new_state(w.rows, w.head_dim)
+    out = torch.empty(w.rows, w.head_dim, dtype=torch.float32, device="cuda")
+    lse = torch.empty(w.rows, dtype=torch.float32, device="cuda")
+
+    def step():
+        ba.fwd_block(qd, blocks, w.order, st, reset=True, n_kv_heads=w.n_kv_heads, q_pos0=w.q_pos0, causal=w.causal)
+        ba.finalize(st, out=out, lse=lse)
+
+    for _ in range(warmup):
+        step()
+    timer = Timer(torch)
+    for _ in range(steps):
+        e0 = timer.start()
+        step()
+        timer.stop(e0)
+    torch.cuda.synchronize()
+    us = timer.median_ms() * 1e3
+    log(f"tiny exact f32: {us:.1f} us per fwd_block + finalize")
+    res = {"workload": w.name, "us": round(us, 2), "step": "fwd_block (4 blocks, order 1,2,3,0) + finalize, fp32",
+           "input_sha256": input_sha256((q, k, v))}
+    if check:
+        from oracle import attention as ora
+        t0 = time.perf_counter()
+        a, m, l, lse_ref = ora.attend(q.f64(), k.f64(), v.f64(), w.scale, w.q_pos0 + np.arange(w.q_len), None,
+                                      w.causal)
+        el = time.perf_counter() - t0
+        T, Hq, D = w.q_len, w.n_q_heads, w.head_dim
+        res["oracle"] = {"work": "full", "seconds": round(el, 3), "cores": blas_threads()}
+        res["errors"] = {"out": errors(out.cpu().numpy().reshape(T, Hq, D), a),
+                         "m_max_abs": float(np.abs(st[0].cpu().numpy().reshape(T, Hq) - m).max()),
+                         "l_max_rel": float((np.abs(st[1].cpu().numpy().reshape(T, Hq) - l) / l).max()),
+                         "lse_max_abs": lse_errors(lse.cpu().numpy().reshape(T, Hq), lse_ref)}
+    return res
+
+
+def check_fanout(w, r):
+    """The fan-out decode against the oracle on every branch and head (full work)."""
+    from oracle import attention as ora
+    q, pk, pv, sk, sv = r["ins"]
+    t0 = time.perf_counter()
+    a, lse_ref = ora.fanout_decode(q.f64(), pk.f64(), pv.f64(), sk.f64(), sv.f64(), w.scale)
+    el = time.perf_counter() - t0
+    out = r["out"].float().cpu().numpy()
+    lse = r["lse"].cpu().numpy()
+    return {"oracle": {"work": "full", "seconds": round(el, 2), "cores": blas_threads()},
+            "errors": dict(errors(out, a), lse_max_abs=lse_errors(lse, lse_ref))}
+
+
+def check_shard_merge(w, r):
+    """The sharded sweep, 32-way merge and finalize against the oracle on all 64 rows (full work)."""
+    from oracle import attention as ora
+    q, k, v = r["q"], r["k"], r["v"]
+    t0 = time.perf_counter()
+    a, _, _, lse_ref = ora.attend(q.f64(), k.f64(), v.f64(), w.scale)
+    el = time.perf_counter() - t0
+    nb, Hq, D = q.shape
+    out = r["out"].float().cpu().numpy().reshape(nb, Hq, D)
+    lse = r["lse"].cpu().numpy().reshape(nb, Hq)
+    return {"oracle": {"work": "full", "seconds": round(el, 2), "cores": blas_threads()},
+            "errors": dict(errors(out, a), lse_max_abs=lse_errors(lse, lse_ref))}
+
+
+def strip_private(d):
+    return {k: v for k, v in d.items() if not k.startswith("_")}
 
 
 def main():
@@ -602,12 +785,13 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="all",
-                    choices=["all", "causal_prefill", "ring_share", "fanout", "shard_merge", "merge_scaled",
-                             "layouts", "fanout_prefill", "fanout_paged", "backward", "copy_calibration",
-                             "gemm_reference"])
-    ap.add_argument("--no-cpu", action="store_true")
+                    choices=["all", "ring_share", "causal_prefill", "tiny_exact", "fanout", "shard_merge",
+                             "merge_scaled", "layouts", "fanout_prefill", "fanout_paged", "backward",
+                             "copy_calibration", "gemm_reference"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing and error checks")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle time on the headline workload's sample")
     ap.add_argument("--no-clock", action="store_true", help="skip the amd-smi clock sampling run")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -621,40 +805,51 @@ def main():
         sys.exit(3)
     from exact_blockwise_long_amd import blockattn as ba
     from exact_blockwise_long_amd import workloads as wl
-    from tests import helpers as H
     ba.load()
+    H = DevIO(ba)
     log(f"device: {torch.cuda.get_device_name(0)}; HIP runtime {ba.hip_runtimes_loaded()}")
+    check = not args.no_cpu
 
     secondary = {}
     only = args.workload
-    if only in ("ring_share",):
-        secondary["ring_share"] = bench_ring_share(torch, ba, H, wl.RING_SHARE, max(1, args.steps // 10), 1)
-    if only == "fanout":
-        secondary["fanout_decode"] = bench_fanout(torch, ba, H, wl.FANOUT_DECODE, args.steps, args.warmup)
-    if only == "shard_merge":
-        secondary["shard_merge"] = bench_shard_merge(torch, ba, H, wl.SHARD_MERGE, args.steps, args.warmup)
-    if only == "merge_scaled":
-        secondary["merge_scaled"] = bench_merge_scaled(torch, ba, args.steps, args.warmup)
-    if only == "fanout_prefill":
-        secondary["fanout_prefill"] = bench_fanout_prefill(torch, ba, H, wl.FANOUT_PREFILL, args.steps, args.warmup)
-    if only == "layouts":
-        secondary["causal_ring_layouts"] = bench_layouts(torch, ba, H, wl.CAUSAL_RING_LAYOUTS, max(1, args.steps // 10))
-    if only == "fanout_paged":
-        secondary["fanout_decode_paged"] = bench_fanout_paged(torch, ba, H, wl.FANOUT_DECODE, args.steps, args.warmup)
-    if only == "backward":
-        secondary["backward"] = bench_backward(torch, ba, H, wl.CAUSAL_PREFILL, args.steps, args.warmup)
-    if only == "copy_calibration":
-        secondary["copy_calibration"] = copy_calibration(torch, args.steps)
-    if only == "gemm_reference":
-        secondary["gemm_reference"] = gemm_reference(torch, args.steps)
-    if only not in ("all", "causal_prefill"):
+    if only not in ("all", "ring_share"):
+        if only == "causal_prefill":
+            r = bench_prefill(torch, ba, H, wl.CAUSAL_PREFILL, args.steps, args.warmup)
+            secondary["causal_prefill"] = r["result"]
+        if only == "tiny_exact":
+            secondary["tiny_exact"] = bench_tiny(torch, ba, H, wl.TINY_EXACT, args.steps, args.warmup, check)
+        if only == "fanout":
+            secondary["fanout_decode"] = bench_fanout(torch, ba, H, wl.FANOUT_DECODE, args.steps,
+                                                      args.warmup)["result"]
+        if only == "shard_merge":
+            secondary["shard_merge"] = bench_shard_merge(torch, ba, H, wl.SHARD_MERGE, args.steps,
+                                                         args.warmup)["result"]
+        if only == "merge_scaled":
+            secondary["merge_scaled"] = bench_merge_scaled(torch, ba, args.steps, args.warmup)
+        if only == "fanout_prefill":
+            secondary["fanout_prefill"] = bench_fanout_prefill(torch, ba, H, wl.FANOUT_PREFILL, args.steps,
+                                                               args.warmup)
+        if only == "layouts":
+            secondary["causal_ring_layouts"] = bench_layouts(torch, ba, H, wl.CAUSAL_RING_LAYOUTS,
+                                                             max(1, args.steps // 10))
+        if only == "fanout_paged":
+            secondary["fanout_decode_paged"] = bench_fanout_paged(torch, ba, H, wl.FANOUT_DECODE, args.steps,
+                                                                  args.warmup)
+        if only == "backward":
+            secondary["backward"] = bench_backward(torch, ba, H, wl.CAUSAL_PREFILL, args.steps, args.warmup)
+        if only == "copy_calibration":
+            secondary["copy_calibration"] = copy_calibration(torch, args.steps)
+        if only == "gemm_reference":
+            secondary["gemm_reference"] = gemm_reference(torch, args.steps)
         print(json.dumps({"metric": METRIC, "partial": only, "secondary": secondary}), flush=True)
         return
 
-    w = wl.CAUSAL_PREFILL
-    res = bench_prefill(torch, ba, H, w, args.steps, args.warmup)
+    # ---- headline: one GPU's ring share at 256K
+    w = wl.RING_SHARE
+    res = bench_ring_share(torch, ba, H, w, args.steps, args.warmup)
     value = res["flops"] / res["ms_step"] / 1e9
-    achieved = res["flops"] / res["kernel_ms"] / 1e9
+    achieved = res["flops"] / res["kernel_ms_step"] / 1e9
+    cnt = counters_record("walk_kernel_ring_share") or {}
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -668,15 +863,21 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1)*0.5, rounded to bf16)",
-        "config": {"workload": w.name, "q_tokens": w.q_len, "q_pos0": w.q_pos0, "kv_blocks": w.n_blocks,
-                   "block_len": w.block_len, "order": w.order, "n_q_heads": w.n_q_heads,
-                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "causal": w.causal,
-                   "algorithmic_flops_per_step": w.flops()},
-        "roofline": {"kernel": "walk_kernel<128> (bf16 fwd_block_finalize, one launch per step)", "bound": "mfma",
-                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_record("walk_kernel_causal_prefill"),
-                     "kernel_ms_mean": round(res["kernel_ms"], 4)},
+        "config": {"workload": w.name, "q_tokens": w.q_len, "q_pos0": w.q_pos0, "seq_len": w.kv_len,
+                   "kv_blocks": w.n_blocks, "block_len": w.block_len, "order": w.order,
+                   "calls_per_step": len(res["visible"]), "blocks_in_causal_future_no_call": res["skipped"],
+                   "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+                   "causal": w.causal, "state": "fp32 (m, l, O) in HBM between calls",
+                   "algorithmic_flops_per_step": w.flops(), "input_sha256": res["sha"]},
+        "roofline": {"kernel": f"walk_kernel<128> ({len(res['visible'])} launches per step, one per visit)",
+                     "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": cnt.get("hbm_bytes_per_launch"),
+                     "mfma_util_pct": cnt.get("mfma_util_pct"),
+                     "counters_source": "profiles/traffic.json walk_kernel_ring_share (rocprofv3 --pmc, matching "
+                                        "kernel sources)" if cnt else None,
+                     "kernel_ms_per_step": round(res["kernel_ms_step"], 4),
+                     "launch_ms_mean": round(res["launch_ms_mean"], 4),
+                     "achieved_is": "algorithmic FLOP per step / sum of the step's launch durations (HIP events)"},
     }
     if not args.no_clock:
         clk = sample_clock(torch, res["step"], 3.0)
@@ -685,24 +886,48 @@ def main():
             clk["peak_at_measured_clock"] = round(peak_clk, 1)
             clk["frac_at_measured_clock"] = round(achieved / peak_clk, 4)
             line["roofline"]["clock"] = clk
-    if not args.no_secondary and only == "all":
-        secondary["fanout_decode"] = bench_fanout(torch, ba, H, wl.FANOUT_DECODE, args.steps, args.warmup)
+    oracle_checks = {}
+    if check:
+        log("oracle on a sample of the headline workload")
+        fixed = [0, 31, 32, 127, 128, 8191, 8192, w.q_len - 33, w.q_len - 32, w.q_len - 1]
+        chk = oracle_sampled(w, res["q"], res["k"], res["v"], res["out"], res["lse"], fixed, args.cpu_budget, 1234)
+        oracle_checks["ring_share"] = chk
+        line["cpu_baseline"] = cpu_baseline(w, chk)
+        log(f"oracle: {chk['tokens']} tokens in {chk['oracle_s']} s, errors {chk['errors']}")
+    del res
+
+    if not args.no_secondary:
+        r = bench_prefill(torch, ba, H, wl.CAUSAL_PREFILL, args.steps, args.warmup)
+        secondary["causal_prefill"] = r["result"]
+        if check:
+            w2 = wl.CAUSAL_PREFILL
+            oracle_checks["causal_prefill"] = oracle_sampled(w2, r["q"], r["k"], r["v"], r["out"], r["lse"],
+                                                             [0, 4095], 8.0, 4321)
+        del r
+        secondary["tiny_exact"] = bench_tiny(torch, ba, H, wl.TINY_EXACT, args.steps, args.warmup, check)
+        r = bench_fanout(torch, ba, H, wl.FANOUT_DECODE, args.steps, args.warmup)
+        secondary["fanout_decode"] = r["result"]
+        if check:
+            secondary["fanout_decode"].update(check_fanout(wl.FANOUT_DECODE, r))
+        del r
         secondary["fanout_decode_paged"] = bench_fanout_paged(torch, ba, H, wl.FANOUT_DECODE, args.steps,
                                                                args.warmup)
         secondary["fanout_prefill"] = bench_fanout_prefill(torch, ba, H, wl.FANOUT_PREFILL, args.steps, args.warmup)
-        secondary["shard_merge"] = bench_shard_merge(torch, ba, H, wl.SHARD_MERGE, args.steps, args.warmup)
+        r = bench_shard_merge(torch, ba, H, wl.SHARD_MERGE, args.steps, args.warmup)
+        secondary["shard_merge"] = r["result"]
+        if check:
+            secondary["shard_merge"].update(check_shard_merge(wl.SHARD_MERGE, r))
+        del r
         secondary["merge_scaled"] = bench_merge_scaled(torch, ba, args.steps, args.warmup)
-        secondary["backward"] = bench_backward(torch, ba, H, w, args.steps, args.warmup)
-        secondary["ring_share"] = bench_ring_share(torch, ba, H, wl.RING_SHARE, 2, 1)
+        secondary["backward"] = bench_backward(torch, ba, H, wl.CAUSAL_PREFILL, args.steps, args.warmup)
         secondary["causal_ring_layouts"] = bench_layouts(torch, ba, H, wl.CAUSAL_RING_LAYOUTS, 2)
         ref = gemm_reference(torch, args.steps)
         ref["walk_kernel_vs_gemm"] = round(achieved / ref["TFLOP/s"], 4)
         secondary["gemm_reference"] = ref
     if secondary:
         line["secondary"] = secondary
-    if not args.no_cpu:
-        log("timing the CPU oracle on a sample")
-        line["cpu_baseline"] = cpu_baseline(w, res["q"], res["k"], res["v"], args.cpu_budget)
+    if oracle_checks:
+        line["oracle_checks"] = oracle_checks
     print(json.dumps(line), flush=True)
 
 

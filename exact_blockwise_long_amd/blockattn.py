@@ -243,6 +243,16 @@ def _check_blocks(blocks, n_kv_heads: int, head_dim: int, dtype):
                                  f"{tuple(t.shape)} {t.dtype}")
 
 
+def from_host(storage, bf16: bool, device="cuda") -> torch.Tensor:
+    """A host array as a device tensor: uint16 bf16 bit patterns become
+    bfloat16 (bf16=True), float32 values stay float32."""
+    import numpy as np
+    arr = np.ascontiguousarray(storage)
+    if bf16:
+        return torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(arr).to(device)
+
+
 def new_state(rows: int, head_dim: int, device="cuda", stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Uninitialised fp32 state buffers (m [rows], l [rows], o [rows, D])."""
     return (_empty(rows, torch.float32, device, stream),

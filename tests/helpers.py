@@ -5,6 +5,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
+from exact_blockwise_long_amd import blockattn as ba
 from exact_blockwise_long_amd import synth
 
 # Tolerances.  bf16 output: max abs 2e-2 and mean abs 2e-3.  fp32 path: 1e-5.
@@ -17,9 +18,7 @@ F32_TOL = 1e-5
 
 
 def to_device(t: synth.Tensor, device="cuda") -> torch.Tensor:
-    if t.dtype == "bf16":
-        return torch.from_numpy(np.ascontiguousarray(t.storage).view(np.int16)).view(torch.bfloat16).to(device)
-    return torch.from_numpy(np.ascontiguousarray(t.storage)).to(device)
+    return ba.from_host(t.storage, t.dtype == "bf16", device)
 
 
 def host(x: torch.Tensor) -> np.ndarray:
