@@ -57,20 +57,22 @@ def sources_digest() -> str:
     return h.hexdigest()
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", *sources(), "-o", tmp]
+def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
+    """Compile the library to ``out`` (the package's libblockattn.so by default);
+    ``extra_flags`` go to hipcc after the standard ones (e.g. -D tuning macros)."""
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, f"-I{INCLUDE}", *sources(), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    out = "\n".join(line for line in (res.stdout + res.stderr).splitlines()
+    log = "\n".join(line for line in (res.stdout + res.stderr).splitlines()
                     if "packed-fp32-ops' is not a recognized feature" not in line)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
-    if verbose and out.strip():
-        print(out)
-    os.replace(tmp, LIB)
-    return LIB
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{log}")
+    if verbose and log.strip():
+        print(log)
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
