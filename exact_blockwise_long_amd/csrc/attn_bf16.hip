@@ -385,9 +385,49 @@ __device__ inline PageIds load_page_ids(const int32_t* ids, int k0, int k1, int 
   return pi;
 }
 
+// Whether any page id of the range [k0, k1) is corrupt: neither a page of
+// the pool nor the hole marker -1.  Uniform over the workgroup.
+__device__ inline bool pages_corrupt(const PageIds& pi, int k0, int k1, int page_len, int n_pool) {
+  const int n = paged_segments(k0, k1, page_len);
+  const int lane = threadIdx.x & 63;
+  const bool bad = lane < n && (pi.lane_id < -1 || pi.lane_id >= n_pool);
+  bool any = __ballot(bad) != 0;
+  for (int i = 64; i < n && !any; ++i) {
+    const int id = pi.ids[pi.first + i];
+    any = id < -1 || id >= n_pool;
+  }
+  return __builtin_amdgcn_readfirstlane((int)any) != 0;
+}
+
+// The partial state that marks rows whose keys could not be read (a corrupt
+// page id): m = +inf, l = 1, O = NaN.  The log-sum-exp merge keeps it (every
+// other part gets weight exp(m_s - inf) = 0), so the finalised rows come out
+// as NaN with LSE +inf instead of a plausible result over a wrong key set.
+template <int D, int W>
+__device__ inline void store_corrupt(const QSide& qs, int f0, int f1, int g, float* ws_m, float* ws_l, float* ws_o,
+                                     int64_t row_base) {
+  const RowCtx rc = make_rowctx(qs, f0, f1, g);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const LaneRows lr = lane_rows(qs, rc, wave, lane);
+  const int lg = lane >> 4;
+  const float nan = __builtin_bit_cast(float, 0x7FC00000u);
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    if (!lr.valid[qb] || f0 + wave * 32 >= f1) continue;
+    const int64_t r = row_base + lr.srow[qb];
+    if (lg == 0) {
+      ws_m[r] = INFINITY;
+      ws_l[r] = 1.f;
+    }
+#pragma unroll
+    for (int db = 0; db < Cfg<D>::DB; ++db) *(f32x4*)(ws_o + r * D + 16 * db + 4 * lg) = f32x4{nan, nan, nan, nan};
+  }
+}
+
 // Segment i of the range: the piece of page first + i inside [k0, k1), at
-// positions pos_base + key.  A page id outside the pool gives an empty
-// segment (its keys are left out, nothing is read).
+// positions pos_base + key.  A page id of -1 (a hole) gives an empty segment:
+// its keys are left out and nothing is read.
 template <int D>
 __device__ inline Seg paged_seg(const FanoutArgs& a, const PageIds& pi, int k0, int k1, int i, int64_t pos_base) {
   const int PL = a.page_len;
@@ -465,6 +505,10 @@ __global__ __launch_bounds__(kWide ? 2 * kThreads : kThreads, kWide ? 1 : 2) voi
     const int k_end = min(k_off + a.chunk_len, a.prefix.n);
     if (a.prefix_pages) {
       const PageIds pi = load_page_ids(a.prefix_pages, k_off, k_end, a.page_len);
+      if (pages_corrupt(pi, k_off, k_end, a.page_len, a.n_pool_pages)) {
+        store_corrupt<D, W>(a.qs, f0, f1, g, a.ws_m, a.ws_l, a.ws_o, (int64_t)chunk * a.R);
+        return;
+      }
       partial_job_segs<D, kAux, W>(
           a.qs, f0, f1, g, paged_segments(k_off, k_end, a.page_len),
           [&](int i) { return paged_seg<D>(a, pi, k_off, k_end, i, 0); }, a.ws_m, a.ws_l, a.ws_o,
@@ -505,6 +549,10 @@ __global__ __launch_bounds__(kWide ? 2 * kThreads : kThreads, kWide ? 1 : 2) voi
     const int f1 = min(f0 + TR, (b + 1) * TG);
     if (a.suffix_pages) {
       const PageIds pi = load_page_ids(a.suffix_pages + (int64_t)b * a.suffix_pages_per_branch, 0, a.S, a.page_len);
+      if (pages_corrupt(pi, 0, a.S, a.page_len, a.n_pool_pages)) {
+        store_corrupt<D, W>(qs, f0, f1, g, a.ws_m, a.ws_l, a.ws_o, (int64_t)a.suffix_slot * a.R);
+        continue;
+      }
       partial_job_segs<D, kAux, W>(
           qs, f0, f1, g, paged_segments(0, a.S, a.page_len), [&](int i) { return paged_seg<D>(a, pi, 0, a.S, i, 0); },
           a.ws_m, a.ws_l, a.ws_o, (int64_t)a.suffix_slot * a.R, (lds_char*)lds);

@@ -47,9 +47,18 @@ __device__ inline void run_init(Run& r) {
 }
 
 // Fold one part into the running state.  A part with m = -inf contributes
-// nothing (its l and O are not used, so garbage there cannot leak in).
+// nothing (its l and O are not used, so garbage there cannot leak in).  A
+// part with m = +inf marks a row whose keys could not be read (the fan-out's
+// corrupt page ids): the row takes that part as it is (l = 1, O = NaN) and
+// ignores every other part, so it finalises to NaN with LSE +inf.
 __device__ inline void run_add(Run& r, float m, float l, const f32x4& o) {
-  if (m == -INFINITY) return;
+  if (m == -INFINITY || r.m == INFINITY) return;
+  if (m == INFINITY) {
+    r.m = m;
+    r.l = l;
+    r.o = o;
+    return;
+  }
   if (m > r.m) {
     const float a = exp_nat(r.m - m);  // 0 when r.m = -inf
     r.l = r.l * a + l;

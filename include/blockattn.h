@@ -217,8 +217,10 @@ size_t blockattn_shard_workspace_bytes(const ba_problem* p, const ba_kv_block* b
  * computed over a disjoint key set).  For every row r:
  *   m* = max_s m_s[r];  w_s = exp(m_s[r] - m*) (0 when m_s[r] = -inf);
  *   l* = sum_s w_s l_s[r];  o*[r,:] = sum_s w_s o_s[r,:].
- * Parts whose m is -inf contribute nothing and their o is not read.  Rows are
- * never combined with other rows.  `out` may be one of the parts (in place);
+ * Parts whose m is -inf contribute nothing and their o is not read.  A part
+ * whose m is +inf (the marker of rows whose keys could not be read, see
+ * ba_kv_pages) is passed through: the row takes that part's l and o and
+ * ignores the others.  Rows are never combined with other rows.  `out` may be one of the parts (in place);
  * it must not partially overlap any part.  1 <= n_parts <=
  * BLOCKATTN_MAX_MERGE_PARTS; merge more by merging merged states (the same
  * primitive at every level, [AHBM] s.3.5).  Errors: BA_ERR_NULL, BA_ERR_SHAPE. */
@@ -333,9 +335,13 @@ size_t fanout_prefill_workspace_bytes(const ba_fanout_prefill* f);
  * are DEVICE int32 arrays of at least ceil(prefix_len / page_len) and
  * n_branches * ceil(suffix_len / page_len) entries; the caller owns them and
  * must not change them until the call has run on its stream.  page_len is a
- * positive multiple of 64, so no 64-key tile straddles two pages.  A page id
- * outside [0, n_pool_pages) contributes no keys (its tokens are left out;
- * positions of the other tokens do not move). */
+ * positive multiple of 64, so no 64-key tile straddles two pages.  The id -1
+ * marks a hole: its tokens are left out and the other tokens keep their
+ * positions.  Any other id outside [0, n_pool_pages) is a corrupt table, which
+ * the host cannot see (the tables are device memory): no page is read through
+ * it, and every row whose keys it would name -- a branch's rows for a corrupt
+ * suffix id, every row for a corrupt prefix id -- comes out as NaN with LSE
+ * +inf, so the error shows instead of a result over a wrong key set. */
 typedef struct {
   const int32_t* prefix_pages;
   const int32_t* suffix_pages;

@@ -463,16 +463,20 @@ def fanout_prefill(q, prefix_k, prefix_v, suffix_k, suffix_v, scale):
 def page_gather(pool, pages, n, page_len, n_pool):
     """The tokens of a paged sequence ([AHBM] 3.1: a context is a page table
     over pages that are referenced, not copied).  Token t (0 <= t < n) is row
-    t % page_len of pool page pages[t // page_len]; a page id outside
-    [0, n_pool) holds no tokens (the reading taken: its tokens are left out and
-    no other token moves).  Returns (rows [m, ...], token indices [m]) in token
-    order."""
+    t % page_len of pool page pages[t // page_len].  Readings taken (the pages
+    say nothing about ids that name no page): the id -1 marks a hole, whose
+    tokens are left out while every other token keeps its position; any other
+    id outside [0, n_pool) is a corrupt table, an input error.  Returns
+    (rows [m, ...], token indices [m]) in token order."""
     rows, idx = [], []
     for t in range(n):
         pid = int(pages[t // page_len])
-        if 0 <= pid < n_pool:
-            rows.append(np.asarray(pool[pid][t % page_len], dtype=np.float64))
-            idx.append(t)
+        if pid == -1:
+            continue
+        if not 0 <= pid < n_pool:
+            raise ValueError(f"page id {pid} names no page of a pool of {n_pool}")
+        rows.append(np.asarray(pool[pid][t % page_len], dtype=np.float64))
+        idx.append(t)
     shape = np.asarray(pool).shape[2:]
     return (np.stack(rows) if rows else np.zeros((0,) + tuple(shape))), np.asarray(idx, dtype=np.int64)
 

@@ -358,8 +358,9 @@ def _pages_of(x, page_len):
 
 def pin_fanout_paged():
     """Paged fan-out: pages scattered over a pool in a random order give the
-    contiguous fan-out prefill exactly; a prefix page with an id outside the
-    pool gives the prefill over the prefix with that page's tokens removed."""
+    contiguous fan-out prefill exactly; a prefix page id of -1 (a hole) gives
+    the prefill over the prefix with that page's tokens removed; any other id
+    outside the pool is rejected as a corrupt table."""
     g = _rng(97)
     nb, T, Hq, Hkv, D, P, S, PL = 2, 3, 4, 2, 8, 10, 6, 4
     q = g.standard_normal((nb, T, Hq, D))
@@ -392,13 +393,21 @@ def pin_fanout_paged():
     ra, rlse = ora.fanout_prefill(q, pk, pv, sk, sv, s)
     _close(a, ra, 1e-13, 1e-14, "paged vs contiguous")
     _close(lse, rlse, 1e-13, 0, "paged vs contiguous lse")
-    bad = list(prefix_pages)
-    bad[1] = n_pool + 5
-    a2, lse2 = ora.fanout_paged(q, k_pool, v_pool, bad, suffix_pages, PL, P, S, s)
+    hole = list(prefix_pages)
+    hole[1] = -1
+    a2, lse2 = ora.fanout_paged(q, k_pool, v_pool, hole, suffix_pages, PL, P, S, s)
     keep = np.r_[0:PL, 2 * PL:P]
     ra2, rlse2 = ora.fanout_prefill(q, pk[keep], pv[keep], sk, sv, s)
-    _close(a2, ra2, 1e-13, 1e-14, "paged with a page outside the pool")
-    _close(lse2, rlse2, 1e-13, 0, "paged with a page outside the pool lse")
+    _close(a2, ra2, 1e-13, 1e-14, "paged with a hole page")
+    _close(lse2, rlse2, 1e-13, 0, "paged with a hole page lse")
+    for bad_id in (n_pool, n_pool + 5, -2):
+        bad = list(prefix_pages)
+        bad[1] = bad_id
+        try:
+            ora.fanout_paged(q, k_pool, v_pool, bad, suffix_pages, PL, P, S, s)
+        except ValueError:
+            continue
+        raise AssertionError(f"page id {bad_id} outside the pool was accepted")
 
 
 def _loss_and_grads_fd(q, k, v, d_out, scale, q_pos, k_pos, causal, eps=1e-6):

@@ -372,10 +372,10 @@ def test_fanout_prefill(nb, T, Hq, Hkv, D, P, S):
 
 # ---------------------------------------------------------------- paged fan-out
 
-# (seed, nb, T, Hq, Hkv, D, P, S, page_len, out_of_pool): T = 1 goes through the
+# (seed, nb, T, Hq, Hkv, D, P, S, page_len, holes): T = 1 goes through the
 # decode entry point, T > 1 through the prefill one.  Pages sit at random pool
-# pages among noise pages; the last prefix page and suffix pages are partial.
-# out_of_pool lists (table, index) entries set to an id outside the pool.
+# pages among poisoned pages; the last prefix page and suffix pages are
+# partial.  holes lists (table, index) entries set to the hole marker -1.
 PAGED_CASES = [
     (61, 3, 1, 8, 2, 128, 1000, 37, 64, []),
     (62, 2, 20, 64, 8, 128, 700, 90, 128, []),
@@ -401,14 +401,14 @@ def paged_inputs(seed, nb, T, Hq, Hkv, D, P, S, PL):
 @pytest.mark.parametrize("case", PAGED_CASES, ids=lambda c: f"seed{c[0]}")
 def test_fanout_paged(case):
     seed, nb, T, Hq, Hkv, D, P, S, PL, bad = case
-    announce(f"paged fanout nb={nb} T={T} Hq={Hq} Hkv={Hkv} D={D} P={P} S={S} page_len={PL} out_of_pool={bad} "
+    announce(f"paged fanout nb={nb} T={T} Hq={Hq} Hkv={Hkv} D={D} P={P} S={S} page_len={PL} holes={bad} "
              f"seed {seed}")
     q, pk, pv, sk, sv, n_pool, pp, sp, k_pool, v_pool = paged_inputs(seed, nb, T, Hq, Hkv, D, P, S, PL)
     for table, i in bad:
         if table == "prefix":
-            pp[i] = n_pool + 7
+            pp[i] = -1
         else:
-            sp[i] = -3
+            sp[i] = -1
     kd, vd = H.to_device(k_pool), H.to_device(v_pool)
     ppd = torch.from_numpy(pp).cuda() if P else None
     spd = torch.from_numpy(sp).cuda() if S else None
@@ -433,6 +433,45 @@ def test_fanout_paged(case):
             o2, l2 = ba.fanout_prefix_prefill(qd, *dev)
         torch.cuda.synchronize()
         assert torch.equal(out, o2) and torch.equal(lse, l2), "paged differs from contiguous"
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_fanout_paged_corrupt_page_ids_give_nan_rows(T):
+    """A page id that is neither a pool page nor the hole marker -1 cannot be
+    checked on the host (the tables are device memory).  The rows whose keys
+    it would name come out as NaN with LSE +inf -- a corrupt suffix page only
+    its branch's rows, a corrupt prefix page every row -- and every other row
+    is the oracle's."""
+    seed, nb, Hq, Hkv, D, P, S, PL = 66, 4, 16, 2, 128, 700, 150, 64
+    announce(f"paged fanout with corrupt page ids: nb={nb} T={T} P={P} S={S} page_len={PL} seed {seed}")
+    q, pk, pv, sk, sv, n_pool, pp, sp, k_pool, v_pool = paged_inputs(seed, nb, T, Hq, Hkv, D, P, S, PL)
+    kd, vd = H.to_device(k_pool), H.to_device(v_pool)
+    qd = H.to_device(q)
+
+    def run(ppt, spt):
+        ppd, spd = torch.from_numpy(ppt).cuda(), torch.from_numpy(spt).cuda()
+        if T == 1:
+            o, l = ba.fanout_prefix_decode_paged(qd[:, 0].contiguous(), kd, vd, ppd, spd, P, S)
+            o, l = o[:, None], l[:, None]
+        else:
+            o, l = ba.fanout_prefix_prefill_paged(qd, kd, vd, ppd, spd, P, S)
+        torch.cuda.synchronize()
+        return H.host(o), H.host(l)
+
+    a_ref, lse_ref = ora.fanout_paged(q.f64(), k_pool.f64(), v_pool.f64(), pp, sp, PL, P, S, 1.0 / np.sqrt(D))
+    # a corrupt suffix page of branch 2 (an id past the pool)
+    sp_bad = sp.copy()
+    sp_bad[2, 1] = n_pool + 3
+    out, lse = run(pp, sp_bad)
+    assert np.isnan(out[2]).all() and np.isposinf(lse[2]).all(), "branch 2's rows are not marked"
+    others = [b for b in range(nb) if b != 2]
+    H.assert_bf16_out(out[others], a_ref[others], "other branches")
+    H.assert_close(lse[others], lse_ref[others], H.BF16_LSE, "other branches lse")
+    # a corrupt prefix page (a negative id other than -1): every row
+    pp_bad = pp.copy()
+    pp_bad[3] = -7
+    out, lse = run(pp_bad, sp)
+    assert np.isnan(out).all() and np.isposinf(lse).all(), "rows of a corrupt prefix are not marked"
 
 
 def test_fanout_prefill_one_token_is_the_decode():
