@@ -877,6 +877,7 @@ def main():
                                         "kernel sources)" if cnt else None,
                      "kernel_ms_per_step": round(res["kernel_ms_step"], 4),
                      "launch_ms_mean": round(res["launch_ms_mean"], 4),
+                     "launch_ms_by_visit": [round(x, 4) for x in res["launch_ms_by_visit"]],
                      "achieved_is": "algorithmic FLOP per step / sum of the step's launch durations (HIP events)"},
     }
     if not args.no_clock:
@@ -896,7 +897,7 @@ def main():
         log(f"oracle: {chk['tokens']} tokens in {chk['oracle_s']} s, errors {chk['errors']}")
     del res
 
-    if not args.no_secondary:
+    if not args.no_secondary and only == "all":
         r = bench_prefill(torch, ba, H, wl.CAUSAL_PREFILL, args.steps, args.warmup)
         secondary["causal_prefill"] = r["result"]
         if check:
