@@ -60,7 +60,7 @@ __device__ inline void tile_compute(const lds_char* stage, int lane, const bf16x
   constexpr int NKB = TK / 16;
   constexpr int NCH = TK / 32;
   const lds_char* kl = stage;
-  const lds_char* vl = stage + C::TILEB;
+  const lds_char* vl = v_tile_of<D, TK>(stage);
   const int lr = lane & 15;
   const int lg = lane >> 4;
 

@@ -84,7 +84,7 @@ __device__ inline void dq_tile(const lds_char* stage, int lane, const bf16x8 (&q
                                int n_valid, int krel, const int (&qrel)[2]) {
   using C = Cfg<D>;
   const lds_char* kl = stage;
-  const lds_char* vl = stage + C::TILEB;
+  const lds_char* vl = v_tile_of<D, kTileKeys>(stage);
   const int lr = lane & 15;
   const int lg = lane >> 4;
 #pragma unroll

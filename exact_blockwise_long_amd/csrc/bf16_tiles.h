@@ -32,7 +32,7 @@ struct Cfg {
   static constexpr int ROWB = D * 2;                  // bytes per K or V row in LDS
   static constexpr int CPR = D / 8;                   // 16-byte chunks per row
   static constexpr int TILEB = TK * ROWB;             // bytes of one K (or V) tile
-  static constexpr int STAGEB = 2 * TILEB;            // K tile then V tile
+  static constexpr int STAGEB = 2 * TILEB;            // one stage: a K tile and a V tile
   static constexpr int RPI = 64 / CPR;                // rows per wave-wide 1 KiB load
   static constexpr int LPW = TK / RPI / W;            // loads per wave per tile (each of K and V)
   static constexpr int DC = D / 32;                   // 32-wide d chunks (QK^T K-dim steps)
@@ -159,11 +159,11 @@ __device__ inline LaneOffs<D, W, TK> lane_offsets(const KVSrc& src, int wave, in
 // end at the last byte of key n_read - 1, and the scalar offset is 0, so the
 // range check covers every lane's whole offset.  Rows at or past n_read load
 // zeros without touching memory; their scores are masked, so their P is
-// exactly 0 and 0 * V adds nothing.  `stage` is the LDS byte address of the
-// stage.
+// exactly 0 and 0 * V adds nothing.  `kdst` and `vdst` are the LDS byte
+// addresses of the stage's K and V tiles.
 template <int D, int kAux = kCacheReuse, int W = 4, int TK = kTileKeys>
 __device__ inline void issue_tile(const KVSrc& src, const LaneOffs<D, W, TK>& offs, int k0, int n_read,
-                                  uint32_t stage, int wave) {
+                                  uint32_t kdst, uint32_t vdst, int wave) {
   using C = Cfg<D, W, TK>;
   const __amdgpu_buffer_rsrc_t rk =
       make_rsrc(src.kb + (uint32_t)k0 * src.kst, tile_records<D>(n_read, k0, src.kst));
@@ -172,9 +172,15 @@ __device__ inline void issue_tile(const KVSrc& src, const LaneOffs<D, W, TK>& of
 #pragma unroll
   for (int j = 0; j < C::LPW; ++j) {
     const uint32_t rbase = (uint32_t)((wave * C::LPW + j) * C::RPI);
-    lds_dma16<kAux>(rk, stage + rbase * C::ROWB, offs.k[j], 0);
-    lds_dma16<kAux>(rv, stage + C::TILEB + rbase * C::ROWB, offs.v[j], 0);
+    lds_dma16<kAux>(rk, kdst + rbase * C::ROWB, offs.k[j], 0);
+    lds_dma16<kAux>(rv, vdst + rbase * C::ROWB, offs.v[j], 0);
   }
+}
+
+// The V tile of the stage whose K tile is at `kl` (run_segments' layout).
+template <int D, int TK>
+__device__ inline const lds_char* v_tile_of(const lds_char* kl) {
+  return kl - 2 * Cfg<D, 4, TK>::TILEB;
 }
 
 // Number of keys of segment `s` that some row of the tile can see.
@@ -222,8 +228,14 @@ __device__ inline void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: 
 // Segment bookkeeping (visible key count, buffer resources, per-lane offsets)
 // runs only when a cursor crosses into another segment.
 //
+// LDS layout: the two stages' V tiles first, then their K tiles (V of stage s
+// at s * TILEB, K of stage s at (2 + s) * TILEB), so every transposing read
+// of a V tile addresses from a per-lane base with an immediate offset below
+// 64 KiB that folds in the stage, the key chunk and the row half.
+//
 // `tile(stage, need_mask, n_valid, krel)` computes one tile for the calling
-// wave: `stage` is the LDS address of the tile's K (V follows at TILEB);
+// wave: `stage` is the LDS address of the tile's K (its V is at stage -
+// 2 * TILEB, see kv_tiles);
 // keys at or past n_valid are invalid and, for causal problems, key kk sits
 // at position krel + kk relative to the tile's first query.  It runs only in
 // waves that own rows.
@@ -256,8 +268,9 @@ __device__ inline void run_segments(const QSide& qs, const RowCtx& rc, int n_seg
   int64_t cpos0 = get_seg(cs).pos0;
 
   const uint32_t lds_addr = (uint32_t)(size_t)lds;
-  auto issue_next = [&](int stage_off) {
-    issue_tile<D, kAux, W, TK>(isrc, ilo, ik, is_n, lds_addr + (uint32_t)stage_off, wave);
+  auto issue_next = [&](int stage) {
+    issue_tile<D, kAux, W, TK>(isrc, ilo, ik, is_n, lds_addr + (uint32_t)((2 + stage) * C::TILEB),
+                               lds_addr + (uint32_t)(stage * C::TILEB), wave);
     ik += TK;
     if (ik >= is_n) {
       is = next_nonempty(is + 1, is_n);
@@ -270,10 +283,10 @@ __device__ inline void run_segments(const QSide& qs, const RowCtx& rc, int n_seg
   };
 
   // One tile: wait for it, let the next one start loading, multiply.
-  auto step = [&](int cur_off, int nxt_off) {
+  auto step = [&](int cur, int nxt) {
     wait_all_loads();
     __syncthreads();
-    if (is < n_seg) issue_next(nxt_off);
+    if (is < n_seg) issue_next(nxt);
     if (wave_active) {
       const int n_valid = min(TK, cn - ck);
       const int64_t kpos0 = cpos0 + ck;
@@ -282,7 +295,7 @@ __device__ inline void run_segments(const QSide& qs, const RowCtx& rc, int n_seg
       // whenever a mask is needed; far-past tiles are clamped (never masked).
       const int64_t krel64 = kpos0 - rc.qpos_min;
       const int krel = (int)max((int64_t)-(1 << 30), min((int64_t)(1 << 30), krel64));
-      tile(lds + cur_off, need_mask, n_valid, krel);
+      tile(lds + (2 + cur) * C::TILEB, need_mask, n_valid, krel);
     }
     ck += TK;
     if (ck >= cn) {
@@ -294,9 +307,9 @@ __device__ inline void run_segments(const QSide& qs, const RowCtx& rc, int n_seg
 
   issue_next(0);
   while (true) {
-    step(0, C::STAGEB);
+    step(0, 1);
     if (cs >= n_seg) break;
-    step(C::STAGEB, 0);
+    step(1, 0);
     if (cs >= n_seg) break;
   }
   // Leave no load in flight into LDS that a later phase might reuse.
