@@ -235,7 +235,7 @@ __device__ inline void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: 
 //
 // `tile(stage, need_mask, n_valid, krel)` computes one tile for the calling
 // wave: `stage` is the LDS address of the tile's K (its V is at stage -
-// 2 * TILEB, see kv_tiles);
+// 2 * TILEB, see v_tile_of);
 // keys at or past n_valid are invalid and, for causal problems, key kk sits
 // at position krel + kk relative to the tile's first query.  It runs only in
 // waves that own rows.
