@@ -40,7 +40,7 @@ class Problem(ctypes.Structure):
         ("q_len", ctypes.c_int32), ("q_pos0", ctypes.c_int64),
         ("q_stride_token", ctypes.c_int64), ("q_stride_head", ctypes.c_int64),
         ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("causal", ctypes.c_int32),
-        ("split_mode", ctypes.c_int32),
+        ("split_mode", ctypes.c_int32), ("batch", ctypes.c_int32), ("q_stride_batch", ctypes.c_int64),
     ]
 
 
@@ -49,6 +49,7 @@ class KVBlock(ctypes.Structure):
         ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("len", ctypes.c_int32), ("pos0", ctypes.c_int64),
         ("k_stride_token", ctypes.c_int64), ("k_stride_head", ctypes.c_int64),
         ("v_stride_token", ctypes.c_int64), ("v_stride_head", ctypes.c_int64),
+        ("k_stride_batch", ctypes.c_int64), ("v_stride_batch", ctypes.c_int64),
     ]
 
 
@@ -216,9 +217,28 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def _dim_contig(t: torch.Tensor, name: str):
-    if t.dim() != 3 or t.stride(2) != 1:
-        raise ValueError(f"{name} must be [tokens, heads, head_dim] with a contiguous head_dim axis")
+def _dim_contig(t: torch.Tensor, name: str, batched: bool = False):
+    if t.dim() != (4 if batched else 3) or t.stride(-1) != 1:
+        shape = "[batch, tokens, heads, head_dim]" if batched else "[tokens, heads, head_dim]"
+        raise ValueError(f"{name} must be {shape} with a contiguous head_dim axis")
+
+
+def _qshape(q: torch.Tensor):
+    """(batch, q_len, n_q_heads, head_dim, batched) of a query block: [T, Hq, D]
+    is one sequence, [B, T, Hq, D] a batch of B sequences."""
+    if q.dim() == 3:
+        T, Hq, D = q.shape
+        return 1, T, Hq, D, False
+    if q.dim() == 4:
+        B, T, Hq, D = q.shape
+        return B, T, Hq, D, True
+    raise ValueError("q must be [tokens, heads, head_dim] or [batch, tokens, heads, head_dim]")
+
+
+def _rows(q: torch.Tensor) -> int:
+    """State rows of a query block: batch * q_len * n_q_heads."""
+    B, T, Hq, _, _ = _qshape(q)
+    return B * T * Hq
 
 
 def _check_state(state, rows: int, head_dim: int, name: str = "state"):
@@ -234,13 +254,18 @@ def _check_state(state, rows: int, head_dim: int, name: str = "state"):
         raise ValueError(f"{name}.o must be contiguous fp32 [>= {rows}, {head_dim}]")
 
 
-def _check_blocks(blocks, n_kv_heads: int, head_dim: int, dtype):
-    """Every K/V block must carry n_kv_heads heads of head_dim in the problem's dtype."""
+def _check_blocks(blocks, n_kv_heads: int, head_dim: int, dtype, batch: int = 1):
+    """Every K/V block must carry n_kv_heads heads of head_dim in the problem's
+    dtype: [len, Hkv, D], or [batch, len, Hkv, D] for a batched problem (a
+    3-D block is then shared by all its sequences)."""
     for i, (k, v, _) in enumerate(blocks):
         for t, n in ((k, "k"), (v, "v")):
-            if t.dim() != 3 or t.shape[1] != n_kv_heads or t.shape[2] != head_dim or t.dtype != dtype:
-                raise ValueError(f"block {i}: {n} must be [len, {n_kv_heads}, {head_dim}] {dtype}, got "
-                                 f"{tuple(t.shape)} {t.dtype}")
+            ok_shape = (t.dim() == 3 or (t.dim() == 4 and batch > 1 and t.shape[0] == batch)) and \
+                t.shape[-2] == n_kv_heads and t.shape[-1] == head_dim
+            if not ok_shape or t.dtype != dtype:
+                raise ValueError(f"block {i}: {n} must be [len, {n_kv_heads}, {head_dim}]"
+                                 f"{f' or [{batch}, len, {n_kv_heads}, {head_dim}]' if batch > 1 else ''} {dtype}, "
+                                 f"got {tuple(t.shape)} {t.dtype}")
 
 
 def from_host(storage, bf16: bool, device="cuda") -> torch.Tensor:
@@ -267,21 +292,30 @@ def _state(st) -> State:
 
 def make_problem(q: torch.Tensor, n_kv_heads: int, q_pos0: int = 0, causal: bool = False,
                  scale: float = 0.0, split_mode: int = 0) -> Problem:
-    _dim_contig(q, "q")
-    T, Hq, D = q.shape
-    return Problem(Hq, n_kv_heads, D, T, q_pos0, q.stride(0), q.stride(1), _dtype_code(q), scale,
-                   1 if causal else 0, split_mode)
+    """q [T, Hq, D] (one sequence) or [B, T, Hq, D] (a batch of B sequences)."""
+    B, T, Hq, D, batched = _qshape(q)
+    _dim_contig(q, "q", batched)
+    st = q.stride()
+    qsb, qst, qsh = (st[0], st[1], st[2]) if batched else (0, st[0], st[1])
+    return Problem(Hq, n_kv_heads, D, T, q_pos0, qst, qsh, _dtype_code(q), scale, 1 if causal else 0, split_mode,
+                   B if batched else 0, qsb)
 
 
 def make_blocks(blocks: Sequence[Tuple[torch.Tensor, torch.Tensor, int]]):
+    """Blocks (k, v, pos0), k and v [len, Hkv, D] or [batch, len, Hkv, D]; a 3-D
+    block has batch stride 0 (shared by the sequences of a batched problem)."""
     arr = (KVBlock * max(1, len(blocks)))()
     for i, (k, v, pos0) in enumerate(blocks):
-        _dim_contig(k, "k")
-        _dim_contig(v, "v")
+        batched = k.dim() == 4
+        _dim_contig(k, "k", batched)
+        _dim_contig(v, "v", batched)
         if k.shape != v.shape:
             raise ValueError("k and v blocks must have the same shape")
-        arr[i] = KVBlock(k.data_ptr(), v.data_ptr(), k.shape[0], pos0, k.stride(0), k.stride(1),
-                         v.stride(0), v.stride(1))
+        ks, vs = k.stride(), v.stride()
+        if batched:
+            arr[i] = KVBlock(k.data_ptr(), v.data_ptr(), k.shape[1], pos0, ks[1], ks[2], vs[1], vs[2], ks[0], vs[0])
+        else:
+            arr[i] = KVBlock(k.data_ptr(), v.data_ptr(), k.shape[0], pos0, ks[0], ks[1], vs[0], vs[1], 0, 0)
     return arr
 
 
@@ -292,9 +326,9 @@ def fwd_block(q: torch.Tensor, blocks: Sequence[Tuple[torch.Tensor, torch.Tensor
     """blockattn_fwd_block: walk ``blocks`` in ``order`` updating ``state`` (m, l, o) in place."""
     lib = load()
     p = make_problem(q, n_kv_heads, q_pos0, causal, scale, split_mode)
-    T, Hq, D = q.shape
-    _check_blocks(blocks, n_kv_heads, D, q.dtype)
-    _check_state(state, T * Hq, D)
+    B, T, Hq, D, _ = _qshape(q)
+    _check_blocks(blocks, n_kv_heads, D, q.dtype, B)
+    _check_state(state, B * T * Hq, D)
     arr = make_blocks(blocks)
     n_visit = len(order) if order is not None else len(blocks)
     order_arr = (ctypes.c_int32 * max(1, n_visit))(*(order or []))
@@ -319,9 +353,9 @@ def fwd_block_finalize(q: torch.Tensor, blocks: Sequence[Tuple[torch.Tensor, tor
     ``reset`` and left unspecified."""
     lib = load()
     p = make_problem(q, n_kv_heads, q_pos0, causal, scale, split_mode)
-    T, Hq, D = q.shape
-    rows = T * Hq
-    _check_blocks(blocks, n_kv_heads, D, q.dtype)
+    B, T, Hq, D, _ = _qshape(q)
+    rows = B * T * Hq
+    _check_blocks(blocks, n_kv_heads, D, q.dtype, B)
     _check_state(state, rows, D)
     if out is None:
         out = _empty((rows, D), out_dtype, q.device, stream)
@@ -364,12 +398,12 @@ def shard_states(q: torch.Tensor, blocks, states_out, *, n_kv_heads: int, q_pos0
     """blockattn_shard_states: one partial state per block into ``states_out``."""
     lib = load()
     p = make_problem(q, n_kv_heads, q_pos0, causal, scale, 0)
-    T, Hq, D = q.shape
-    _check_blocks(blocks, n_kv_heads, D, q.dtype)
+    B, T, Hq, D, _ = _qshape(q)
+    _check_blocks(blocks, n_kv_heads, D, q.dtype, B)
     if len(states_out) != len(blocks):
         raise ValueError("one output state per block")
     for i, st in enumerate(states_out):
-        _check_state(st, T * Hq, D, f"states_out[{i}]")
+        _check_state(st, B * T * Hq, D, f"states_out[{i}]")
     arr = make_blocks(blocks)
     sts = (State * max(1, len(blocks)))(*[_state(s) for s in states_out])
     need = lib.blockattn_shard_workspace_bytes(ctypes.byref(p), arr, len(blocks))
@@ -560,27 +594,30 @@ def bwd_block(q: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor, delta: tor
               blocks: Sequence[Tuple[torch.Tensor, torch.Tensor, int]], order: Optional[Sequence[int]],
               dq: torch.Tensor, dkv: Sequence[Tuple[torch.Tensor, torch.Tensor]], *, n_kv_heads: int,
               q_pos0: int = 0, causal: bool = False, scale: float = 0.0, stream=None):
-    """blockattn_bwd_block: accumulate dq [T*Hq, D] and each visited block's (dk, dv) [len, Hkv, D]
-    (all fp32) over the visits of one forward call.  dout has q's shape and strides (bf16)."""
+    """blockattn_bwd_block: accumulate dq [rows, D] and each visited block's (dk, dv) [len, Hkv, D]
+    ([batch, len, Hkv, D] for a batched q, one gradient per sequence), all fp32, over the visits
+    of one forward call.  dout has q's shape and strides (bf16)."""
     lib = load()
     if dout.shape != q.shape or dout.stride() != q.stride() or dout.dtype != torch.bfloat16:
         raise ValueError("dout must be bf16 with q's shape and strides")
     p = make_problem(q, n_kv_heads, q_pos0, causal, scale, 0)
-    T, Hq, D = q.shape
-    _check_blocks(blocks, n_kv_heads, D, q.dtype)
-    if dq.dtype != torch.float32 or not dq.is_contiguous() or dq.numel() != T * Hq * D:
-        raise ValueError("dq must be contiguous fp32 with q_len * n_q_heads * head_dim elements")
+    B, T, Hq, D, batched = _qshape(q)
+    _check_blocks(blocks, n_kv_heads, D, q.dtype, B)
+    rows = B * T * Hq
+    if dq.dtype != torch.float32 or not dq.is_contiguous() or dq.numel() != rows * D:
+        raise ValueError("dq must be contiguous fp32 with batch * q_len * n_q_heads * head_dim elements")
     for name, t in (("lse", lse), ("delta", delta)):
-        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != T * Hq:
-            raise ValueError(f"{name} must be contiguous fp32 with one entry per (token, query head)")
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != rows:
+            raise ValueError(f"{name} must be contiguous fp32 with one entry per (sequence, token, query head)")
     if len(dkv) != len(blocks):
         raise ValueError("one (dk, dv) pair per block")
     for (kb, _, _), (dk, dv) in zip(blocks, dkv):
-        want = (kb.shape[0], n_kv_heads, D)
+        n = kb.shape[-3]
+        want = (B, n, n_kv_heads, D) if batched else (n, n_kv_heads, D)
         if dk.dtype != torch.float32 or dv.dtype != torch.float32 or not dk.is_contiguous() or not dv.is_contiguous():
             raise ValueError("dk and dv must be contiguous fp32")
         if tuple(dk.shape) != want or tuple(dv.shape) != want:
-            raise ValueError(f"dk and dv of a block of {kb.shape[0]} keys must have shape {want}")
+            raise ValueError(f"dk and dv of a block of {n} keys must have shape {want}")
     arr = make_blocks(blocks)
     n_visit = len(order) if order is not None else len(blocks)
     order_arr = (ctypes.c_int32 * max(1, n_visit))(*(order or []))

@@ -47,6 +47,10 @@ constexpr int kMaxChunks = 8192;
 
 float resolve_scale(float s, int D) { return s > 0.f ? s : 1.0f / sqrtf((float)D); }
 
+// Sequences of a problem (batch 0 or 1: one) and its state rows.
+int batch_of(const ba_problem* p) { return p->batch > 1 ? p->batch : 1; }
+int64_t state_rows(const ba_problem* p) { return (int64_t)batch_of(p) * p->q_len * p->n_q_heads; }
+
 ba_status check_problem(const ba_problem* p, const void* q) {
   if (!p) return fail(BA_ERR_NULL, "problem is NULL");
   if (p->dtype != BA_F32 && p->dtype != BA_BF16) return fail(BA_ERR_UNSUPPORTED, "dtype %d", p->dtype);
@@ -56,13 +60,15 @@ ba_status check_problem(const ba_problem* p, const void* q) {
     return fail(BA_ERR_SHAPE, "n_q_heads %d must be a positive multiple of n_kv_heads %d", p->n_q_heads,
                 p->n_kv_heads);
   if (p->q_len < 0) return fail(BA_ERR_SHAPE, "q_len %d < 0", p->q_len);
-  if ((int64_t)p->q_len * p->n_q_heads > (int64_t)1 << 30) return fail(BA_ERR_SHAPE, "too many query rows");
+  if (p->batch < 0) return fail(BA_ERR_SHAPE, "batch %d < 0", p->batch);
+  if (state_rows(p) > (int64_t)1 << 30) return fail(BA_ERR_SHAPE, "too many query rows");
   if (p->q_len > 0) {
     if (!q) return fail(BA_ERR_NULL, "q is NULL");
     if (p->q_stride_token <= 0 || p->q_stride_head <= 0) return fail(BA_ERR_SHAPE, "q strides must be positive");
+    if (p->batch > 1 && p->q_stride_batch <= 0) return fail(BA_ERR_SHAPE, "q_stride_batch must be positive");
     if (p->dtype == BA_BF16) {
       if (((uintptr_t)q % 16) != 0) return fail(BA_ERR_SHAPE, "q not 16-byte aligned");
-      if (p->q_stride_token % 8 != 0 || p->q_stride_head % 8 != 0)
+      if (p->q_stride_token % 8 != 0 || p->q_stride_head % 8 != 0 || (p->batch > 1 && p->q_stride_batch % 8 != 0))
         return fail(BA_ERR_SHAPE, "bf16 q strides must be multiples of 8 elements");
     }
   }
@@ -75,16 +81,21 @@ int64_t head_extent_bf16(int64_t len, int64_t stride_token, int head_dim) {
   return len <= 0 ? 0 : ((len - 1) * stride_token + head_dim) * 2;
 }
 
-ba_status check_block(const ba_kv_block& b, int i, int dtype, int head_dim) {
+ba_status check_block(const ba_kv_block& b, int i, const ba_problem* p) {
+  const int dtype = p->dtype, head_dim = p->head_dim;
+  const bool batched = p->batch > 1;
   if (b.len < 0) return fail(BA_ERR_SHAPE, "block %d: len %d < 0", i, b.len);
   if (b.len == 0) return BA_OK;
   if (!b.k || !b.v) return fail(BA_ERR_NULL, "block %d: k or v is NULL", i);
   if (b.k_stride_token <= 0 || b.k_stride_head <= 0 || b.v_stride_token <= 0 || b.v_stride_head <= 0)
     return fail(BA_ERR_SHAPE, "block %d: strides must be positive", i);
+  if (batched && (b.k_stride_batch < 0 || b.v_stride_batch < 0))
+    return fail(BA_ERR_SHAPE, "block %d: batch strides must be >= 0", i);
   if (dtype == BA_BF16) {
     if (((uintptr_t)b.k % 16) != 0 || ((uintptr_t)b.v % 16) != 0)
       return fail(BA_ERR_SHAPE, "block %d: k/v not 16-byte aligned", i);
-    if (b.k_stride_token % 8 || b.k_stride_head % 8 || b.v_stride_token % 8 || b.v_stride_head % 8)
+    if (b.k_stride_token % 8 || b.k_stride_head % 8 || b.v_stride_token % 8 || b.v_stride_head % 8 ||
+        (batched && (b.k_stride_batch % 8 || b.v_stride_batch % 8)))
       return fail(BA_ERR_SHAPE, "block %d: bf16 strides must be multiples of 8 elements", i);
     // The tile loads' range check ends a block after its last key only when
     // one key's row does not run into the next key's.
@@ -132,6 +143,8 @@ ba::QSide make_qside(const ba_problem* p, const void* q) {
   qs.q = q;
   qs.qs_t = p->q_stride_token;
   qs.qs_h = p->q_stride_head;
+  qs.B = batch_of(p);
+  qs.qs_b = qs.B > 1 ? p->q_stride_batch : 0;
   qs.q_pos0 = p->q_pos0;
   qs.Hq = p->n_q_heads;
   qs.Hkv = p->n_kv_heads;
@@ -142,7 +155,9 @@ ba::QSide make_qside(const ba_problem* p, const void* q) {
   return qs;
 }
 
-ba::Seg make_seg(const ba_kv_block& b) {
+// `batch`: the problem's sequences; the block's batch strides count only for
+// more than one.
+ba::Seg make_seg(const ba_kv_block& b, int batch) {
   ba::Seg s;
   s.k = b.k;
   s.v = b.v;
@@ -150,6 +165,8 @@ ba::Seg make_seg(const ba_kv_block& b) {
   s.ks_h = b.k_stride_head;
   s.vs_t = b.v_stride_token;
   s.vs_h = b.v_stride_head;
+  s.ks_b = batch > 1 ? b.k_stride_batch : 0;
+  s.vs_b = batch > 1 ? b.v_stride_batch : 0;
   s.pos0 = b.pos0;
   s.n = b.len;
   s.pad_ = 0;
@@ -167,7 +184,7 @@ int64_t usable_keys(const ba_problem* p, const ba_kv_block& b) {
 
 int row_tiles(const ba_problem* p) {
   int64_t flat = (int64_t)p->q_len * (p->n_q_heads / p->n_kv_heads);
-  return (int)((flat + ba::kTileRows - 1) / ba::kTileRows) * p->n_kv_heads;
+  return (int)((flat + ba::kTileRows - 1) / ba::kTileRows) * p->n_kv_heads * batch_of(p);
 }
 
 // Row tiling of a split launch.  More than one 128-row tile per KV head makes
@@ -186,7 +203,7 @@ SplitGeom split_geom(const ba_problem* p) {
   const int64_t narrow = (flat + ba::kTileRows - 1) / ba::kTileRows;
   sg.wide = BA_SPLIT_WIDE && narrow >= 2;
   const int64_t per_head = sg.wide ? (flat + ba::kWideTileRows - 1) / ba::kWideTileRows : narrow;
-  sg.tiles = (int)per_head * p->n_kv_heads;
+  sg.tiles = (int)per_head * p->n_kv_heads * batch_of(p);
   sg.target = sg.wide ? kTargetWorkgroups / 2 : kTargetWorkgroups;
   return sg;
 }
@@ -255,7 +272,7 @@ ba_status prepare_fwd(const ba_problem* p, const void* q, const ba_kv_block* blo
   st = resolve_order(n_blocks, order, n_visit, v);
   if (st) return st;
   for (int j : v.idx) {
-    st = check_block(blocks[j], j, p->dtype, p->head_dim);
+    st = check_block(blocks[j], j, p);
     if (st) return st;
   }
   split = fwd_uses_split(p);
@@ -317,7 +334,7 @@ ba_status fwd_run(const ba_problem* p, const void* q, const ba_kv_block* blocks,
     if (st) return st;
   }
   const int D = p->head_dim;
-  const int64_t R = (int64_t)p->q_len * p->n_q_heads;
+  const int64_t R = state_rows(p);
   const size_t need = split ? partial_bytes(sp.n_chunks, R, D) : 0;
   if (split && sp.n_chunks > 0) {
     if (!workspace || workspace_bytes < need)
@@ -337,7 +354,7 @@ ba_status fwd_run(const ba_problem* p, const void* q, const ba_kv_block* blocks,
     for (int j : v.idx) {
       // blocks no query of the block can see (causal future, or empty) are skipped
       if (usable_keys(p, blocks[j]) == 0) continue;
-      a.seg[a.n_seg++] = make_seg(blocks[j]);
+      a.seg[a.n_seg++] = make_seg(blocks[j], batch_of(p));
     }
     if (fin && p->dtype != BA_BF16) {
       // The fp32 walk keeps the state; finalisation follows as its own launch.
@@ -373,7 +390,7 @@ ba_status fwd_run(const ba_problem* p, const void* q, const ba_kv_block* blocks,
     a.wide = sp.wide ? 1 : 0;
     a.n_seg = (int)v.idx.size();
     for (int i = 0; i < a.n_seg; ++i) {
-      a.seg[i] = make_seg(blocks[v.idx[i]]);
+      a.seg[i] = make_seg(blocks[v.idx[i]], batch_of(p));
       a.chunk_begin[i] = sp.begin[i];
     }
     a.chunk_begin[a.n_seg] = sp.begin[a.n_seg];
@@ -434,7 +451,7 @@ size_t blockattn_fwd_workspace_bytes(const ba_problem* p, const ba_kv_block* blo
   if (prepare_fwd(p, p ? (const void*)256 : nullptr, blocks, n_blocks, order, n_visit, v, sp, split) != BA_OK)
     return 0;
   if (!split || p->q_len == 0) return 0;
-  return partial_bytes(sp.n_chunks, (int64_t)p->q_len * p->n_q_heads, p->head_dim);
+  return partial_bytes(sp.n_chunks, state_rows(p), p->head_dim);
 }
 
 ba_status blockattn_fwd_block(const ba_problem* p, const void* q, const ba_kv_block* blocks, int32_t n_blocks,
@@ -494,7 +511,7 @@ ba_status blockattn_bwd_block(const ba_problem* p, const void* q, const void* do
   st = resolve_order(n_blocks, order, n_visit, v);
   if (st) return st;
   for (int j : v.idx) {
-    st = check_block(blocks[j], j, p->dtype, p->head_dim);
+    st = check_block(blocks[j], j, p);
     if (st) return st;
   }
   if (p->q_len == 0 || v.idx.empty()) return ok();
@@ -502,11 +519,12 @@ ba_status blockattn_bwd_block(const ba_problem* p, const void* q, const void* do
   if (((uintptr_t)dout % 16) != 0 || ((uintptr_t)dq % 16) != 0) return fail(BA_ERR_SHAPE, "dout/dq not 16-byte aligned");
   if (!dk || !dv) return fail(BA_ERR_NULL, "dk or dv pointer array is NULL");
   const int D = p->head_dim;
-  const int64_t R = (int64_t)p->q_len * p->n_q_heads;
+  const int64_t R = state_rows(p);
   const int64_t q_extent =
       ((int64_t)(p->q_len - 1) * p->q_stride_token + (int64_t)(p->n_q_heads - 1) * p->q_stride_head + D) * 2;
-  if (q_extent > (int64_t)UINT32_MAX || R * 4 > (int64_t)UINT32_MAX)
-    return fail(BA_ERR_SHAPE, "the backward pass addresses q, dout, lse and delta with 32-bit offsets");
+  const int64_t seq_rows = (int64_t)p->q_len * p->n_q_heads;   // one sequence's lse and delta rows
+  if (q_extent > (int64_t)UINT32_MAX || seq_rows * 4 > (int64_t)UINT32_MAX)
+    return fail(BA_ERR_SHAPE, "the backward pass addresses a sequence's q, dout, lse and delta with 32-bit offsets");
   ba::BwdArgs a;
   memset(&a, 0, sizeof(a));
   a.qs = make_qside(p, q);
@@ -516,7 +534,7 @@ ba_status blockattn_bwd_block(const ba_problem* p, const void* q, const void* do
   a.dq = dq;
   a.scale = a.qs.c / ba::kLog2e;
   a.q_bytes = (uint32_t)q_extent;
-  a.rows_bytes = (uint32_t)(R * 4);
+  a.rows_bytes = (uint32_t)(seq_rows * 4);
   a.g_magic = 0xFFFFFFFFu / (uint32_t)a.qs.G;
   a.n_seg = 0;
   int tiles = 0;
@@ -531,7 +549,7 @@ ba_status blockattn_bwd_block(const ba_problem* p, const void* q, const void* do
     if (!dk[j] || !dv[j]) return fail(BA_ERR_NULL, "dk or dv of visited block %d is NULL", j);
     if (((uintptr_t)dk[j] % 16) != 0 || ((uintptr_t)dv[j] % 16) != 0)
       return fail(BA_ERR_SHAPE, "dk/dv of block %d not 16-byte aligned", j);
-    a.seg[a.n_seg] = make_seg(blocks[j]);
+    a.seg[a.n_seg] = make_seg(blocks[j], batch_of(p));
     a.dk[a.n_seg] = dk[j];
     a.dv[a.n_seg] = dv[j];
     a.tile_begin[a.n_seg] = tiles;
@@ -549,11 +567,11 @@ size_t blockattn_shard_workspace_bytes(const ba_problem* p, const ba_kv_block* b
   if (p->dtype != BA_BF16 || p->q_len == 0) return 0;
   std::vector<int64_t> keys;
   for (int i = 0; i < n_blocks; ++i) {
-    if (check_block(blocks[i], i, p->dtype, p->head_dim) != BA_OK) return 0;
+    if (check_block(blocks[i], i, p) != BA_OK) return 0;
     keys.push_back(usable_keys(p, blocks[i]));
   }
   SplitPlan sp = plan_split(keys, split_geom(p));
-  return partial_bytes(sp.n_chunks, (int64_t)p->q_len * p->n_q_heads, p->head_dim);
+  return partial_bytes(sp.n_chunks, state_rows(p), p->head_dim);
 }
 
 ba_status blockattn_shard_states(const ba_problem* p, const void* q, const ba_kv_block* blocks, int32_t n_blocks,
@@ -567,7 +585,7 @@ ba_status blockattn_shard_states(const ba_problem* p, const void* q, const ba_kv
   if (!blocks || !states_out) return fail(BA_ERR_NULL, "blocks or states_out is NULL");
   std::vector<int64_t> keys;
   for (int i = 0; i < n_blocks; ++i) {
-    st = check_block(blocks[i], i, p->dtype, p->head_dim);
+    st = check_block(blocks[i], i, p);
     if (st) return st;
     st = check_state(states_out[i], "states_out");
     if (st) return st;
@@ -575,7 +593,7 @@ ba_status blockattn_shard_states(const ba_problem* p, const void* q, const ba_kv
   }
   if (p->q_len == 0) return ok();
   const int D = p->head_dim;
-  const int64_t R = (int64_t)p->q_len * p->n_q_heads;
+  const int64_t R = state_rows(p);
   SplitPlan sp = plan_split(keys, split_geom(p));
   const size_t need = partial_bytes(sp.n_chunks, R, D);
   float *wm = nullptr, *wl = nullptr, *wo = nullptr;
@@ -595,7 +613,7 @@ ba_status blockattn_shard_states(const ba_problem* p, const void* q, const ba_kv
     a.wide = sp.wide ? 1 : 0;
     a.n_seg = n_blocks;
     for (int i = 0; i < n_blocks; ++i) {
-      a.seg[i] = make_seg(blocks[i]);
+      a.seg[i] = make_seg(blocks[i], batch_of(p));
       a.chunk_begin[i] = sp.begin[i];
     }
     a.chunk_begin[n_blocks] = sp.begin[n_blocks];
@@ -843,14 +861,14 @@ ba_status fanout_run(const FanoutShape& f, const void* q, const void* prefix_k, 
   ba::FanoutArgs a;
   memset(&a, 0, sizeof(a));
   a.qs = qs;
-  ba_kv_block b;
+  ba_kv_block b = {};
   b.k = prefix_k;
   b.v = prefix_v;
   b.len = f.P;
   b.pos0 = 0;
   b.k_stride_token = b.v_stride_token = (int64_t)f.Hkv * D;
   b.k_stride_head = b.v_stride_head = D;
-  a.prefix = make_seg(b);
+  a.prefix = make_seg(b, 1);
   a.row_tiles = fp.row_tiles;
   a.chunk_len = fp.chunk_len;
   a.n_chunks = fp.n_chunks;
@@ -963,7 +981,7 @@ size_t blockattn_workspace_bytes(const ba_problem* p, const ba_fanout* f) {
     const SplitGeom geom = split_geom(p);
     const int tiles = geom.tiles;
     const int64_t want = std::max<int64_t>(1, (geom.target + tiles - 1) / (tiles > 0 ? tiles : 1));
-    need = partial_bytes(want + BLOCKATTN_MAX_VISITS, (int64_t)p->q_len * p->n_q_heads, p->head_dim);
+    need = partial_bytes(want + BLOCKATTN_MAX_VISITS, state_rows(p), p->head_dim);
   }
   if (f && check_fanout(f) == BA_OK && f->n_branches > 0) need = std::max(need, fanout_bytes(decode_shape(f)));
   return need;

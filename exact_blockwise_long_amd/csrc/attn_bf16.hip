@@ -282,14 +282,18 @@ constexpr int kWalkKeys = 128;
 template <int D>
 __global__ __launch_bounds__(64 * kWalkWaves, 1) void walk_kernel(WalkArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[2 * Cfg<D, kWalkWaves, kWalkKeys>::STAGEB];
+  // Consecutive workgroups take the KV heads (each XCD keeps one head's K/V in
+  // its L2), then the sequences, then the row tiles, longest first.
   const int Hkv = a.qs.Hkv;
   const int g = blockIdx.x % Hkv;
+  const int rest = blockIdx.x / Hkv;
+  const int b = rest % a.qs.B;
   const int n_tiles = (a.qs.q_len * a.qs.G + kWalkRows - 1) / kWalkRows;
-  const int tile = n_tiles - 1 - (int)(blockIdx.x / Hkv);
+  const int tile = n_tiles - 1 - rest / a.qs.B;
   const int total = a.qs.q_len * a.qs.G;
   const int f0 = tile * kWalkRows;
   const int f1 = min(f0 + kWalkRows, total);
-  const RowCtx rc = make_rowctx(a.qs, f0, f1, g);
+  const RowCtx rc = make_rowctx(a.qs, f0, f1, g, b);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const LaneRows lr = lane_rows(a.qs, rc, wave, lane);
@@ -333,9 +337,9 @@ __device__ inline Seg chunk_seg(const Seg* seg, int n_seg, const int32_t* chunk_
 // Partial state of one row tile over the keys of n_seg segments (get_seg(i)
 // returns segment i), written to a workspace slot.
 template <int D, int kAux, int W = 4, int TK = kTileKeys, class GetSeg>
-__device__ inline void partial_job_segs(const QSide& qs, int f0, int f1, int g, int n_seg, GetSeg get_seg,
+__device__ inline void partial_job_segs(const QSide& qs, int f0, int f1, int g, int b, int n_seg, GetSeg get_seg,
                                         float* ws_m, float* ws_l, float* ws_o, int64_t row_base, lds_char* lds) {
-  const RowCtx rc = make_rowctx(qs, f0, f1, g);
+  const RowCtx rc = make_rowctx(qs, f0, f1, g, b);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const LaneRows lr = lane_rows(qs, rc, wave, lane);
@@ -354,10 +358,10 @@ __device__ inline void partial_job_segs(const QSide& qs, int f0, int f1, int g, 
 }
 
 template <int D, int kAux, int W = 4, int TK = kTileKeys>
-__device__ inline void partial_job(const QSide& qs, int f0, int f1, int g, const Seg& sg, float* ws_m,
+__device__ inline void partial_job(const QSide& qs, int f0, int f1, int g, int b, const Seg& sg, float* ws_m,
                                    float* ws_l, float* ws_o, int64_t row_base, lds_char* lds) {
-  partial_job_segs<D, kAux, W, TK>(qs, f0, f1, g, 1, [&](int) -> const Seg& { return sg; }, ws_m, ws_l, ws_o, row_base,
-                               lds);
+  partial_job_segs<D, kAux, W, TK>(qs, f0, f1, g, b, 1, [&](int) -> const Seg& { return sg; }, ws_m, ws_l, ws_o,
+                                   row_base, lds);
 }
 
 // The page ids of one job's key range [k0, k1) of a paged sequence whose
@@ -406,7 +410,7 @@ __device__ inline bool pages_corrupt(const PageIds& pi, int k0, int k1, int page
 template <int D, int W>
 __device__ inline void store_corrupt(const QSide& qs, int f0, int f1, int g, float* ws_m, float* ws_l, float* ws_o,
                                      int64_t row_base) {
-  const RowCtx rc = make_rowctx(qs, f0, f1, g);
+  const RowCtx rc = make_rowctx(qs, f0, f1, g, 0);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const LaneRows lr = lane_rows(qs, rc, wave, lane);
@@ -447,6 +451,8 @@ __device__ inline Seg paged_seg(const FanoutArgs& a, const PageIds& pi, int k0, 
   sg.vs_h = D;
   sg.pos0 = pos_base + s0;
   sg.n = ok ? s1 - s0 : 0;
+  sg.ks_b = 0;
+  sg.vs_b = 0;
   sg.pad_ = 0;
   return sg;
 }
@@ -461,13 +467,15 @@ __global__ __launch_bounds__(kWide ? 2 * kThreads : kThreads, kWide ? 1 : 2) voi
   __shared__ __attribute__((aligned(16))) char lds[2 * Cfg<D, W, TK>::STAGEB];
   const int Hkv = a.qs.Hkv;
   const int g = blockIdx.x % Hkv;
-  const int tile = blockIdx.x / Hkv;
+  const int rest = blockIdx.x / Hkv;
+  const int b = rest % a.qs.B;
+  const int tile = rest / a.qs.B;
   const int chunk = blockIdx.y;
   const int total = a.qs.q_len * a.qs.G;
   const int f0 = tile * TR;
   const int f1 = min(f0 + TR, total);
   const Seg cs = chunk_seg(a.seg, a.n_seg, a.chunk_begin, a.chunk_len, chunk);
-  partial_job<D, kAux, W, TK>(a.qs, f0, f1, g, cs, a.ws_m, a.ws_l, a.ws_o, (int64_t)chunk * a.R, (lds_char*)lds);
+  partial_job<D, kAux, W, TK>(a.qs, f0, f1, g, b, cs, a.ws_m, a.ws_l, a.ws_o, (int64_t)chunk * a.R, (lds_char*)lds);
 }
 
 // Shared-prefix fan-out (decode, or prefill of the private suffixes), one
@@ -510,7 +518,7 @@ __global__ __launch_bounds__(kWide ? 2 * kThreads : kThreads, kWide ? 1 : 2) voi
         return;
       }
       partial_job_segs<D, kAux, W>(
-          a.qs, f0, f1, g, paged_segments(k_off, k_end, a.page_len),
+          a.qs, f0, f1, g, 0, paged_segments(k_off, k_end, a.page_len),
           [&](int i) { return paged_seg<D>(a, pi, k_off, k_end, i, 0); }, a.ws_m, a.ws_l, a.ws_o,
           (int64_t)chunk * a.R, (lds_char*)lds);
       return;
@@ -520,7 +528,7 @@ __global__ __launch_bounds__(kWide ? 2 * kThreads : kThreads, kWide ? 1 : 2) voi
     sg.v = (const uint16_t*)sg.v + (int64_t)k_off * sg.vs_t;
     sg.pos0 = k_off;
     sg.n = k_end - k_off;
-    partial_job<D, kAux, W>(a.qs, f0, f1, g, sg, a.ws_m, a.ws_l, a.ws_o, (int64_t)chunk * a.R, (lds_char*)lds);
+    partial_job<D, kAux, W>(a.qs, f0, f1, g, 0, sg, a.ws_m, a.ws_l, a.ws_o, (int64_t)chunk * a.R, (lds_char*)lds);
     return;
   }
   const int j = id - n_prefix_jobs;
@@ -554,7 +562,7 @@ __global__ __launch_bounds__(kWide ? 2 * kThreads : kThreads, kWide ? 1 : 2) voi
         continue;
       }
       partial_job_segs<D, kAux, W>(
-          qs, f0, f1, g, paged_segments(0, a.S, a.page_len), [&](int i) { return paged_seg<D>(a, pi, 0, a.S, i, 0); },
+          qs, f0, f1, g, 0, paged_segments(0, a.S, a.page_len), [&](int i) { return paged_seg<D>(a, pi, 0, a.S, i, 0); },
           a.ws_m, a.ws_l, a.ws_o, (int64_t)a.suffix_slot * a.R, (lds_char*)lds);
       continue;
     }
@@ -567,8 +575,10 @@ __global__ __launch_bounds__(kWide ? 2 * kThreads : kThreads, kWide ? 1 : 2) voi
     sg.vs_h = D;
     sg.pos0 = 0;
     sg.n = a.S;
+    sg.ks_b = 0;
+    sg.vs_b = 0;
     sg.pad_ = 0;
-    partial_job<D, kAux, W>(qs, f0, f1, g, sg, a.ws_m, a.ws_l, a.ws_o, (int64_t)a.suffix_slot * a.R,
+    partial_job<D, kAux, W>(qs, f0, f1, g, 0, sg, a.ws_m, a.ws_l, a.ws_o, (int64_t)a.suffix_slot * a.R,
                             (lds_char*)lds);
   }
 }
@@ -577,7 +587,7 @@ __global__ __launch_bounds__(kWide ? 2 * kThreads : kThreads, kWide ? 1 : 2) voi
 
 hipError_t launch_walk_bf16(const WalkArgs& a, int D, hipStream_t s) {
   const int tiles = (a.qs.q_len * a.qs.G + kWalkRows - 1) / kWalkRows;
-  dim3 grid(tiles * a.qs.Hkv);
+  dim3 grid(tiles * a.qs.Hkv * a.qs.B);
   if (D == 128)
     hipLaunchKernelGGL(walk_kernel<128>, grid, dim3(64 * kWalkWaves), 0, s, a);
   else
@@ -598,9 +608,12 @@ void launch_split_d(const SplitArgs& a, dim3 grid, bool stream, hipStream_t s) {
 hipError_t launch_split_bf16(const SplitArgs& a, int n_chunks, int D, hipStream_t s) {
   const int tile_rows = a.wide ? kWideTileRows : kTileRows;
   const int per_head = (a.qs.q_len * a.qs.G + tile_rows - 1) / tile_rows;
-  dim3 grid(per_head * a.qs.Hkv, n_chunks);
-  // One row tile per KV head: every K/V byte is read by one workgroup.
-  const bool stream = per_head == 1;
+  dim3 grid(per_head * a.qs.Hkv * a.qs.B, n_chunks);
+  // One row tile per KV head, and no K/V shared between sequences: every K/V
+  // byte is read by one workgroup.
+  bool shared = false;
+  for (int i = 0; i < a.n_seg && a.qs.B > 1; ++i) shared = shared || a.seg[i].ks_b == 0 || a.seg[i].vs_b == 0;
+  const bool stream = per_head == 1 && !shared;
   if (D == 128)
     launch_split_d<128>(a, grid, stream, s);
   else

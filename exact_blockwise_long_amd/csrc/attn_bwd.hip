@@ -178,12 +178,14 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(BwdArgs a) {
   const QSide& qs = a.qs;
   const int Hkv = qs.Hkv;
   const int g = blockIdx.x % Hkv;
+  const int rest = blockIdx.x / Hkv;
+  const int b = rest % qs.B;
   const int n_tiles = (qs.q_len * qs.G + kDqRows - 1) / kDqRows;
-  const int tile = n_tiles - 1 - (int)(blockIdx.x / Hkv);  // causal: longest rows first
+  const int tile = n_tiles - 1 - rest / qs.B;  // causal: longest rows first
   const int total = qs.q_len * qs.G;
   const int f0 = tile * kDqRows;
   const int f1 = min(f0 + kDqRows, total);
-  const RowCtx rc = make_rowctx(qs, f0, f1, g);
+  const RowCtx rc = make_rowctx(qs, f0, f1, g, b);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const LaneRows lr = lane_rows(qs, rc, wave, lane);
@@ -392,7 +394,9 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdArgs a) {
   const QSide& qs = a.qs;
   const int Hkv = qs.Hkv;
   const int g = blockIdx.x % Hkv;
-  const int tile = blockIdx.x / Hkv;
+  const int rest = blockIdx.x / Hkv;
+  const int b = rest % qs.B;                    // sequence
+  const int tile = rest / qs.B;
   int si = 0;
   while (si + 1 < a.n_seg && a.tile_begin[si + 1] <= tile) ++si;
   const Seg& sg = a.seg[si];
@@ -416,8 +420,10 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdArgs a) {
   bf16x8 kf[C::DC], vf[C::DC];
   {
     const int kk = min(key_idx, n_keys - 1);
-    const uint16_t* kp = (const uint16_t*)sg.k + (int64_t)kk * sg.ks_t + (int64_t)g * sg.ks_h + 8 * (lane >> 4);
-    const uint16_t* vp = (const uint16_t*)sg.v + (int64_t)kk * sg.vs_t + (int64_t)g * sg.vs_h + 8 * (lane >> 4);
+    const uint16_t* kp = (const uint16_t*)sg.k + (int64_t)b * sg.ks_b + (int64_t)kk * sg.ks_t + (int64_t)g * sg.ks_h +
+                         8 * (lane >> 4);
+    const uint16_t* vp = (const uint16_t*)sg.v + (int64_t)b * sg.vs_b + (int64_t)kk * sg.vs_t + (int64_t)g * sg.vs_h +
+                         8 * (lane >> 4);
 #pragma unroll
     for (int dc = 0; dc < C::DC; ++dc) {
       kf[dc] = *(const bf16x8*)(kp + 32 * dc);
@@ -440,10 +446,14 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdArgs a) {
   const int t_begin = r_begin >= total ? t_end : r_begin / kRowTile;
 
   if (t_begin < t_end) {
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qs.q, a.q_bytes);
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.dout, a.q_bytes);
-    const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse, a.rows_bytes);
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.delta, a.rows_bytes);
+    // The sequence's own Q, dO, LSE and delta rows: q_bytes and rows_bytes are
+    // one sequence's extents.
+    const int64_t q_off = (int64_t)b * qs.qs_b;
+    const int64_t row0 = (int64_t)b * qs.q_len * qs.Hq;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint16_t*)qs.q + q_off, a.q_bytes);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc((const uint16_t*)a.dout + q_off, a.q_bytes);
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse + row0, a.rows_bytes);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.delta + row0, a.rows_bytes);
     const uint32_t lds_addr = (uint32_t)(size_t)(lds_char*)lds;
     // Row tiles are walked from the last one down: every workgroup of a KV
     // head then starts at the same row tile and the resident ones stream Q
@@ -465,9 +475,9 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdArgs a) {
     wait_all_loads();
   }
 
-  // dk[key, g, 16*db + 4*(lane/16) + i] += scale * dK^T; dv likewise, unscaled.
+  // dk[b, key, g, 16*db + 4*(lane/16) + i] += scale * dK^T; dv likewise, unscaled.
   if (key_idx < n_keys && t_begin < t_end) {
-    const int64_t base = ((int64_t)key_idx * Hkv + g) * D + 4 * (lane >> 4);
+    const int64_t base = (((int64_t)b * n_keys + key_idx) * Hkv + g) * D + 4 * (lane >> 4);
     float* dkp = a.dk[si] + base;
     float* dvp = a.dv[si] + base;
 #pragma unroll
@@ -496,8 +506,8 @@ hipError_t launch_delta(const DeltaArgs& a, int D, hipStream_t s) {
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, int n_key_tiles, int D, hipStream_t s) {
   const int tiles = (a.qs.q_len * a.qs.G + kDqRows - 1) / kDqRows;
-  dim3 grid_q(tiles * a.qs.Hkv);
-  dim3 grid_k(n_key_tiles * a.qs.Hkv);
+  dim3 grid_q(tiles * a.qs.Hkv * a.qs.B);
+  dim3 grid_k(n_key_tiles * a.qs.Hkv * a.qs.B);
   if (D == 128) {
     hipLaunchKernelGGL(dq_kernel<128>, grid_q, dim3(64 * kDqWaves), 0, s, a);
     if (n_key_tiles > 0) hipLaunchKernelGGL(dkdv_kernel<128>, grid_k, dim3(kThreads), 0, s, a);

@@ -20,7 +20,9 @@ __global__ __launch_bounds__(kRows) void walk_f32_kernel(WalkArgs a) {
   __shared__ float vs[kKeys][D];
   const QSide& qs = a.qs;
   const int g = blockIdx.x % qs.Hkv;
-  const int tile = blockIdx.x / qs.Hkv;
+  const int rest = blockIdx.x / qs.Hkv;
+  const int b = rest % qs.B;       // sequence
+  const int tile = rest / qs.B;
   const int total = qs.q_len * qs.G;
   const int f0 = tile * kRows;
   const int f1 = min(f0 + kRows, total);
@@ -32,10 +34,10 @@ __global__ __launch_bounds__(kRows) void walk_f32_kernel(WalkArgs a) {
   const int h = g * qs.G + (fc - t * qs.G);
   const int64_t qpos = qs.q_pos0 + t;
   const int64_t qpos_max = qs.q_pos0 + (f1 - 1) / qs.G;
-  const int64_t srow = (int64_t)t * qs.Hq + h;
+  const int64_t srow = ((int64_t)b * qs.q_len + t) * qs.Hq + h;
 
   float q[D], o[D];
-  const float* qp = (const float*)qs.q + (int64_t)t * qs.qs_t + (int64_t)h * qs.qs_h;
+  const float* qp = (const float*)qs.q + (int64_t)b * qs.qs_b + (int64_t)t * qs.qs_t + (int64_t)h * qs.qs_h;
 #pragma unroll
   for (int d = 0; d < D; ++d) q[d] = qp[d];
   float m2, l;
@@ -59,8 +61,8 @@ __global__ __launch_bounds__(kRows) void walk_f32_kernel(WalkArgs a) {
       int64_t lim = qpos_max - s.pos0 + 1;
       n = (int)max((int64_t)0, min((int64_t)n, lim));
     }
-    const float* kb = (const float*)s.k + (int64_t)g * s.ks_h;
-    const float* vb = (const float*)s.v + (int64_t)g * s.vs_h;
+    const float* kb = (const float*)s.k + (int64_t)b * s.ks_b + (int64_t)g * s.ks_h;
+    const float* vb = (const float*)s.v + (int64_t)b * s.vs_b + (int64_t)g * s.vs_h;
     for (int k0 = 0; k0 < n; k0 += kKeys) {
       const int nv = min(kKeys, n - k0);
       __syncthreads();
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(kRows) void walk_f32_kernel(WalkArgs a) {
 
 hipError_t launch_walk_f32(const WalkArgs& a, int D, hipStream_t s) {
   const int tiles = (a.qs.q_len * a.qs.G + kRows - 1) / kRows;
-  dim3 grid(tiles * a.qs.Hkv);
+  dim3 grid(tiles * a.qs.Hkv * a.qs.B);
   if (D == 128)
     hipLaunchKernelGGL(walk_f32_kernel<128>, grid, dim3(kRows), 0, s, a);
   else

@@ -106,6 +106,8 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
 struct RowCtx {
   int f0, f1;              // flat row range [f0, f1) of this tile
   int g;                   // KV head
+  int b;                   // sequence
+  int64_t row0;            // state row of the sequence's first row: b * q_len * Hq
   int64_t qpos_min, qpos_max;
 };
 
@@ -121,10 +123,10 @@ struct KVSrc {
 };
 
 template <int D>
-__device__ inline KVSrc make_src(const Seg& s, int g) {
+__device__ inline KVSrc make_src(const Seg& s, const RowCtx& rc) {
   KVSrc r;
-  r.kb = (const char*)s.k + (int64_t)g * s.ks_h * 2;
-  r.vb = (const char*)s.v + (int64_t)g * s.vs_h * 2;
+  r.kb = (const char*)s.k + ((int64_t)rc.g * s.ks_h + (int64_t)rc.b * s.ks_b) * 2;
+  r.vb = (const char*)s.v + ((int64_t)rc.g * s.vs_h + (int64_t)rc.b * s.vs_b) * 2;
   r.kst = (uint32_t)(s.ks_t * 2);
   r.vst = (uint32_t)(s.vs_t * 2);
   r.pos0 = s.pos0;
@@ -195,7 +197,7 @@ __device__ inline int seg_effective(const Seg& s, const QSide& qs, const RowCtx&
 // so the kernels rebuild it after the key loop instead of keeping it live.
 struct LaneRows {
   int qrel[2];       // query position minus the tile's first query position
-  int64_t srow[2];   // state row t*Hq + h
+  int64_t srow[2];   // state row (b*q_len + t)*Hq + h
   bool valid[2];
   const uint16_t* qptr[2];
 };
@@ -212,8 +214,8 @@ __device__ inline LaneRows lane_rows(const QSide& qs, const RowCtx& rc, int wave
     int j = fc - t * qs.G;
     int h = rc.g * qs.G + j;
     lr.qrel[qb] = t - t0;
-    lr.srow[qb] = (int64_t)t * qs.Hq + h;
-    lr.qptr[qb] = (const uint16_t*)qs.q + (int64_t)t * qs.qs_t + (int64_t)h * qs.qs_h;
+    lr.srow[qb] = rc.row0 + (int64_t)t * qs.Hq + h;
+    lr.qptr[qb] = (const uint16_t*)qs.q + (int64_t)rc.b * qs.qs_b + (int64_t)t * qs.qs_t + (int64_t)h * qs.qs_h;
   }
   return lr;
 }
@@ -261,7 +263,7 @@ __device__ inline void run_segments(const QSide& qs, const RowCtx& rc, int n_seg
   int is = next_nonempty(0, is_n);
   if (is >= n_seg) return;
   int ik = 0;
-  KVSrc isrc = make_src<D>(get_seg(is), rc.g);
+  KVSrc isrc = make_src<D>(get_seg(is), rc);
   LaneOffs<D, W, TK> ilo = lane_offsets<D, W, TK>(isrc, wave, lane);
   // compute cursor
   int cs = is, ck = 0, cn = is_n;
@@ -276,7 +278,7 @@ __device__ inline void run_segments(const QSide& qs, const RowCtx& rc, int n_seg
       is = next_nonempty(is + 1, is_n);
       ik = 0;
       if (is < n_seg) {
-        isrc = make_src<D>(get_seg(is), rc.g);
+        isrc = make_src<D>(get_seg(is), rc);
         ilo = lane_offsets<D, W, TK>(isrc, wave, lane);
       }
     }
@@ -316,11 +318,13 @@ __device__ inline void run_segments(const QSide& qs, const RowCtx& rc, int n_seg
   wait_all_loads();
 }
 
-__device__ inline RowCtx make_rowctx(const QSide& qs, int f0, int f1, int g) {
+__device__ inline RowCtx make_rowctx(const QSide& qs, int f0, int f1, int g, int b) {
   RowCtx rc;
   rc.f0 = f0;
   rc.f1 = f1;
   rc.g = g;
+  rc.b = b;
+  rc.row0 = (int64_t)b * qs.q_len * qs.Hq;
   rc.qpos_min = qs.q_pos0 + f0 / qs.G;
   rc.qpos_max = qs.q_pos0 + (f1 - 1) / qs.G;
   return rc;

@@ -15,25 +15,29 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // One contiguous key range: keys [0, n) of this segment sit at absolute
-// positions pos0 + i; k/v point at key 0 of the range.
+// positions pos0 + i; k/v point at key 0 of the range of sequence 0, the
+// range of sequence b sitting b * ks_b (vs_b) elements further.
 struct Seg {
   const void* k;
   const void* v;
   int64_t ks_t, ks_h, vs_t, vs_h;
+  int64_t ks_b, vs_b;
   int64_t pos0;
   int32_t n;
   int32_t pad_;
 };
 
 // The query side shared by every attention kernel.  Query "flat rows" of KV
-// head g are f = t * G + j for token t < q_len and group member j < G; flat
-// row f reads q head g * G + j of token t, sits at position q_pos0 + t, and
-// owns state row t * Hq + g * G + j.
+// head g of sequence b are f = t * G + j for token t < q_len and group member
+// j < G; flat row f reads q head g * G + j of token t of sequence b (b * qs_b
+// elements after q), sits at position q_pos0 + t, and owns state row
+// (b * q_len + t) * Hq + g * G + j.  A workgroup serves one (sequence, KV head).
 struct QSide {
   const void* q;
-  int64_t qs_t, qs_h;
+  int64_t qs_t, qs_h, qs_b;
   int64_t q_pos0;
   int32_t Hq, Hkv, G, q_len;
+  int32_t B;      // sequences (>= 1)
   float c;        // logit scale * log2(e): the kernels work in base 2
   int32_t causal;
 };
@@ -167,7 +171,7 @@ struct BwdArgs {
   const float* delta;
   float* dq;
   float scale;
-  uint32_t q_bytes;      // bytes from q (and dout) to the end of its last row
+  uint32_t q_bytes;      // bytes from one sequence's q (and dout) to the end of its last row
   uint32_t rows_bytes;   // bytes of lse and delta
   uint32_t g_magic;      // floor((2^32 - 1) / G): flat row -> token by one multiply-high and one fix-up
   int32_t n_seg;

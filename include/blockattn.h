@@ -38,8 +38,9 @@
  *   - Strides are in elements.  The head_dim axis is always contiguous.
  *     bf16 tensors need 16-byte aligned base pointers and strides that are
  *     multiples of 8 elements; state `o` arrays need 16-byte alignment.
- *   - A "state" is three fp32 arrays indexed by row r = token * n_q_heads +
- *     q_head: m[rows], l[rows], o[rows * head_dim] (row-major, o unnormalised).
+ *   - A "state" is three fp32 arrays indexed by row r = (b * q_len + token) *
+ *     n_q_heads + q_head, b the sequence of a batched problem (0 without a
+ *     batch): m[rows], l[rows], o[rows * head_dim] (row-major, o unnormalised).
  *     m is in natural-log units of the scaled logit.  The initial state of
  *     [RAC] s.3 is m = -inf, l = 0, o = 0; a row that has seen no key keeps it.
  *   - GQA: query head h reads KV head h / (n_q_heads / n_kv_heads).
@@ -62,7 +63,7 @@
 extern "C" {
 #endif
 
-#define BLOCKATTN_ABI_VERSION 1
+#define BLOCKATTN_ABI_VERSION 2
 #define BLOCKATTN_MAX_VISITS 32      /* max K/V blocks visited by one fwd call   */
 #define BLOCKATTN_MAX_MERGE_PARTS 64 /* max partial states merged by one call    */
 
@@ -80,7 +81,14 @@ typedef enum { BA_F32 = 0, BA_BF16 = 1 } ba_dtype;
 
 /* The stationary query block ([RAC] s.3: Q_k stays on its device).
  * q is [q_len, n_q_heads, head_dim] with the given token and head strides;
- * query row t sits at absolute position q_pos0 + t. */
+ * query row t sits at absolute position q_pos0 + t.
+ *
+ * batch > 1 runs that many independent sequences of the same shape, positions
+ * and visit order in one call: q is [batch, q_len, n_q_heads, head_dim] with
+ * q_stride_batch elements between sequences; every K/V block holds the keys of
+ * all of them at its k/v_stride_batch (0: the sequences share the block's
+ * keys); state, output and log-sum-exp rows number batch * q_len * n_q_heads.
+ * batch 0 or 1 is one sequence (q_stride_batch is then not read). */
 typedef struct {
   int32_t n_q_heads;      /* Hq, a multiple of n_kv_heads                      */
   int32_t n_kv_heads;     /* Hkv                                               */
@@ -95,10 +103,14 @@ typedef struct {
   int32_t split_mode;     /* 0: automatic; 1: never split the keys (one pass in
                              visit order); 2: always split (bf16 only).  Only
                              rounding differs between the modes.              */
+  int32_t batch;          /* independent sequences (0 or 1: one)               */
+  int64_t q_stride_batch; /* elements between consecutive sequences of q      */
 } ba_problem;
 
 /* One K/V block: k and v are [len, n_kv_heads, head_dim]; key i sits at
- * absolute position pos0 + i ([RAC] s.3, contiguous blocks of the sequence). */
+ * absolute position pos0 + i ([RAC] s.3, contiguous blocks of the sequence).
+ * For a batched problem they are [batch, len, n_kv_heads, head_dim] with the
+ * batch strides below (not read without a batch). */
 typedef struct {
   const void* k;
   const void* v;
@@ -106,6 +118,7 @@ typedef struct {
   int64_t pos0;
   int64_t k_stride_token, k_stride_head;
   int64_t v_stride_token, v_stride_head;
+  int64_t k_stride_batch, v_stride_batch;  /* >= 0; 0 shares the keys */
 } ba_kv_block;
 
 /* fp32 online-softmax state; see the conventions above. */
@@ -151,9 +164,11 @@ typedef struct {
  *
  * Errors: BA_ERR_NULL (p, q, blocks with n_visit > 0, a block's k/v with
  * len > 0, or a state array); BA_ERR_SHAPE (bad head counts, head_dim, negative
- * lengths, non-positive strides, a bf16 block whose token stride is below
- * head_dim, a bf16 block one of whose KV heads spans
- * 4 GiB or more: the bf16 kernels address it with 32-bit offsets); BA_ERR_ORDER (duplicate/out-of-range order
+ * lengths or batch, non-positive token or head strides, with batch > 1 a
+ * non-positive q_stride_batch or a negative k/v_stride_batch, more than 2^30
+ * state rows, a bf16 block whose token stride is below head_dim, a bf16 block
+ * one of whose KV heads spans 4 GiB or more in one sequence: the bf16 kernels
+ * address it with 32-bit offsets); BA_ERR_ORDER (duplicate/out-of-range order
  * entry, n_visit > BLOCKATTN_MAX_VISITS or > n_blocks); BA_ERR_UNSUPPORTED
  * (dtype); BA_ERR_WORKSPACE. */
 ba_status blockattn_fwd_block(const ba_problem* p, const void* q,
@@ -165,9 +180,9 @@ ba_status blockattn_fwd_block(const ba_problem* p, const void* q,
 
 /* The last visits of a query block and its finalisation in one call ([RAC]
  * s.2 and s.7): the result is that of blockattn_fwd_block with the same
- * arguments followed by blockattn_finalize(state, q_len * n_q_heads,
- * head_dim, out, out_dtype, out_row_stride, lse) -- out [q_len * n_q_heads
- * rows, state-row order t * n_q_heads + h] of A = O / l in out_dtype (BA_BF16,
+ * arguments followed by blockattn_finalize(state, rows, head_dim, out,
+ * out_dtype, out_row_stride, lse) with rows = batch * q_len * n_q_heads --
+ * out [rows, state-row order] of A = O / l in out_dtype (BA_BF16,
  * rounded to nearest even, or BA_F32), lse (may be NULL) of m + ln l, and 0 /
  * -inf for rows that saw no key -- up to rounding: the bf16 walk writes A and
  * LSE from its registers instead of storing the state and reading it back.
@@ -398,26 +413,30 @@ ba_status blockattn_bwd_delta(int64_t rows, int32_t head_dim, const void* out, i
  * dQ for the stationary query block and dK, dV for the visiting block).
  *
  * p, q, blocks, n_blocks, order and n_visit are those of the forward; dout
- * ([q_len, n_q_heads, head_dim] bf16 with q's strides) is the gradient of the
- * loss with respect to the finalised output; lse [q_len * n_q_heads] is the
+ * ([batch,] q_len, n_q_heads, head_dim] bf16 with q's strides) is the gradient
+ * of the loss with respect to the finalised output; lse [rows] is the
  * forward's final log-sum-exp (blockattn_finalize, natural log; -inf for a
  * row that saw no key) and delta the output of blockattn_bwd_delta, both in
  * state-row order.  With P = exp(scale q.k - lse) over the row's visible keys:
  *   dq[r, :] += scale * sum_j P_rj (dP_rj - delta_r) k_j,  dP_rj = dout_r . v_j;
  *   dk_b[j, g, :] += scale * sum_r P_rj (dP_rj - delta_r) q_r;
  *   dv_b[j, g, :] += sum_r P_rj dout_r,
- * summed over the query heads r of KV head g.  dq is fp32 [q_len * n_q_heads,
- * head_dim] (state-row order); dk and dv are HOST arrays of n_blocks device
- * pointers, entry b pointing at fp32 [blocks[b].len, n_kv_heads, head_dim]
- * (contiguous) for every visited block; all accumulate (+=), so one call per
+ * summed over the query heads r of KV head g.  dq is fp32 [rows, head_dim]
+ * (state-row order); dk and dv are HOST arrays of n_blocks device pointers,
+ * entry b pointing at fp32 [blocks[b].len, n_kv_heads, head_dim] (contiguous)
+ * for every visited block -- [batch, len, n_kv_heads, head_dim] for a batched
+ * problem, one gradient per sequence also where the sequences share the
+ * block's keys (their sum is the shared keys' gradient); rows = batch * q_len
+ * * n_q_heads.  All accumulate (+=), so one call per
  * ring step (reverse order or any order) builds the full gradients; within a
  * call the blocks are processed in key-position order (order changes only
  * rounding).  Blocks no query of the block can see are skipped.  The dk/dv buffers of different
  * blocks of one call are updated concurrently and must not overlap; calls that
  * share buffers must be ordered (one stream).  The caller owns every buffer;
  * nothing is kept after the call returns.  Results do not depend on scheduling
- * (no atomics).  bf16 only; q, dout, lse and delta must each span less than
- * 4 GiB.  Errors: as blockattn_fwd_block, plus
+ * (no atomics).  bf16 only; one sequence's q (and dout) rows, and the lse and
+ * delta rows of all sequences, must each span less than 4 GiB.  Errors: as
+ * blockattn_fwd_block, plus
  * BA_ERR_NULL (dout, lse, delta, dq, or a visited block's dk/dv) and
  * BA_ERR_UNSUPPORTED (fp32 problems). */
 ba_status blockattn_bwd_block(const ba_problem* p, const void* q, const void* dout,

@@ -8,6 +8,8 @@ enqueued (pointers are never dereferenced on the host).
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 import torch  # noqa: F401  (load torch's HIP runtime first)
@@ -47,10 +49,33 @@ def test_single_hip_runtime(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.blockattn_abi_version() == 1
+    assert lib.blockattn_abi_version() == 2
     for s in range(7):
         assert lib.blockattn_status_str(s)
     assert lib.blockattn_status_str(99) == b"unknown status"
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not installed")
+def test_struct_layouts_match_the_header(tmp_path):
+    """Every field of the public structs sits at the same offset in the
+    header (compiled as C) and in the binding's ctypes declarations."""
+    exe = str(tmp_path / "abi_layout")
+    subprocess.run(["gcc", "-std=c11", "-Wall", f"-I{os.path.join(ROOT, 'include')}", "-I/opt/rocm/include",
+                    "-D__HIP_PLATFORM_AMD__", os.path.join(ROOT, "tests", "abi_layout.c"), "-o", exe], check=True)
+    lines = subprocess.run([exe], capture_output=True, text=True, check=True, timeout=60).stdout.split("\n")
+    py = {"ba_problem": ba.Problem, "ba_kv_block": ba.KVBlock, "ba_state": ba.State, "ba_fanout": ba.Fanout,
+          "ba_fanout_prefill": ba.FanoutPrefill, "ba_kv_pages": ba.KVPages}
+    seen = {n: set() for n in py}
+    for ln in filter(None, lines):
+        struct, field, value = ln.split()
+        cls = py[struct]
+        if field == "sizeof":
+            assert ctypes.sizeof(cls) == int(value), (struct, ctypes.sizeof(cls), value)
+        else:
+            assert getattr(cls, field).offset == int(value), (struct, field)
+            seen[struct].add(field)
+    for n, cls in py.items():
+        assert seen[n] == {f for f, _ in cls._fields_}, n
 
 
 def _problem(**kw):
@@ -82,7 +107,8 @@ def _fwd(lib, p, blocks, n_blocks, order, n_visit, ws=None, ws_bytes=0, state=No
 @pytest.mark.parametrize("kw,expect", [
     (dict(head_dim=96), 2), (dict(n_q_heads=6, n_kv_heads=4), 2), (dict(n_kv_heads=0), 2),
     (dict(q_len=-1), 2), (dict(dtype=7), 3), (dict(q_stride_token=0), 2), (dict(split_mode=5), 2),
-    (dict(q_stride_head=12), 2),
+    (dict(q_stride_head=12), 2), (dict(batch=-1), 2), (dict(batch=2, q_stride_batch=0), 2),
+    (dict(batch=2, q_stride_batch=12), 2), (dict(batch=1 << 24, q_stride_batch=16 * 8 * 128), 2),
 ])
 def test_fwd_rejects_bad_problem(lib, kw, expect):
     assert _fwd(lib, _problem(**kw), _blocks(2), 2, [0, 1], 2) == expect
@@ -102,6 +128,29 @@ def test_fwd_null_arguments(lib):
 @pytest.mark.parametrize("order,n_blocks", [([0, 0], 2), ([0, 2], 2), ([-1], 2), (list(range(33)), 40)])
 def test_fwd_rejects_bad_order(lib, order, n_blocks):
     assert _fwd(lib, _problem(), _blocks(n_blocks), n_blocks, order, len(order)) == 4
+
+
+def test_fwd_rejects_bad_batch_strides(lib):
+    p = _problem(batch=3, q_stride_batch=16 * 8 * 128)
+    for field, value in (("k_stride_batch", -8), ("v_stride_batch", -8), ("k_stride_batch", 12)):
+        b = _blocks(2)
+        setattr(b[1], field, value)
+        assert _fwd(lib, p, b, 2, None, 2) == 2, field
+    # batch strides are not read without a batch, and 0 (shared keys) is valid with one
+    b = _blocks(2)
+    b[0].k_stride_batch = -8
+    assert lib.blockattn_fwd_workspace_bytes(ctypes.byref(_problem(split_mode=2)), b, 2, None, 2) > 0
+    assert lib.blockattn_fwd_workspace_bytes(ctypes.byref(_problem(split_mode=2, batch=3,
+                                                                   q_stride_batch=16 * 8 * 128)),
+                                             _blocks(2), 2, None, 2) > 0
+
+
+def test_batch_scales_the_workspace(lib):
+    """Split partial states cover every sequence's rows."""
+    one = lib.blockattn_fwd_workspace_bytes(ctypes.byref(_problem(split_mode=2)), _blocks(3), 3, None, 3)
+    three = lib.blockattn_fwd_workspace_bytes(
+        ctypes.byref(_problem(split_mode=2, batch=3, q_stride_batch=16 * 8 * 128)), _blocks(3), 3, None, 3)
+    assert one > 0 and three > one
 
 
 def test_fwd_rejects_misaligned(lib):
