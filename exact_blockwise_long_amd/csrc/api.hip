@@ -746,7 +746,7 @@ struct FanoutPlan {
 // walks bpj branches' private suffixes of one KV head one after another (or
 // one row tile of one branch when a branch has more than one); a prefix job
 // walks one chunk of the shared prefix for one row tile of a KV head.
-FanoutPlan plan_fanout_tiles(const FanoutShape& f, int tile_rows, int target) {
+FanoutPlan plan_fanout_tiles(const FanoutShape& f, int tile_rows, int target, int key_align) {
   FanoutPlan fp;
   const int G = f.Hq / f.Hkv;
   const int64_t rows = (int64_t)f.nb * f.T * G;
@@ -776,7 +776,7 @@ FanoutPlan plan_fanout_tiles(const FanoutShape& f, int tile_rows, int target) {
     int64_t want = (target - (suffix_small ? 0 : fp.suffix_jobs)) / xs;
     if (want < 1) want = 1;
     int64_t cl = (f.P + want - 1) / want;
-    cl = (cl + 63) / 64 * 64;
+    cl = (cl + key_align - 1) / key_align * key_align;
     if (cl < 256) cl = 256;
     fp.chunk_len = (int)cl;
     fp.n_chunks = (int)((f.P + cl - 1) / cl);
@@ -790,11 +790,13 @@ FanoutPlan plan_fanout_tiles(const FanoutShape& f, int tile_rows, int target) {
 // More than one 128-row tile per KV head (a prefill, or a decode of many
 // branches per group) makes the launch matrix-core bound: it then runs 8-wave
 // workgroups of 256-row tiles, one per compute unit, sized to half as many
-// jobs, so each K/V tile staged in LDS serves twice the rows (as in the walk).
+// jobs, so each K/V tile staged in LDS serves twice the rows (as in the walk),
+// and its prefix chunks start at multiples of 128 keys for the walk's 128-key
+// tiles (fanout_kernel).
 FanoutPlan plan_fanout(const FanoutShape& f) {
-  FanoutPlan fp = plan_fanout_tiles(f, ba::kTileRows, ba::kFanoutTargetWorkgroups);
+  FanoutPlan fp = plan_fanout_tiles(f, ba::kTileRows, ba::kFanoutTargetWorkgroups, 64);
   if (BA_FANOUT_WIDE && fp.row_tiles >= 2) {
-    fp = plan_fanout_tiles(f, ba::kWideTileRows, ba::kFanoutTargetWorkgroups / 2);
+    fp = plan_fanout_tiles(f, ba::kWideTileRows, ba::kFanoutTargetWorkgroups / 2, 128);
     fp.wide = true;
   }
   return fp;
@@ -880,6 +882,8 @@ ba_status fanout_run(const FanoutShape& f, const void* q, const void* prefix_k, 
   a.srt = fp.srt;
   a.bpj = fp.bpj;
   a.wide = fp.wide ? 1 : 0;
+  // Wide launches walk the prefix in 128-key tiles unless its pages split them.
+  a.prefix_keys = fp.wide && (!pages || pages->page_len % 128 == 0) ? 128 : 64;
   if (pages) {
     // The kernel takes the paged path for a job kind when its table is set.
     a.sk = nullptr;

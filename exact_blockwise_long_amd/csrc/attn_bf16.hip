@@ -489,14 +489,19 @@ __global__ __launch_bounds__(kWide ? 2 * kThreads : kThreads, kWide ? 1 : 2) voi
 // kWide: 8-wave workgroups of 256-row tiles, one per compute unit, as in the
 // walk (for launches with more than one 128-row tile per KV head, which the
 // matrix cores bound); otherwise 4 waves and 128-row tiles.
-template <int D, int kAux, bool kWide>
+//
+// TKP: the prefix jobs' key tile.  Wide launches take the walk's 128-key
+// tiles (that workgroup per compute unit has the LDS for them) when the prefix
+// is contiguous or its pages are multiples of 128 keys, 64 otherwise: a paged
+// walk then visits exactly the contiguous walk's tiles (chunks start at
+// multiples of 128 keys) and gives its result bit for bit.  Suffix jobs take
+// 64-key tiles.
+template <int D, int kAux, bool kWide, int TKP = kTileKeys>
 __global__ __launch_bounds__(kWide ? 2 * kThreads : kThreads, kWide ? 1 : 2) void fanout_kernel(FanoutArgs a) {
   constexpr int W = kWide ? 8 : 4;
   constexpr int TR = 32 * W;   // rows of a row tile
-  // 64-key tiles throughout, so that a paged walk (whose page pieces can be
-  // 64 keys long) visits exactly the contiguous walk's tiles and gives its
-  // result bit for bit.
-  __shared__ __attribute__((aligned(16))) char lds[2 * Cfg<D>::STAGEB];
+  static_assert(TKP == kTileKeys || kWide, "128-key tiles need the LDS of one workgroup per compute unit");
+  __shared__ __attribute__((aligned(16))) char lds[2 * Cfg<D, W, TKP>::STAGEB];
   const int Hkv = a.qs.Hkv;
   const int G = a.qs.G;
   const int total = a.qs.q_len * G;
@@ -517,7 +522,7 @@ __global__ __launch_bounds__(kWide ? 2 * kThreads : kThreads, kWide ? 1 : 2) voi
         store_corrupt<D, W>(a.qs, f0, f1, g, a.ws_m, a.ws_l, a.ws_o, (int64_t)chunk * a.R);
         return;
       }
-      partial_job_segs<D, kAux, W>(
+      partial_job_segs<D, kAux, W, TKP>(
           a.qs, f0, f1, g, 0, paged_segments(k_off, k_end, a.page_len),
           [&](int i) { return paged_seg<D>(a, pi, k_off, k_end, i, 0); }, a.ws_m, a.ws_l, a.ws_o,
           (int64_t)chunk * a.R, (lds_char*)lds);
@@ -528,7 +533,8 @@ __global__ __launch_bounds__(kWide ? 2 * kThreads : kThreads, kWide ? 1 : 2) voi
     sg.v = (const uint16_t*)sg.v + (int64_t)k_off * sg.vs_t;
     sg.pos0 = k_off;
     sg.n = k_end - k_off;
-    partial_job<D, kAux, W>(a.qs, f0, f1, g, 0, sg, a.ws_m, a.ws_l, a.ws_o, (int64_t)chunk * a.R, (lds_char*)lds);
+    partial_job<D, kAux, W, TKP>(a.qs, f0, f1, g, 0, sg, a.ws_m, a.ws_l, a.ws_o, (int64_t)chunk * a.R,
+                                 (lds_char*)lds);
     return;
   }
   const int j = id - n_prefix_jobs;
@@ -627,10 +633,16 @@ void launch_fanout_w(const FanoutArgs& a, dim3 grid, hipStream_t s) {
   // and each suffix is read by one workgroup.
   const bool stream = a.row_tiles == 1 && a.srt == 1;
   const dim3 block(kWide ? 2 * kThreads : kThreads);
-  if (stream)
+  if (kWide && a.prefix_keys == 128) {
+    if (stream)
+      hipLaunchKernelGGL((fanout_kernel<D, kCacheStream, kWide, (kWide ? 128 : kTileKeys)>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((fanout_kernel<D, kCacheReuse, kWide, (kWide ? 128 : kTileKeys)>), grid, block, 0, s, a);
+  } else if (stream) {
     hipLaunchKernelGGL((fanout_kernel<D, kCacheStream, kWide>), grid, block, 0, s, a);
-  else
+  } else {
     hipLaunchKernelGGL((fanout_kernel<D, kCacheReuse, kWide>), grid, block, 0, s, a);
+  }
 }
 
 hipError_t launch_fanout_bf16(const FanoutArgs& a, int n_jobs, int D, hipStream_t s) {

@@ -104,6 +104,7 @@ struct FanoutArgs {
   int32_t srt;       // row tiles of one branch's rows
   int32_t bpj;       // branches per suffix job (srt == 1)
   int32_t wide;      // 1: 8-wave workgroups and 256-row tiles (row_tiles, srt in those)
+  int32_t prefix_keys;  // key tile of the prefix jobs: 128 (wide launches) or 64
   // Paged K/V (prefix_pages != nullptr): prefix.k / prefix.v are the pools,
   // page p of a table starts page_len * Hkv * D elements after the pool base.
   const int32_t* prefix_pages;

@@ -161,7 +161,13 @@ def test_random_fanout(seed):
     else:
         o2, l2 = ba.fanout_prefix_prefill_paged(qd, kd, vd, ppd, spd, P, S)
     torch.cuda.synchronize()
-    assert torch.equal(out, o2) and torch.equal(lse, l2), f"paged (page_len {PL}) differs from contiguous"
+    if nb * T * (Hq // Hkv) <= 128 or PL % 128 == 0:
+        # the same key tiles as the contiguous call (wide launches take 128-key
+        # prefix tiles, which 64-key pages would split): bit for bit
+        assert torch.equal(out, o2) and torch.equal(lse, l2), f"paged (page_len {PL}) differs from contiguous"
+    else:
+        H.assert_bf16_out(H.host(o2), a_ref, f"random fanout seed {seed}, paged (page_len {PL})")
+        H.assert_close(H.host(l2), lse_ref, H.BF16_LSE, "paged lse")
 
 
 @pytest.mark.parametrize("seed", range(4000, 4016))
