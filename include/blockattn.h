@@ -367,7 +367,11 @@ typedef struct {
 /* fanout_prefix_decode and fanout_prefix_prefill over paged K/V: the same
  * attention, positions, outputs and workspace sizes (fanout_workspace_bytes,
  * fanout_prefill_workspace_bytes).  With every id valid the results equal the
- * contiguous entry points' bit for bit.  Errors: as the contiguous entry
+ * contiguous entry points' bit for bit when page_len is a multiple of 128, or
+ * when a KV head's query rows (n_branches * n_new * n_q_heads / n_kv_heads)
+ * number at most 128; otherwise (pages of an odd multiple of 64 keys under a
+ * launch that walks the prefix in 128-key tiles) they agree up to rounding.
+ * Errors: as the contiguous entry
  * points, plus BA_ERR_NULL (pages, a needed page table, a pool) and
  * BA_ERR_SHAPE (page_len not a positive multiple of 64, n_pool_pages < 1,
  * misaligned pool). */
