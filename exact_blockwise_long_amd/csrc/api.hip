@@ -519,7 +519,6 @@ ba_status blockattn_bwd_block(const ba_problem* p, const void* q, const void* do
   if (((uintptr_t)dout % 16) != 0 || ((uintptr_t)dq % 16) != 0) return fail(BA_ERR_SHAPE, "dout/dq not 16-byte aligned");
   if (!dk || !dv) return fail(BA_ERR_NULL, "dk or dv pointer array is NULL");
   const int D = p->head_dim;
-  const int64_t R = state_rows(p);
   const int64_t q_extent =
       ((int64_t)(p->q_len - 1) * p->q_stride_token + (int64_t)(p->n_q_heads - 1) * p->q_stride_head + D) * 2;
   const int64_t seq_rows = (int64_t)p->q_len * p->n_q_heads;   // one sequence's lse and delta rows
