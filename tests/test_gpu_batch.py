@@ -227,3 +227,41 @@ def test_batch_backward_equals_one_call_per_sequence():
         assert np.all(np.isfinite(got)), name
         # the backward tests' bounds: max error / max |ref| <= 2e-2, mean error / mean |ref| <= 5e-3
         assert err.max() / np.abs(ref).max() <= 2e-2 and err.mean() / np.abs(ref).mean() <= 5e-3, name
+
+
+def test_batch_backward_shared_keys_one_gradient_per_sequence():
+    """Blocks shared by all sequences (3-D K/V under a batched q): each
+    sequence gets its own dK/dV, equal to its own call's bit for bit."""
+    seed, B, T, Hq, Hkv, D, lens, order, q_pos0 = 109, 3, 90, 8, 2, 64, [100, 60], [1, 0], 120
+    announce(f"batch backward, shared keys, seed {seed} B={B} T={T} Hq={Hq} Hkv={Hkv} D={D} lens={lens} causal")
+    g = synth.rng(seed)
+    q = synth.normal(g, (B, T, Hq, D), 0.5, "bf16")
+    k = synth.normal(g, (sum(lens), Hkv, D), 0.5, "bf16")
+    v = synth.normal(g, (sum(lens), Hkv, D), 0.5, "bf16")
+    do = synth.normal(g, (B, T, Hq, D), 0.5, "bf16")
+    qd, kd, vd, dod = (H.to_device(x) for x in (q, k, v, do))
+    blocks = blocks_of(kd, vd, lens)
+    kw = dict(n_kv_heads=Hkv, q_pos0=q_pos0, causal=True)
+
+    def grads(qx, dox, batched):
+        rows = (B if batched else 1) * T * Hq
+        st = ba.new_state(rows, D)
+        ba.fwd_block(qx, blocks, order, st, reset=True, split_mode=1, **kw)
+        out, lse = ba.finalize(st)
+        delta = ba.bwd_delta(out, dox)
+        dq = torch.zeros(rows, D, dtype=torch.float32, device="cuda")
+        shape = (lambda n: (B, n, Hkv, D)) if batched else (lambda n: (n, Hkv, D))
+        dkv = [(torch.zeros(shape(n), dtype=torch.float32, device="cuda"),
+                torch.zeros(shape(n), dtype=torch.float32, device="cuda")) for n in lens]
+        ba.bwd_block(qx, dox, lse, delta, blocks, order, dq, dkv, **kw)
+        return dq, dkv
+
+    dq, dkv = grads(qd, dod, True)
+    torch.cuda.synchronize()
+    R = T * Hq
+    for b in range(B):
+        dq1, dkv1 = grads(qd[b], dod[b], False)
+        torch.cuda.synchronize()
+        assert torch.equal(dq[b * R:(b + 1) * R], dq1), f"dq of sequence {b}"
+        for i, ((dk, dv), (dk1, dv1)) in enumerate(zip(dkv, dkv1)):
+            assert torch.equal(dk[b], dk1) and torch.equal(dv[b], dv1), f"dk/dv of block {i}, sequence {b}"
