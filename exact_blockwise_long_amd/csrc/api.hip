@@ -193,12 +193,30 @@ int row_tiles(const ba_problem* p) {
 // fan-out do).  One tile per KV head stays on 4-wave workgroups.
 struct SplitGeom {
   bool wide = false;
-  int tiles = 0;    // row tiles x KV heads
-  int target = 0;   // workgroups the planner aims for
+  int tiles = 0;       // row tiles x KV heads x sequences
+  int target = 0;      // workgroups the planner aims for
+  int key_align = 64;  // chunk lengths are multiples of this
+  int min_chunk = 256;
 };
+
+// Rows per workgroup of the fp32 walk and its split form (one wave).
+constexpr int kF32TileRows = 64;
+
+int f32_row_tiles(const ba_problem* p) {
+  int64_t flat = (int64_t)p->q_len * (p->n_q_heads / p->n_kv_heads);
+  return (int)((flat + kF32TileRows - 1) / kF32TileRows) * p->n_kv_heads * batch_of(p);
+}
 
 SplitGeom split_geom(const ba_problem* p) {
   SplitGeom sg;
+  if (p->dtype == BA_F32) {
+    // One-wave workgroups over 32-key LDS tiles: aim for four per compute unit.
+    sg.tiles = f32_row_tiles(p);
+    sg.target = 2 * kTargetWorkgroups;
+    sg.key_align = 32;
+    sg.min_chunk = 32;
+    return sg;
+  }
   const int64_t flat = (int64_t)p->q_len * (p->n_q_heads / p->n_kv_heads);
   const int64_t narrow = (flat + ba::kTileRows - 1) / ba::kTileRows;
   sg.wide = BA_SPLIT_WIDE && narrow >= 2;
@@ -225,8 +243,8 @@ SplitPlan plan_split(const std::vector<int64_t>& keys, const SplitGeom& geom) {
   int64_t want = (geom.target + tiles - 1) / (tiles > 0 ? tiles : 1);
   if (want < 1) want = 1;
   int64_t cl = (total + want - 1) / want;
-  cl = (cl + 63) / 64 * 64;
-  if (cl < 256) cl = 256;
+  cl = (cl + geom.key_align - 1) / geom.key_align * geom.key_align;
+  if (cl < geom.min_chunk) cl = geom.min_chunk;
   for (;;) {
     int64_t n = 0;
     for (int64_t k : keys) n += (k + cl - 1) / cl;
@@ -256,10 +274,14 @@ void partial_ptrs(void* ws, int64_t slots, int64_t R, float** m, float** l, floa
 }
 
 bool fwd_uses_split(const ba_problem* p) {
-  if (p->dtype != BA_BF16) return false;
   if (p->split_mode == 1) return false;
   if (p->split_mode == 2) return true;
-  return row_tiles(p) < kWalkMinWorkgroups;
+  return (p->dtype == BA_F32 ? f32_row_tiles(p) : row_tiles(p)) < kWalkMinWorkgroups;
+}
+
+hipError_t launch_split(const ba_problem* p, const ba::SplitArgs& a, int n_chunks, hipStream_t stream) {
+  return p->dtype == BA_F32 ? ba::launch_split_f32(a, n_chunks, p->head_dim, stream)
+                            : ba::launch_split_bf16(a, n_chunks, p->head_dim, stream);
 }
 
 // Full validation of a forward call; fills the visit list and split plan.
@@ -394,7 +416,7 @@ ba_status fwd_run(const ba_problem* p, const void* q, const ba_kv_block* blocks,
       a.chunk_begin[i] = sp.begin[i];
     }
     a.chunk_begin[a.n_seg] = sp.begin[a.n_seg];
-    hipError_t e = ba::launch_split_bf16(a, sp.n_chunks, D, stream);
+    hipError_t e = launch_split(p, a, sp.n_chunks, stream);
     if (e != hipSuccess) return hip_status(e, "fwd_block split launch");
   }
   if (!fin && !reset_state && sp.n_chunks == 0) return ok();
@@ -563,7 +585,7 @@ ba_status blockattn_bwd_block(const ba_problem* p, const void* q, const void* do
 size_t blockattn_shard_workspace_bytes(const ba_problem* p, const ba_kv_block* blocks, int32_t n_blocks) {
   if (check_problem(p, (const void*)256) != BA_OK || !blocks || n_blocks <= 0 || n_blocks > BLOCKATTN_MAX_VISITS)
     return 0;
-  if (p->dtype != BA_BF16 || p->q_len == 0) return 0;
+  if (p->q_len == 0) return 0;
   std::vector<int64_t> keys;
   for (int i = 0; i < n_blocks; ++i) {
     if (check_block(blocks[i], i, p) != BA_OK) return 0;
@@ -578,7 +600,6 @@ ba_status blockattn_shard_states(const ba_problem* p, const void* q, const ba_kv
                                  hipStream_t stream) {
   ba_status st = check_problem(p, q);
   if (st) return st;
-  if (p->dtype != BA_BF16) return fail(BA_ERR_UNSUPPORTED, "shard_states supports bf16 only");
   if (n_blocks <= 0 || n_blocks > BLOCKATTN_MAX_VISITS)
     return fail(BA_ERR_ORDER, "n_blocks %d outside [1, %d]", n_blocks, BLOCKATTN_MAX_VISITS);
   if (!blocks || !states_out) return fail(BA_ERR_NULL, "blocks or states_out is NULL");
@@ -616,7 +637,7 @@ ba_status blockattn_shard_states(const ba_problem* p, const void* q, const ba_kv
       a.chunk_begin[i] = sp.begin[i];
     }
     a.chunk_begin[n_blocks] = sp.begin[n_blocks];
-    hipError_t e = ba::launch_split_bf16(a, sp.n_chunks, D, stream);
+    hipError_t e = launch_split(p, a, sp.n_chunks, stream);
     if (e != hipSuccess) return hip_status(e, "shard_states split launch");
   }
   ba::MergeGroupArgs mg;

@@ -320,20 +320,6 @@ __global__ __launch_bounds__(64 * kWalkWaves, 1) void walk_kernel(WalkArgs a) {
     store_acc<D>(acc, lane_rows(a.qs, rc, wave, lane), lane, a.m, a.l, a.o, 0);
 }
 
-// Chunk `chunk` of the segment table as a segment of its own.
-__device__ inline Seg chunk_seg(const Seg* seg, int n_seg, const int32_t* chunk_begin, int chunk_len, int chunk) {
-  int s_i = 0;
-  while (s_i + 1 < n_seg && chunk_begin[s_i + 1] <= chunk) ++s_i;
-  const Seg& base = seg[s_i];
-  const int k_off = (chunk - chunk_begin[s_i]) * chunk_len;
-  Seg cs = base;
-  cs.k = (const uint16_t*)base.k + (int64_t)k_off * base.ks_t;
-  cs.v = (const uint16_t*)base.v + (int64_t)k_off * base.vs_t;
-  cs.pos0 = base.pos0 + k_off;
-  cs.n = min(chunk_len, base.n - k_off);
-  return cs;
-}
-
 // Partial state of one row tile over the keys of n_seg segments (get_seg(i)
 // returns segment i), written to a workspace slot.
 template <int D, int kAux, int W = 4, int TK = kTileKeys, class GetSeg>
@@ -474,7 +460,7 @@ __global__ __launch_bounds__(kWide ? 2 * kThreads : kThreads, kWide ? 1 : 2) voi
   const int total = a.qs.q_len * a.qs.G;
   const int f0 = tile * TR;
   const int f1 = min(f0 + TR, total);
-  const Seg cs = chunk_seg(a.seg, a.n_seg, a.chunk_begin, a.chunk_len, chunk);
+  const Seg cs = chunk_seg<uint16_t>(a.seg, a.n_seg, a.chunk_begin, a.chunk_len, chunk);
   partial_job<D, kAux, W, TK>(a.qs, f0, f1, g, b, cs, a.ws_m, a.ws_l, a.ws_o, (int64_t)chunk * a.R, (lds_char*)lds);
 }
 

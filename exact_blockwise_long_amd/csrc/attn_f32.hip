@@ -5,7 +5,10 @@
 // initial state, causal rule of section 5 -- with every product, sum and
 // exponential in fp32 on the vector ALUs.  One lane owns one query row and
 // keeps q, O, m, l in registers; 32-key K/V tiles are staged in LDS and read
-// by broadcast.  Meant for exactness checks at small sizes, not for speed.
+// by broadcast.  Meant for exactness checks at small sizes, not for speed.  A
+// call whose row tiles do not fill the GPU splits its keys into chunks walked
+// in parallel (split_f32_kernel) whose partial states merge afterwards, as
+// on the bf16 path.
 #include "internal.h"
 
 namespace ba {
@@ -14,15 +17,17 @@ namespace {
 constexpr int kRows = 64;   // one wave, one row per lane
 constexpr int kKeys = 32;   // keys per LDS tile
 
-template <int D>
-__global__ __launch_bounds__(kRows) void walk_f32_kernel(WalkArgs a) {
+// The recurrence for one workgroup's tile of 64 flat rows of KV head g of
+// sequence b over get_seg(0..n_seg): from the initial state when `reset`, else
+// from the state rows of (m_in, l_in, o_in); the result goes to state row
+// row_base + r of (m_out, l_out, o_out).  Every lane of the workgroup runs the
+// key loops (their barriers), also lanes past the tile's last row.
+template <int D, class GetSeg>
+__device__ inline void f32_tile(const QSide& qs, int b, int g, int tile, int n_seg, GetSeg get_seg, bool reset,
+                                const float* m_in, const float* l_in, const float* o_in, float* m_out, float* l_out,
+                                float* o_out, int64_t row_base) {
   __shared__ float ks[kKeys][D];
   __shared__ float vs[kKeys][D];
-  const QSide& qs = a.qs;
-  const int g = blockIdx.x % qs.Hkv;
-  const int rest = blockIdx.x / qs.Hkv;
-  const int b = rest % qs.B;       // sequence
-  const int tile = rest / qs.B;
   const int total = qs.q_len * qs.G;
   const int f0 = tile * kRows;
   const int f1 = min(f0 + kRows, total);
@@ -41,21 +46,21 @@ __global__ __launch_bounds__(kRows) void walk_f32_kernel(WalkArgs a) {
 #pragma unroll
   for (int d = 0; d < D; ++d) q[d] = qp[d];
   float m2, l;
-  if (a.reset) {
+  if (reset) {
     m2 = -INFINITY;
     l = 0.f;
 #pragma unroll
     for (int d = 0; d < D; ++d) o[d] = 0.f;
   } else {
-    float mm = a.m[srow];
+    float mm = m_in[srow];
     m2 = (mm == -INFINITY) ? -INFINITY : mm * kLog2e;
-    l = a.l[srow];
+    l = l_in[srow];
 #pragma unroll
-    for (int d = 0; d < D; ++d) o[d] = a.o[srow * D + d];
+    for (int d = 0; d < D; ++d) o[d] = o_in[srow * D + d];
   }
 
-  for (int si = 0; si < a.n_seg; ++si) {
-    const Seg& s = a.seg[si];
+  for (int si = 0; si < n_seg; ++si) {
+    const Seg& s = get_seg(si);
     int n = s.n;
     if (qs.causal) {
       int64_t lim = qpos_max - s.pos0 + 1;
@@ -102,10 +107,33 @@ __global__ __launch_bounds__(kRows) void walk_f32_kernel(WalkArgs a) {
     }
   }
   if (!valid) return;
-  a.m[srow] = (m2 == -INFINITY) ? -INFINITY : m2 * kLn2;
-  a.l[srow] = l;
+  const int64_t r = row_base + srow;
+  m_out[r] = (m2 == -INFINITY) ? -INFINITY : m2 * kLn2;
+  l_out[r] = l;
 #pragma unroll
-  for (int d = 0; d < D; ++d) a.o[srow * D + d] = o[d];
+  for (int d = 0; d < D; ++d) o_out[r * D + d] = o[d];
+}
+
+// Workgroups take the KV heads, then the sequences, then the row tiles.
+template <int D>
+__global__ __launch_bounds__(kRows) void walk_f32_kernel(WalkArgs a) {
+  const int g = blockIdx.x % a.qs.Hkv;
+  const int rest = blockIdx.x / a.qs.Hkv;
+  f32_tile<D>(a.qs, rest % a.qs.B, g, rest / a.qs.B, a.n_seg, [&](int i) -> const Seg& { return a.seg[i]; },
+              a.reset != 0, a.m, a.l, a.o, a.m, a.l, a.o, 0);
+}
+
+// The split form: workgroup (row tile, sequence, KV head) x chunk walks one
+// key chunk from the initial state and writes its partial state to workspace
+// slot `chunk` (see SplitArgs); the partial states merge afterwards.
+template <int D>
+__global__ __launch_bounds__(kRows) void split_f32_kernel(SplitArgs a) {
+  const int g = blockIdx.x % a.qs.Hkv;
+  const int rest = blockIdx.x / a.qs.Hkv;
+  const int chunk = blockIdx.y;
+  const Seg cs = chunk_seg<float>(a.seg, a.n_seg, a.chunk_begin, a.chunk_len, chunk);
+  f32_tile<D>(a.qs, rest % a.qs.B, g, rest / a.qs.B, 1, [&](int) -> const Seg& { return cs; }, true, nullptr,
+              nullptr, nullptr, a.ws_m, a.ws_l, a.ws_o, (int64_t)chunk * a.R);
 }
 
 }  // namespace
@@ -117,6 +145,16 @@ hipError_t launch_walk_f32(const WalkArgs& a, int D, hipStream_t s) {
     hipLaunchKernelGGL(walk_f32_kernel<128>, grid, dim3(kRows), 0, s, a);
   else
     hipLaunchKernelGGL(walk_f32_kernel<64>, grid, dim3(kRows), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_f32(const SplitArgs& a, int n_chunks, int D, hipStream_t s) {
+  const int tiles = (a.qs.q_len * a.qs.G + kRows - 1) / kRows;
+  dim3 grid(tiles * a.qs.Hkv * a.qs.B, n_chunks);
+  if (D == 128)
+    hipLaunchKernelGGL(split_f32_kernel<128>, grid, dim3(kRows), 0, s, a);
+  else
+    hipLaunchKernelGGL(split_f32_kernel<64>, grid, dim3(kRows), 0, s, a);
   return hipGetLastError();
 }
 

@@ -61,7 +61,7 @@ struct WalkArgs {
   float* fin_lse;
 };
 
-// Split: workgroup (row tile, KV head) x chunk; chunk c of the segment table
+// Split: workgroup (row tile, sequence, KV head) x chunk; chunk c of the segment table
 // lies in segment s with chunk_begin[s] <= c < chunk_begin[s+1] and covers
 // keys [(c - chunk_begin[s]) * chunk_len, ...) of it.  Each writes the partial
 // state of its rows over its chunk into slot c of the workspace:
@@ -211,10 +211,27 @@ constexpr int kWideTileRows = 256;   // row tile of the 8-wave split and fan-out
 #endif
 constexpr int kFanoutTargetWorkgroups = BA_FANOUT_TARGET_WG;
 
+// Chunk `chunk` of a split launch's segment table as a segment of its own
+// (T: the element type of K and V).
+template <typename T>
+__device__ inline Seg chunk_seg(const Seg* seg, int n_seg, const int32_t* chunk_begin, int chunk_len, int chunk) {
+  int s_i = 0;
+  while (s_i + 1 < n_seg && chunk_begin[s_i + 1] <= chunk) ++s_i;
+  const Seg& base = seg[s_i];
+  const int k_off = (chunk - chunk_begin[s_i]) * chunk_len;
+  Seg cs = base;
+  cs.k = (const T*)base.k + (int64_t)k_off * base.ks_t;
+  cs.v = (const T*)base.v + (int64_t)k_off * base.vs_t;
+  cs.pos0 = base.pos0 + k_off;
+  cs.n = min(chunk_len, base.n - k_off);
+  return cs;
+}
+
 hipError_t launch_walk_bf16(const WalkArgs& a, int D, hipStream_t s);
 hipError_t launch_split_bf16(const SplitArgs& a, int n_chunks, int D, hipStream_t s);
 hipError_t launch_fanout_bf16(const FanoutArgs& a, int n_jobs, int D, hipStream_t s);
 hipError_t launch_walk_f32(const WalkArgs& a, int D, hipStream_t s);
+hipError_t launch_split_f32(const SplitArgs& a, int n_chunks, int D, hipStream_t s);
 hipError_t launch_merge_groups(const MergeGroupArgs& a, int D, hipStream_t s);
 hipError_t launch_merge_ptrs(const MergePtrArgs& a, int D, hipStream_t s);
 hipError_t launch_finalize(const FinalizeArgs& a, int D, hipStream_t s);

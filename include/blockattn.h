@@ -101,7 +101,7 @@ typedef struct {
   float scale;            /* logit scale; <= 0 selects 1/sqrt(head_dim)        */
   int32_t causal;         /* non-zero: apply the causal rule                   */
   int32_t split_mode;     /* 0: automatic; 1: never split the keys (one pass in
-                             visit order); 2: always split (bf16 only).  Only
+                             visit order); 2: always split.  Only
                              rounding differs between the modes.              */
   int32_t batch;          /* independent sequences (0 or 1: one)               */
   int64_t q_stride_batch; /* elements between consecutive sequences of q      */
@@ -153,7 +153,7 @@ typedef struct {
  * fp32 accumulation and rounds P to bf16 (nearest-even) before PV; f32 runs
  * every step in fp32.
  *
- * When the query block has too few rows to fill the GPU (bf16 only) the keys
+ * When the query block has too few rows to fill the GPU the keys
  * are split into chunks computed in parallel and merged by log-sum-exp; that
  * needs `workspace` of blockattn_fwd_workspace_bytes() bytes (device memory,
  * 256-byte aligned).  Otherwise workspace may be NULL.
@@ -214,7 +214,7 @@ size_t blockattn_fwd_workspace_bytes(const ba_problem* p, const ba_kv_block* blo
  * For every block i < n_blocks, writes states_out[i] = the online-softmax
  * state of all query rows over block i alone (as if blockattn_fwd_block
  * visited only block i from the initial state).  states_out is a HOST array
- * of n_blocks states; they must not overlap.  bf16 only.  Needs
+ * of n_blocks states; they must not overlap.  bf16 or fp32.  Needs
  * blockattn_shard_workspace_bytes() bytes of workspace.  Errors as for
  * blockattn_fwd_block; n_blocks <= BLOCKATTN_MAX_VISITS. */
 ba_status blockattn_shard_states(const ba_problem* p, const void* q,

@@ -169,8 +169,12 @@ def test_split_needs_workspace(lib):
     assert _fwd(lib, p, _blocks(3), 3, None, 3, ws=FAKE, ws_bytes=need - 1) == 5
     # walk mode needs none
     assert lib.blockattn_fwd_workspace_bytes(ctypes.byref(_problem(split_mode=1)), _blocks(3), 3, None, 3) == 0
-    # the f32 path never splits
-    assert lib.blockattn_fwd_workspace_bytes(ctypes.byref(_problem(dtype=ba.BA_F32, split_mode=0)),
+    # the f32 path splits a query block too small to fill the GPU as well, unless told not to
+    f32 = _problem(dtype=ba.BA_F32, split_mode=0, q_stride_token=8 * 128)
+    need32 = lib.blockattn_fwd_workspace_bytes(ctypes.byref(f32), _blocks(3), 3, None, 3)
+    assert need32 > 0
+    assert _fwd(lib, f32, _blocks(3), 3, None, 3) == 5
+    assert lib.blockattn_fwd_workspace_bytes(ctypes.byref(_problem(dtype=ba.BA_F32, split_mode=1)),
                                              _blocks(3), 3, None, 3) == 0
 
 
@@ -178,10 +182,12 @@ def test_shard_states_validation(lib):
     p = _problem()
     sts = (ba.State * 2)(_state(), _state())
     assert lib.blockattn_shard_states(ctypes.byref(p), FAKE, _blocks(2), 0, sts, None, 0, None) == 4
-    assert lib.blockattn_shard_states(ctypes.byref(_problem(dtype=ba.BA_F32)), FAKE, _blocks(2), 2, sts,
-                                      None, 0, None) == 3
     assert lib.blockattn_shard_states(ctypes.byref(p), FAKE, _blocks(2), 2, sts, None, 0, None) == 5
     assert lib.blockattn_shard_workspace_bytes(ctypes.byref(p), _blocks(2), 2) > 0
+    # fp32 problems take the fp32 split kernel: the same workspace rule
+    f32 = _problem(dtype=ba.BA_F32)
+    assert lib.blockattn_shard_states(ctypes.byref(f32), FAKE, _blocks(2), 2, sts, None, 0, None) == 5
+    assert lib.blockattn_shard_workspace_bytes(ctypes.byref(f32), _blocks(2), 2) > 0
 
 
 def test_merge_validation(lib):

@@ -149,7 +149,7 @@ def test_batch_f32_equals_one_call_per_sequence():
     announce(f"batch f32 seed {seed} B={B} T={T} Hq={Hq} Hkv={Hkv} D={D} lens={lens} causal")
     q, k, v = make_batch(seed, B, T, Hq, Hkv, D, sum(lens), dtype="f32")
     qd, kd, vd = H.to_device(q), H.to_device(k), H.to_device(v)
-    kw = dict(n_kv_heads=Hkv, q_pos0=40, causal=True)
+    kw = dict(n_kv_heads=Hkv, q_pos0=40, causal=True, split_mode=1)
     st = ba.new_state(B * T * Hq, D)
     out, lse = ba.fwd_block_finalize(qd, blocks_of(kd, vd, lens), order, st, reset=True, out_dtype=torch.float32,
                                      **kw)
@@ -161,6 +161,16 @@ def test_batch_f32_equals_one_call_per_sequence():
         assert torch.equal(out[b * R:(b + 1) * R], o1) and torch.equal(lse[b * R:(b + 1) * R], l1)
         a_ref, lse_ref = oracle_seq(q, k, v, b, T, 40, True, 1.0 / np.sqrt(D), False)
         H.assert_close(H.host(out[b * R:(b + 1) * R]).reshape(T, Hq, D), a_ref, H.F32_TOL, f"f32 seq {b}")
+    # the key split (chunks planned for the whole batch) against the oracle
+    kw["split_mode"] = 2
+    st = ba.new_state(B * T * Hq, D)
+    out, lse = ba.fwd_block_finalize(qd, blocks_of(kd, vd, lens), order, st, reset=True, out_dtype=torch.float32,
+                                     **kw)
+    torch.cuda.synchronize()
+    for b in range(B):
+        a_ref, lse_ref = oracle_seq(q, k, v, b, T, 40, True, 1.0 / np.sqrt(D), False)
+        H.assert_close(H.host(out[b * R:(b + 1) * R]).reshape(T, Hq, D), a_ref, H.F32_TOL, f"f32 split seq {b}")
+        H.assert_close(H.host(lse[b * R:(b + 1) * R]).reshape(T, Hq), lse_ref, H.F32_TOL, f"f32 split seq {b} lse")
 
 
 def test_batch_strided_query_view():

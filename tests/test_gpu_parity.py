@@ -118,6 +118,44 @@ def test_f32_gqa_ragged(causal):
     check_state_vs_oracle(st, q, k, v, 60, causal, bf16=False, what="f32 gqa")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_f32_key_split_matches_walk_and_oracle(causal):
+    """The fp32 key split (chunks walked in parallel, partial states merged)
+    against the fp32 walk and the oracle, with a caller state carried in."""
+    lens = [200, 77, 129]
+    announce(f"f32 key split GQA 8/2 D64 T=90 lens {lens} causal={causal} seed 12")
+    q, k, v = make_case(12, 90, 8, 2, 64, lens, dtype="f32", qscale=1.0, kscale=1.0, vscale=1.0)
+    qd = H.to_device(q)
+    blocks = device_blocks(k, v, lens)
+    kw = dict(n_kv_heads=2, q_pos0=300, causal=causal)
+    assert ba.fwd_workspace_bytes(qd, blocks, None, split_mode=0, **kw) > 0   # small: splits by itself
+    outs = {}
+    for mode in (1, 2):
+        st = ba.new_state(90 * 8, 64)
+        ba.fwd_block(qd, blocks, [2], st, reset=True, split_mode=mode, **kw)      # one visit, then the rest
+        ba.fwd_block(qd, blocks, [0, 1], st, reset=False, split_mode=mode, **kw)
+        torch.cuda.synchronize()
+        check_state_vs_oracle(st, q, k, v, 300, causal, bf16=False, what=f"f32 split_mode {mode}")
+        outs[mode] = ba.finalize(st, torch.float32)
+    torch.cuda.synchronize()
+    H.assert_close(H.host(outs[2][0]), H.host(outs[1][0]), 1e-6, "split vs walk output")
+    H.assert_close(H.host(outs[2][1]), H.host(outs[1][1]), 1e-6, "split vs walk lse")
+
+
+def test_f32_shard_states_and_merge():
+    lens = [96, 130, 64]
+    announce(f"f32 shard states D128 T=40 Hq 4 Hkv 1 lens {lens} seed 13")
+    q, k, v = make_case(13, 40, 4, 1, 128, lens, dtype="f32", qscale=1.0, kscale=1.0, vscale=1.0)
+    qd = H.to_device(q)
+    blocks = device_blocks(k, v, lens)
+    states = [ba.new_state(40 * 4, 128) for _ in lens]
+    ba.shard_states(qd, blocks, states, n_kv_heads=1)
+    merged = ba.new_state(40 * 4, 128)
+    ba.merge_states(states, merged)
+    torch.cuda.synchronize()
+    check_state_vs_oracle(merged, q, k, v, 0, False, bf16=False, what="f32 shards merged")
+
+
 # ---------------------------------------------------------------- bf16 path
 
 BF16_CASES = [
