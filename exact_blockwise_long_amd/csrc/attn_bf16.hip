@@ -103,11 +103,14 @@ __device__ inline void tile_compute(const lds_char* stage, int lane, const bf16x
   bf16x8 pf[NCH][2];  // [key chunk of 32][qb]
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    float mx = -INFINITY;
+    // Two chains of three-operand maxima (v_max3_f32): 2 instructions per 4 scores.
+    float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-      mx = fmaxf(mx, fmaxf(fmaxf(s[kb][qb][0], s[kb][qb][1]), fmaxf(s[kb][qb][2], s[kb][qb][3])));
-    mx = wave_max_cols(mx) * c;            // tile max of this lane's row, base 2
+    for (int kb = 0; kb < NKB; ++kb) {
+      m0 = fmaxf(fmaxf(m0, s[kb][qb][0]), s[kb][qb][1]);
+      m1 = fmaxf(fmaxf(m1, s[kb][qb][2]), s[kb][qb][3]);
+    }
+    float mx = wave_max_cols(fmaxf(m0, m1)) * c;   // tile max of this lane's row, base 2
     acc.mt[qb] = fmaxf(acc.mt[qb], mx);
     const float m_old = acc.m2[qb];
     // Move the reference only when the tile max is more than kTau above it

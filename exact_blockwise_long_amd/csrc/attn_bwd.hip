@@ -243,21 +243,34 @@ struct BwdCfg {
   static constexpr int ROWB = D * 2;
   static constexpr int CPR = D / 8;
   static constexpr int TILEB = kRowTile * ROWB;        // one Q (or dO) tile
-  static constexpr int STAGEB = 2 * TILEB + 2 * kRowTile * 4;  // Q, dO, L2, D
   static constexpr int RPI = 64 / CPR;                 // rows per wave-wide 1 KiB load
   static constexpr int LPW = kRowTile / RPI / 4;       // loads per wave per tile
   static constexpr int DC = D / 32;
   static constexpr int DB = D / 16;
+  // LDS: the two stages' Q tiles, then their dO tiles, then per stage the
+  // rows' log-sum-exp and D (64 floats each).  Every Q and dO read then
+  // addresses from a per-lane base with an immediate offset below 64 KiB that
+  // folds in the stage.
+  static constexpr int QOFF = 0;
+  static constexpr int GOFF = 2 * TILEB;
+  static constexpr int LOFF = 4 * TILEB;
+  static constexpr int LSTAGE = 2 * kRowTile * 4;
+  static constexpr int LDSB = LOFF + 2 * LSTAGE;
 };
 
-// Issues the loads of query-row tile f0 .. f0 + 63 (flat rows of KV head g)
-// into the stage at `stage`: Q and dO rows (swizzled as the K/V tiles are), then the
-// rows' log-sum-exp and D.  Rows past the last are loaded as the last row; the
-// caller masks them.
+// Per-lane byte offsets of one row tile's loads: Q and dO rows (load j of
+// this lane) and, in waves 0 and 1, the log-sum-exp or D of row f0 + lane.
 template <int D>
-__device__ inline void issue_rows(const BwdArgs& a, __amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rg,
-                                  __amdgpu_buffer_rsrc_t rl, __amdgpu_buffer_rsrc_t rd, int f0, int g,
-                                  uint32_t stage, int wave, int lane) {
+struct RowOffs {
+  uint32_t q[BwdCfg<D>::LPW];
+  uint32_t l;
+};
+
+// The offsets of the loads of query-row tile f0 .. f0 + 63 (flat rows of KV
+// head g).  Rows past the last are loaded as the last row; the caller masks
+// them.
+template <int D>
+__device__ inline RowOffs<D> row_offsets(const BwdArgs& a, int f0, int g, int wave, int lane) {
   using C = BwdCfg<D>;
   const QSide& qs = a.qs;
   const uint32_t G = (uint32_t)qs.G;
@@ -265,36 +278,48 @@ __device__ inline void issue_rows(const BwdArgs& a, __amdgpu_buffer_rsrc_t rq, _
   const uint32_t st = (uint32_t)qs.qs_t, sh = (uint32_t)qs.qs_h;   // q spans < 4 GiB: 32-bit offsets
   const int rsub = lane / C::CPR;
   const int p = lane % C::CPR;
+  RowOffs<D> o;
 #pragma unroll
   for (int j = 0; j < C::LPW; ++j) {
     const int row = (wave * C::LPW + j) * C::RPI + rsub;
     const uint32_t f = min((uint32_t)(f0 + row), last);
     const uint32_t t = div_g(f, G, a.g_magic);
     const uint32_t h = (uint32_t)g * G + (f - t * G);
-    const uint32_t off = (t * st + h * sh) * 2u + (uint32_t)((p ^ swz<D>(row)) * 16);
-    const uint32_t dst = stage + (uint32_t)((wave * C::LPW + j) * C::RPI) * C::ROWB;
-    lds_dma16(rq, dst, off, 0);
-    lds_dma16(rg, dst + C::TILEB, off, 0);
+    o.q[j] = (t * st + h * sh) * 2u + (uint32_t)((p ^ swz<D>(row)) * 16);
   }
-  if (wave < 2) {
-    const uint32_t f = min((uint32_t)(f0 + lane), last);
-    const uint32_t t = div_g(f, G, a.g_magic);
-    const uint32_t h = (uint32_t)g * G + (f - t * G);
-    const uint32_t off = (t * (uint32_t)qs.Hq + h) * 4u;
-    lds_dma4(wave == 0 ? rl : rd, stage + 2 * C::TILEB + (uint32_t)(wave * kRowTile * 4), off, 0);
-  }
+  const uint32_t f = min((uint32_t)(f0 + lane), last);
+  const uint32_t t = div_g(f, G, a.g_magic);
+  const uint32_t h = (uint32_t)g * G + (f - t * G);
+  o.l = (t * (uint32_t)qs.Hq + h) * 4u;
+  return o;
 }
 
-// One tile of 64 query rows for one wave's 16 keys.
+// Issues the loads of one row tile into the stage whose Q tile is at `qdst`
+// (its dO tile at qdst + GOFF, its log-sum-exp and D at `ldst`): Q and dO
+// rows, swizzled as the K/V tiles are, then the rows' log-sum-exp and D.
 template <int D>
-__device__ inline void dkdv_tile(const lds_char* stage, int lane, const bf16x8 (&kf)[BwdCfg<D>::DC],
-                                 const bf16x8 (&vf)[BwdCfg<D>::DC], f32x4 (&dk)[BwdCfg<D>::DB],
-                                 f32x4 (&dv)[BwdCfg<D>::DB], float c, bool need_mask, int f0, int f_begin,
-                                 int f_end) {
+__device__ inline void issue_rows(__amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rg, __amdgpu_buffer_rsrc_t rl,
+                                  __amdgpu_buffer_rsrc_t rd, const RowOffs<D>& o, uint32_t qdst, uint32_t ldst,
+                                  int wave) {
   using C = BwdCfg<D>;
-  const lds_char* ql = stage;
-  const lds_char* gl = stage + C::TILEB;
-  const float* l2s = (const float*)(stage + 2 * C::TILEB);
+#pragma unroll
+  for (int j = 0; j < C::LPW; ++j) {
+    const uint32_t dst = qdst + (uint32_t)((wave * C::LPW + j) * C::RPI) * C::ROWB;
+    lds_dma16(rq, dst, o.q[j], 0);
+    lds_dma16(rg, dst + C::GOFF, o.q[j], 0);
+  }
+  if (wave < 2) lds_dma4(wave == 0 ? rl : rd, ldst + (uint32_t)(wave * kRowTile * 4), o.l, 0);
+}
+
+// One tile of 64 query rows for one wave's 16 keys: the stage's Q tile at
+// `ql`, its dO tile at `gl`, the rows' log-sum-exp and D at `ls`.
+template <int D>
+__device__ inline void dkdv_tile(const lds_char* ql, const lds_char* gl, const lds_char* ls, int lane,
+                                 const bf16x8 (&kf)[BwdCfg<D>::DC], const bf16x8 (&vf)[BwdCfg<D>::DC],
+                                 f32x4 (&dk)[BwdCfg<D>::DB], f32x4 (&dv)[BwdCfg<D>::DB], float c, bool need_mask,
+                                 int f0, int f_begin, int f_end) {
+  using C = BwdCfg<D>;
+  const float* l2s = (const float*)ls;
   const float* dls = l2s + kRowTile;
   const int lr = lane & 15;
   const int lg = lane >> 4;
@@ -390,7 +415,7 @@ __device__ inline void dkdv_tile(const lds_char* stage, int lane, const bf16x8 (
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdArgs a) {
   using C = BwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) char lds[2 * C::STAGEB];
+  __shared__ __attribute__((aligned(16))) char lds[C::LDSB];
   const QSide& qs = a.qs;
   const int Hkv = qs.Hkv;
   const int g = blockIdx.x % Hkv;
@@ -455,22 +480,52 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdArgs a) {
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse + row0, a.rows_bytes);
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.delta + row0, a.rows_bytes);
     const uint32_t lds_addr = (uint32_t)(size_t)(lds_char*)lds;
+    // When the group size divides the row tile, the rows of tile t are those
+    // of tile 0 moved by 64 t / G tokens: each lane's offsets are computed once
+    // and stepped.  A tile that reaches past the last row (clamped loads), or
+    // any tile when G does not divide 64, computes them in full.
+    const bool stepped = kRowTile % qs.G == 0;
+    RowOffs<D> base = {};
+    if (stepped) base = row_offsets<D>(a, 0, g, wave, lane);
+    const uint32_t tok_step = stepped ? (uint32_t)(kRowTile / qs.G) : 0u;
+    const uint32_t q_step = tok_step * (uint32_t)qs.qs_t * 2u;
+    const uint32_t l_step = tok_step * (uint32_t)qs.Hq * 4u;
+    auto issue = [&](int t, int stage) {
+      RowOffs<D> o;
+      if (stepped && (t + 1) * kRowTile <= total) {
+        o = base;
+#pragma unroll
+        for (int j = 0; j < C::LPW; ++j) o.q[j] += (uint32_t)t * q_step;
+        o.l += (uint32_t)t * l_step;
+      } else {
+        o = row_offsets<D>(a, t * kRowTile, g, wave, lane);
+      }
+      issue_rows<D>(rq, rg, rl, rd, o, lds_addr + (uint32_t)(C::QOFF + stage * C::TILEB),
+                    lds_addr + (uint32_t)(C::LOFF + stage * C::LSTAGE), wave);
+    };
+    // One row tile in stage `cur` (a constant in each unrolled copy below, so
+    // the stage's LDS offsets are immediates): wait for it, let the next one
+    // start loading into the other stage, multiply.
+    auto step = [&](int t, int cur) {
+      wait_all_loads();
+      __syncthreads();
+      if (t > t_begin) issue(t - 1, cur ^ 1);
+      const int f0 = t * kRowTile;
+      const bool need_mask = (k0 + kTileKeys > n_keys) || (f0 + kRowTile > total) || (f0 < full_from);
+      const lds_char* l = (const lds_char*)lds;
+      dkdv_tile<D>(l + C::QOFF + cur * C::TILEB, l + C::GOFF + cur * C::TILEB, l + C::LOFF + cur * C::LSTAGE, lane,
+                   kf, vf, dk, dv, qs.c, need_mask, f0, f_begin, f_end);
+    };
     // Row tiles are walked from the last one down: every workgroup of a KV
     // head then starts at the same row tile and the resident ones stream Q
     // and dO in step, so each tile is fetched once into L2 and read from there
     // by the others (the causal rule only moves where a workgroup stops).
-    issue_rows<D>(a, rq, rg, rl, rd, (t_end - 1) * kRowTile, g, lds_addr, wave, lane);
-    for (int t = t_end - 1; t >= t_begin; --t) {
-      const int cur = (t_end - 1 - t) & 1;
-      wait_all_loads();
-      __syncthreads();
-      if (t > t_begin)
-        issue_rows<D>(a, rq, rg, rl, rd, (t - 1) * kRowTile, g, lds_addr + (uint32_t)((cur ^ 1) * C::STAGEB),
-                      wave, lane);
-      const int f0 = t * kRowTile;
-      const bool need_mask = (k0 + kTileKeys > n_keys) || (f0 + kRowTile > total) || (f0 < full_from);
-      dkdv_tile<D>((const lds_char*)lds + cur * C::STAGEB, lane, kf, vf, dk, dv, qs.c, need_mask, f0, f_begin,
-                   f_end);
+    issue(t_end - 1, 0);
+    for (int t = t_end - 1;;) {
+      step(t, 0);
+      if (--t < t_begin) break;
+      step(t, 1);
+      if (--t < t_begin) break;
     }
     wait_all_loads();
   }
