@@ -331,16 +331,22 @@ __device__ inline void dkdv_tile(const lds_char* ql, const lds_char* gl, const l
     s[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
     dp[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  // Each 32-wide d chunk: its eight Q and dO fragment reads first, then the
+  // eight products, so the reads' LDS latency overlaps.
 #pragma unroll
   for (int dc = 0; dc < C::DC; ++dc) {
+    bf16x8 qa[4], ga[4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       const int row = 16 * rb + lr;
       const int off = row * C::ROWB + (((4 * dc + lg) ^ swz<D>(row)) * 16);
-      const bf16x8 qa = *(const lds_bf16x8*)(ql + off);
-      const bf16x8 ga = *(const lds_bf16x8*)(gl + off);
-      s[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[dc], s[rb], 0, 0, 0);
-      dp[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga, vf[dc], dp[rb], 0, 0, 0);
+      qa[rb] = *(const lds_bf16x8*)(ql + off);
+      ga[rb] = *(const lds_bf16x8*)(gl + off);
+    }
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      s[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rb], kf[dc], s[rb], 0, 0, 0);
+      dp[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga[rb], vf[dc], dp[rb], 0, 0, 0);
     }
   }
   // A row that saw no key has L = -inf and gives exp2(+inf) here; every pair
