@@ -67,6 +67,42 @@ def test_random_forward(seed):
     check_state_vs_oracle(st, q, k, v, c["q_pos0"], c["causal"], what=f"random seed {seed}")
 
 
+def draw_long(seed):
+    """Longer draws than draw(): query blocks of 257-1024 tokens against blocks
+    of up to 1000 keys (several row and key tiles, the wide workgroups, key
+    splits across many chunks), every fifth seed on the fp32 path at sizes its
+    vector-ALU kernels finish quickly."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    D = int(g.choice([64, 128]))
+    Hkv = int(g.choice([1, 2, 4, 8]))
+    G = int(g.choice([1, 2, 4, 8, 16]))
+    while Hkv * G > 64:
+        G //= 2
+    f32 = seed % 5 == 0
+    n_blocks = int(g.integers(1, 7))
+    pool = [0, 1, 31, 127, 128, 129, 255, 256, 300] if f32 else [0, 1, 127, 128, 255, 256, 300, 511, 513, 1000]
+    lens = [int(x) for x in g.choice(pool, size=n_blocks)]
+    if sum(lens) == 0:
+        lens[0] = 33
+    L = sum(lens)
+    T = int(g.choice([17, 65, 130] if f32 else [257, 511, 700, 1024]))
+    causal = bool(g.integers(0, 2))
+    q_pos0 = max(int(g.integers(-T // 2, L + 40)), 0) if causal else 0
+    return dict(D=D, Hkv=Hkv, Hq=Hkv * G, lens=lens, T=T, causal=causal, q_pos0=q_pos0,
+                order=g.permutation(n_blocks).tolist(), split_mode=int(g.integers(0, 3)),
+                per_visit=bool(g.integers(0, 2)), f32=f32)
+
+
+@pytest.mark.parametrize("seed", range(6000, 6048))
+def test_random_forward_long(seed):
+    c = draw_long(seed)
+    announce(f"random long forward seed {seed}: {c}")
+    q, k, v = make_case(seed, c["T"], c["Hq"], c["Hkv"], c["D"], c["lens"], dtype="f32" if c["f32"] else "bf16")
+    st = run_fwd(q, k, v, c["lens"], c["order"], Hkv=c["Hkv"], q_pos0=c["q_pos0"], causal=c["causal"],
+                 split_mode=c["split_mode"], per_visit=c["per_visit"])
+    check_state_vs_oracle(st, q, k, v, c["q_pos0"], c["causal"], bf16=not c["f32"], what=f"random long seed {seed}")
+
+
 @pytest.mark.parametrize("seed", range(2000, 2032))
 def test_random_backward(seed):
     c = draw(seed)
