@@ -1,6 +1,7 @@
 """GPU parity at the edges of the C ABI, against the CPU fp64 oracle: the
 largest visit count one call accepts, empty and one-key blocks, MHA decode
-(G = 1) and wide groups (G = 16), strided views out of fused QKV buffers,
+(G = 1), wide groups (G = 16) and multi-query attention (G = 64, also in the
+fan-out decode), strided views out of fused QKV buffers,
 head-major layouts, an explicit logit scale, every split mode, and two
 calls running at once on two streams.  Every case prints its name,
 shape and seed before it touches the GPU."""
@@ -79,9 +80,11 @@ def test_max_visits_in_one_call(split_mode):
 
 
 @pytest.mark.parametrize("Hq,Hkv,T,causal", [(8, 8, 1, False), (8, 8, 1, True), (16, 1, 33, True),
-                                             (16, 1, 33, False)])
+                                             (16, 1, 33, False), (64, 1, 33, True), (64, 1, 1, False)])
 def test_group_sizes_and_decode(Hq, Hkv, T, causal):
-    """MHA (G = 1) with a single query token, and a 16-wide group."""
+    """MHA (G = 1) with a single query token, a 16-wide group, and multi-query
+    attention (64 query heads on one KV head: several row tiles per token
+    block, the wide workgroups)."""
     seed, D, lens = 82, 128, [300, 1, 129]
     announce(f"groups: Hq={Hq} Hkv={Hkv} T={T} causal={causal} lens={lens} seed {seed}")
     g = synth.rng(seed)
@@ -92,6 +95,26 @@ def test_group_sizes_and_decode(Hq, Hkv, T, causal):
     for mode in (0, 1, 2):
         run_and_check(q, k, v, lens, [2, 0, 1], Hkv=Hkv, q_pos0=L - T, causal=causal, split_mode=mode,
                       what=f"G={Hq // Hkv} T={T} mode {mode}")
+
+
+@pytest.mark.parametrize("nb", [16, 1])
+def test_fanout_multi_query(nb):
+    """Fan-out decode with 64 query heads on one KV head: 64 rows per branch,
+    so 16 branches make one KV head's 1024 rows (the wide launch)."""
+    seed, Hq, Hkv, D, P, S = 83, 64, 1, 128, 3000, 257
+    announce(f"fanout multi-query: nb={nb} Hq={Hq} Hkv={Hkv} D={D} P={P} S={S} seed {seed}")
+    g = synth.rng(seed)
+    q = synth.normal(g, (nb, Hq, D), 0.5, "bf16")
+    pk = synth.normal(g, (P, Hkv, D), 0.5, "bf16")
+    pv = synth.normal(g, (P, Hkv, D), 0.5, "bf16")
+    sk = synth.normal(g, (nb, S, Hkv, D), 0.5, "bf16")
+    sv = synth.normal(g, (nb, S, Hkv, D), 0.5, "bf16")
+    out, lse = ba.fanout_prefix_decode(*(H.to_device(t) for t in (q, pk, pv, sk, sv)))
+    torch.cuda.synchronize()
+    a_ref, lse_ref = ora.fanout_decode(q.f64(), pk.f64(), pv.f64(), sk.f64(), sv.f64(), 1.0 / np.sqrt(D))
+    stats = H.assert_bf16_out(H.host(out), a_ref, f"fanout multi-query nb={nb}")
+    H.assert_close(H.host(lse), lse_ref, H.BF16_LSE, "lse")
+    print(f"    max/mean abs err {stats[0]:.2e}/{stats[1]:.2e}", flush=True)
 
 
 def test_strided_views_and_explicit_scale():
