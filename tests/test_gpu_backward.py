@@ -139,6 +139,21 @@ def test_backward_matches_oracle(case, per_visit):
             assert not dk[dead].any() and not dv[dead].any(), "gradient on keys no query sees"
 
 
+def test_backward_positions_beyond_32_bits():
+    """The backward of a causal walk whose absolute positions start at 3e9."""
+    seed, T, Hq, Hkv, D, lens, order = 47, 90, 8, 2, 128, [100, 64, 129], [2, 0, 1]
+    base = 3_000_000_000
+    q_pos0 = base + 120
+    announce(f"bwd positions past 2^31: keys at {base}.., q_pos0={q_pos0}, T={T}, lens={lens}, seed {seed}")
+    q, k, v, do = make_case(seed, T, Hq, Hkv, D, lens)
+    dq, dk, dv = gpu_grads(q, k, v, do, lens, order, Hkv=Hkv, q_pos0=q_pos0, causal=True, per_visit=True,
+                           kpos0=base)
+    rq, rk, rv = oracle_grads(q, k, v, do, q_pos0, True, kpos0=base)
+    check_grad(dq, rq, "dQ")
+    check_grad(dk, rk, "dK")
+    check_grad(dv, rv, "dV")
+
+
 def test_backward_deterministic():
     seed, T, Hq, Hkv, D, lens, order, q_pos0, causal = CASES[0]
     announce(f"bwd determinism seed {seed}")

@@ -36,16 +36,17 @@ def _gpu():
 
 
 def run_and_check(q, k, v, lens, order, *, Hkv, q_pos0, causal, split_mode, scale=0.0, qd=None, kd=None, vd=None,
-                  what=""):
-    """fwd_block over blocks cut from k, v in the given lengths (positions in
-    block order), then finalize; compared with the oracle's attention."""
+                  what="", kpos0=0):
+    """fwd_block over blocks cut from k, v in the given lengths (keys at
+    positions kpos0, kpos0 + 1, ... in block order), then finalize; compared
+    with the oracle's attention."""
     T, Hq, D = q.shape
     qd = H.to_device(q) if qd is None else qd
     kd = H.to_device(k) if kd is None else kd
     vd = H.to_device(v) if vd is None else vd
     blocks, off = [], 0
     for n in lens:
-        blocks.append((kd[off:off + n], vd[off:off + n], off))
+        blocks.append((kd[off:off + n], vd[off:off + n], kpos0 + off))
         off += n
     st = ba.new_state(T * Hq, D)
     ba.fwd_block(qd, blocks, order, st, reset=True, n_kv_heads=Hkv, q_pos0=q_pos0, causal=causal,
@@ -53,7 +54,8 @@ def run_and_check(q, k, v, lens, order, *, Hkv, q_pos0, causal, split_mode, scal
     out, lse = ba.finalize(st)
     torch.cuda.synchronize()
     s = scale if scale > 0 else 1.0 / np.sqrt(D)
-    a_ref, _, _, lse_ref = ora.attend(q.f64(), k.f64(), v.f64(), s, q_pos0 + np.arange(T), None, causal)
+    a_ref, _, _, lse_ref = ora.attend(q.f64(), k.f64(), v.f64(), s, q_pos0 + np.arange(T),
+                                      kpos0 + np.arange(k.shape[0]), causal)
     stats = H.assert_bf16_out(H.host(out).reshape(T, Hq, D), a_ref, what)
     H.assert_close(H.host(lse).reshape(T, Hq), lse_ref, H.BF16_LSE, what + " lse")
     print(f"    {what}: max/mean abs err {stats[0]:.2e}/{stats[1]:.2e}", flush=True)
@@ -77,6 +79,25 @@ def test_max_visits_in_one_call(split_mode):
     v = synth.normal(g, (L, Hkv, D), 0.5, "bf16")
     run_and_check(q, k, v, lens, order, Hkv=Hkv, q_pos0=q_pos0, causal=True, split_mode=split_mode,
                   what=f"{MAX_VISITS} visits mode {split_mode}")
+
+
+@pytest.mark.parametrize("split_mode", [0, 1, 2])
+def test_positions_beyond_32_bits(split_mode):
+    """A causal walk whose absolute positions start at 3e9 (past 2^31): the
+    queries sit inside the keys, so blocks are wholly visible, straddle the
+    diagonal or lie wholly in the future."""
+    seed, T, Hq, Hkv, D, lens = 84, 150, 8, 2, 128, [200, 65, 300, 129]
+    base = 3_000_000_000
+    L = sum(lens)
+    q_pos0 = base + 260
+    announce(f"positions past 2^31: keys at {base}..{base + L - 1}, q_pos0={q_pos0}, T={T}, mode {split_mode}, "
+             f"seed {seed}")
+    g = synth.rng(seed)
+    q = synth.normal(g, (T, Hq, D), 0.5, "bf16")
+    k = synth.normal(g, (L, Hkv, D), 0.5, "bf16")
+    v = synth.normal(g, (L, Hkv, D), 0.5, "bf16")
+    run_and_check(q, k, v, lens, [3, 1, 0, 2], Hkv=Hkv, q_pos0=q_pos0, causal=True, split_mode=split_mode,
+                  kpos0=base, what=f"positions past 2^31 mode {split_mode}")
 
 
 @pytest.mark.parametrize("Hq,Hkv,T,causal", [(8, 8, 1, False), (8, 8, 1, True), (16, 1, 33, True),
