@@ -154,6 +154,24 @@ def test_backward_positions_beyond_32_bits():
     check_grad(dv, rv, "dV")
 
 
+def test_backward_single_key_closed_form():
+    """One visible key: every row's softmax weight on it is 1, so dP equals D
+    row by row, dS = P (dP - D) = 0, and dQ = dK = 0 while dV is the sum of dO
+    over the rows.  The GPU's dP and D are two fp32 sums rounded differently,
+    so dQ and dK come out at rounding level, not exactly 0."""
+    seed, T, Hq, Hkv, D = 48, 65, 16, 2, 128
+    lens = [0, 1]
+    announce(f"bwd single key: T={T} Hq={Hq} Hkv={Hkv} D={D} lens={lens} seed {seed}")
+    q, k, v, do = make_case(seed, T, Hq, Hkv, D, lens)
+    dq, dk, dv = gpu_grads(q, k, v, do, lens, [1, 0], Hkv=Hkv, q_pos0=0, causal=True, per_visit=False)
+    g = do.f64().reshape(T, Hkv, Hq // Hkv, D)
+    dv_ref = g.sum(axis=(0, 2))[None]                       # [1, Hkv, D]
+    print(f"    max |dQ| {np.abs(dq).max():.2e}, max |dK| {np.abs(dk).max():.2e}, "
+          f"max |dV - sum dO| {np.abs(dv - dv_ref).max():.2e}", flush=True)
+    assert np.abs(dq).max() <= 1e-5 and np.abs(dk).max() <= 1e-5
+    assert np.abs(dv - dv_ref).max() <= 1e-4 * max(1.0, np.abs(dv_ref).max())
+
+
 def test_backward_deterministic():
     seed, T, Hq, Hkv, D, lens, order, q_pos0, causal = CASES[0]
     announce(f"bwd determinism seed {seed}")
