@@ -109,6 +109,48 @@ def test_batch_walk_equals_one_call_per_sequence(case):
         H.assert_close(H.host(lse2[b * R:(b + 1) * R]).reshape(T, Hq), lse_ref, H.BF16_LSE, f"seq {b} lse")
 
 
+@pytest.mark.parametrize("seed", range(7000, 7024))
+def test_batch_random(seed):
+    """Seeded random batched problems: batch 2-5, group sizes 1-8, ragged and
+    empty blocks, causal or not, shared or per-sequence keys, every split mode.
+    Without a key split each sequence must equal its own call bit for bit; every
+    sequence must match the oracle."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    B = int(g.choice([2, 3, 5]))
+    D = int(g.choice([64, 128]))
+    Hkv = int(g.choice([1, 2, 8]))
+    Hq = Hkv * int(g.choice([1, 4, 8]))
+    n_blocks = int(g.integers(1, 5))
+    lens = [int(x) for x in g.choice([0, 1, 63, 64, 65, 129, 300], size=n_blocks)]
+    if sum(lens) == 0:
+        lens[0] = 40
+    L = sum(lens)
+    T = int(g.choice([1, 17, 65, 200]))
+    causal = bool(g.integers(0, 2))
+    q_pos0 = max(int(g.integers(-T // 2, L + 20)), 0) if causal else 0
+    shared = bool(g.integers(0, 2))
+    mode = int(g.integers(0, 3))
+    order = g.permutation(n_blocks).tolist()
+    announce(f"batch random seed {seed}: B={B} T={T} Hq={Hq} Hkv={Hkv} D={D} lens={lens} order={order} "
+             f"q_pos0={q_pos0} causal={causal} shared_kv={shared} split_mode={mode}")
+    q, k, v = make_batch(seed, B, T, Hq, Hkv, D, L, shared_kv=shared)
+    qd, kd, vd = H.to_device(q), H.to_device(k), H.to_device(v)
+    kw = dict(n_kv_heads=Hkv, q_pos0=q_pos0, causal=causal, split_mode=mode)
+    st = ba.new_state(B * T * Hq, D)
+    out, lse = ba.fwd_block_finalize(qd, blocks_of(kd, vd, lens), order, st, reset=True, **kw)
+    torch.cuda.synchronize()
+    R = T * Hq
+    for b in range(B):
+        if mode == 1:
+            o1, l1 = per_sequence(qd, kd, vd, lens, order, b, shared, **kw)
+            torch.cuda.synchronize()
+            assert torch.equal(out[b * R:(b + 1) * R], o1) and torch.equal(lse[b * R:(b + 1) * R], l1), \
+                f"sequence {b} differs from its own call"
+        a_ref, lse_ref = oracle_seq(q, k, v, b, T, q_pos0, causal, 1.0 / np.sqrt(D), shared)
+        H.assert_bf16_out(H.host(out[b * R:(b + 1) * R]).reshape(T, Hq, D), a_ref, f"seq {b}")
+        H.assert_close(H.host(lse[b * R:(b + 1) * R]).reshape(T, Hq), lse_ref, H.BF16_LSE, f"seq {b} lse")
+
+
 def test_batch_split_against_oracle():
     seed, B, T, Hq, Hkv, D, lens, order = 104, 3, 40, 8, 2, 128, [700, 333], [1, 0]
     announce(f"batch split seed {seed} B={B} T={T} Hq={Hq} Hkv={Hkv} D={D} lens={lens} causal")
