@@ -323,27 +323,51 @@ __global__ __launch_bounds__(64 * kWalkWaves, 1) void walk_kernel(WalkArgs a) {
     store_acc<D>(acc, lane_rows(a.qs, rc, wave, lane), lane, a.m, a.l, a.o, 0);
 }
 
-// Partial state of one row tile over the keys of n_seg segments (get_seg(i)
-// returns segment i), written to a workspace slot.
-template <int D, int kAux, int W = 4, int TK = kTileKeys, class GetSeg>
-__device__ inline void partial_job_segs(const QSide& qs, int f0, int f1, int g, int b, int n_seg, GetSeg get_seg,
-                                        float* ws_m, float* ws_l, float* ws_o, int64_t row_base, lds_char* lds) {
-  const RowCtx rc = make_rowctx(qs, f0, f1, g, b);
+// The query side of a job: its rows' bookkeeping and Q fragments.  The Q
+// loads are issued here and waited for only at the first product, so a job
+// that must load something else first (a page table) issues both together.
+template <int D>
+struct JobQ {
+  RowCtx rc;
+  LaneRows lr;
+  bool wave_active;
+  bf16x8 qf[2][Cfg<D>::DC];
+};
+
+template <int D>
+__device__ inline JobQ<D> job_q(const QSide& qs, int f0, int f1, int g, int b) {
+  JobQ<D> j;
+  j.rc = make_rowctx(qs, f0, f1, g, b);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const LaneRows lr = lane_rows(qs, rc, wave, lane);
-  const bool wave_active = f0 + wave * 32 < f1;
-  bf16x8 qf[2][Cfg<D>::DC];
-  load_q<D>(lr, lane, qf);
+  j.lr = lane_rows(qs, j.rc, wave, lane);
+  j.wave_active = f0 + wave * 32 < f1;
+  load_q<D>(j.lr, lane, j.qf);
+  return j;
+}
+
+// Partial state of a job's rows over the keys of n_seg segments (get_seg(i)
+// returns segment i), written to a workspace slot.
+template <int D, int kAux, int W, int TK, class GetSeg>
+__device__ inline void job_walk(const QSide& qs, const JobQ<D>& j, int n_seg, GetSeg get_seg, float* ws_m,
+                                float* ws_l, float* ws_o, int64_t row_base, lds_char* lds) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   Acc<D> acc;
   init_acc<D>(acc);
   run_segments<D, kAux, W, TK>(
-      qs, rc, n_seg, get_seg,
+      qs, j.rc, n_seg, get_seg,
       [&](const lds_char* stage, bool need_mask, int n_valid, int krel) {
-        tile_compute<D, TK>(stage, lane, qf, acc, qs.c, need_mask, qs.causal != 0, n_valid, krel, lr.qrel);
+        tile_compute<D, TK>(stage, lane, j.qf, acc, qs.c, need_mask, qs.causal != 0, n_valid, krel, j.lr.qrel);
       },
-      lds, wave_active);
-  store_acc<D>(acc, lane_rows(qs, rc, wave, lane), lane, ws_m, ws_l, ws_o, row_base);
+      lds, j.wave_active);
+  store_acc<D>(acc, lane_rows(qs, j.rc, wave, lane), lane, ws_m, ws_l, ws_o, row_base);
+}
+
+template <int D, int kAux, int W = 4, int TK = kTileKeys, class GetSeg>
+__device__ inline void partial_job_segs(const QSide& qs, int f0, int f1, int g, int b, int n_seg, GetSeg get_seg,
+                                        float* ws_m, float* ws_l, float* ws_o, int64_t row_base, lds_char* lds) {
+  job_walk<D, kAux, W, TK>(qs, job_q<D>(qs, f0, f1, g, b), n_seg, get_seg, ws_m, ws_l, ws_o, row_base, lds);
 }
 
 template <int D, int kAux, int W = 4, int TK = kTileKeys>
@@ -507,14 +531,14 @@ __global__ __launch_bounds__(kWide ? 2 * kThreads : kThreads, kWide ? 1 : 2) voi
     const int k_end = min(k_off + a.chunk_len, a.prefix.n);
     if (a.prefix_pages) {
       const PageIds pi = load_page_ids(a.prefix_pages, k_off, k_end, a.page_len);
+      const JobQ<D> jq = job_q<D>(a.qs, f0, f1, g, 0);   // Q loads in flight with the page ids
       if (pages_corrupt(pi, k_off, k_end, a.page_len, a.n_pool_pages)) {
         store_corrupt<D, W>(a.qs, f0, f1, g, a.ws_m, a.ws_l, a.ws_o, (int64_t)chunk * a.R);
         return;
       }
-      partial_job_segs<D, kAux, W, TKP>(
-          a.qs, f0, f1, g, 0, paged_segments(k_off, k_end, a.page_len),
-          [&](int i) { return paged_seg<D>(a, pi, k_off, k_end, i, 0); }, a.ws_m, a.ws_l, a.ws_o,
-          (int64_t)chunk * a.R, (lds_char*)lds);
+      job_walk<D, kAux, W, TKP>(a.qs, jq, paged_segments(k_off, k_end, a.page_len),
+                                [&](int i) { return paged_seg<D>(a, pi, k_off, k_end, i, 0); }, a.ws_m, a.ws_l,
+                                a.ws_o, (int64_t)chunk * a.R, (lds_char*)lds);
       return;
     }
     Seg sg = a.prefix;
@@ -552,13 +576,14 @@ __global__ __launch_bounds__(kWide ? 2 * kThreads : kThreads, kWide ? 1 : 2) voi
     const int f1 = min(f0 + TR, (b + 1) * TG);
     if (a.suffix_pages) {
       const PageIds pi = load_page_ids(a.suffix_pages + (int64_t)b * a.suffix_pages_per_branch, 0, a.S, a.page_len);
+      const JobQ<D> jq = job_q<D>(qs, f0, f1, g, 0);   // Q loads in flight with the page ids
       if (pages_corrupt(pi, 0, a.S, a.page_len, a.n_pool_pages)) {
         store_corrupt<D, W>(qs, f0, f1, g, a.ws_m, a.ws_l, a.ws_o, (int64_t)a.suffix_slot * a.R);
         continue;
       }
-      partial_job_segs<D, kAux, W>(
-          qs, f0, f1, g, 0, paged_segments(0, a.S, a.page_len), [&](int i) { return paged_seg<D>(a, pi, 0, a.S, i, 0); },
-          a.ws_m, a.ws_l, a.ws_o, (int64_t)a.suffix_slot * a.R, (lds_char*)lds);
+      job_walk<D, kAux, W, kTileKeys>(qs, jq, paged_segments(0, a.S, a.page_len),
+                                      [&](int i) { return paged_seg<D>(a, pi, 0, a.S, i, 0); }, a.ws_m, a.ws_l,
+                                      a.ws_o, (int64_t)a.suffix_slot * a.R, (lds_char*)lds);
       continue;
     }
     Seg sg;
