@@ -574,7 +574,7 @@ ba_status blockattn_bwd_block(const ba_problem* p, const void* q, const void* do
     a.dk[a.n_seg] = dk[j];
     a.dv[a.n_seg] = dv[j];
     a.tile_begin[a.n_seg] = tiles;
-    tiles += (int)((blocks[j].len + 63) / 64);
+    tiles += (int)((blocks[j].len + ba::kDkvKeys - 1) / ba::kDkvKeys);
     ++a.n_seg;
   }
   a.tile_begin[a.n_seg] = tiles;

@@ -236,7 +236,9 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void dq_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------- dK, dV
 
-constexpr int kRowTile = 64;   // query rows per LDS stage of the dK/dV kernel
+constexpr int kRowTile = 64;    // query rows per LDS stage of the dK/dV kernel
+constexpr int kDkvWaves = 8;    // four pairs of waves, each pair on 32 of the workgroup's kDkvKeys keys
+static_assert(kDkvKeys == 32 * kDkvWaves / 2, "a dK/dV workgroup covers 32 keys per pair of waves");
 
 template <int D>
 struct BwdCfg {
@@ -244,18 +246,23 @@ struct BwdCfg {
   static constexpr int CPR = D / 8;
   static constexpr int TILEB = kRowTile * ROWB;        // one Q (or dO) tile
   static constexpr int RPI = 64 / CPR;                 // rows per wave-wide 1 KiB load
-  static constexpr int LPW = kRowTile / RPI / 4;       // loads per wave per tile
+  static constexpr int LPW = kRowTile / RPI / kDkvWaves;   // loads per wave per tile
   static constexpr int DC = D / 32;
   static constexpr int DB = D / 16;
+  static constexpr int DBH = DB / 2;                   // 16-wide d blocks in half of D
   // LDS: the two stages' Q tiles, then their dO tiles, then per stage the
-  // rows' log-sum-exp and D (64 floats each).  Every Q and dO read then
-  // addresses from a per-lane base with an immediate offset below 64 KiB that
-  // folds in the stage.
+  // rows' log-sum-exp and D (64 floats each), then per wave the P and dS
+  // fragments it hands to the other wave of its pair.  Every Q and dO read
+  // addresses from a per-lane base with an immediate offset below 64 KiB
+  // that folds in the stage.
   static constexpr int QOFF = 0;
   static constexpr int GOFF = 2 * TILEB;
   static constexpr int LOFF = 4 * TILEB;
   static constexpr int LSTAGE = 2 * kRowTile * 4;
-  static constexpr int LDSB = LOFF + 2 * LSTAGE;
+  static constexpr int XOFF = LOFF + 2 * LSTAGE;
+  static constexpr int XWAVE = 2 * 2 * 64 * 16;       // [key block][P, dS][lane] x 16 bytes
+  static constexpr int LDSB = XOFF + kDkvWaves * XWAVE;
+  static_assert(LPW >= 1 && LPW * RPI * kDkvWaves == kRowTile, "row tile loads split evenly over the waves");
 };
 
 // Per-lane byte offsets of one row tile's loads: Q and dO rows (load j of
@@ -311,95 +318,127 @@ __device__ inline void issue_rows(__amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsr
   if (wave < 2) lds_dma4(wave == 0 ? rl : rd, ldst + (uint32_t)(wave * kRowTile * 4), o.l, 0);
 }
 
-// One tile of 64 query rows for one wave's 16 keys: the stage's Q tile at
-// `ql`, its dO tile at `gl`, the rows' log-sum-exp and D at `ls`.
+// Every wave's LDS writes done and visible to the workgroup, without waiting
+// for the next row tile's loads still in flight into the other stage.
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// One tile of 64 query rows for one wave of a pair.  The pair shares 32 keys,
+// two 16-key blocks kb whose K and V the wave keeps in registers.  Wave half h
+// forms S = Q K^T and dP = dO V^T for rows 32h .. 32h + 31 (keys along the
+// accumulator columns, so P and dS come out in the B-operand layout of the
+// products over rows), hands P and dS to the other wave through LDS at `xl`
+// (the other wave's at `xo`), and then accumulates dV^T += dO^T P and
+// dK^T += Q^T dS over all 64 rows for its half of D, whose A operands are
+// transposing reads of the dO and Q tiles.  Stage: Q tile at `ql`, dO tile at
+// `gl`, the rows' log-sum-exp and D at `ls`.
 template <int D>
-__device__ inline void dkdv_tile(const lds_char* ql, const lds_char* gl, const lds_char* ls, int lane,
-                                 const bf16x8 (&kf)[BwdCfg<D>::DC], const bf16x8 (&vf)[BwdCfg<D>::DC],
-                                 f32x4 (&dk)[BwdCfg<D>::DB], f32x4 (&dv)[BwdCfg<D>::DB], float c, bool need_mask,
-                                 int f0, int f_begin, int f_end) {
+__device__ inline void dkdv_tile(const lds_char* ql, const lds_char* gl, const lds_char* ls, lds_char* xl,
+                                 const lds_char* xo, int lane, int h, const bf16x8 (&kf)[2][BwdCfg<D>::DC],
+                                 const bf16x8 (&vf)[2][BwdCfg<D>::DC], f32x4 (&dk)[BwdCfg<D>::DBH][2],
+                                 f32x4 (&dv)[BwdCfg<D>::DBH][2], float c, bool need_mask, int f0,
+                                 const int (&f_begin)[2], const int (&f_end)[2]) {
   using C = BwdCfg<D>;
   const float* l2s = (const float*)ls;
   const float* dls = l2s + kRowTile;
   const int lr = lane & 15;
   const int lg = lane >> 4;
 
-  // s[rb][i], dp[rb][i]: query row 16*rb + 4*lg + i of the tile against key lr.
-  f32x4 s[4], dp[4];
+  // s[rb][kb][i], dp[rb][kb][i]: row 32h + 16*rb + 4*lg + i of the tile against key 16*kb + lr.
+  f32x4 s[2][2], dp[2][2];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    s[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    dp[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  // Each 32-wide d chunk: its eight Q and dO fragment reads first, then the
-  // eight products, so the reads' LDS latency overlaps.
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dp[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  // Each 32-wide d chunk: its four Q and dO fragment reads first, then the
+  // eight products, each fragment serving both key blocks.
 #pragma unroll
   for (int dc = 0; dc < C::DC; ++dc) {
-    bf16x8 qa[4], ga[4];
+    bf16x8 qa[2], ga[2];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const int row = 16 * rb + lr;
+    for (int rb = 0; rb < 2; ++rb) {
+      const int row = 32 * h + 16 * rb + lr;
       const int off = row * C::ROWB + (((4 * dc + lg) ^ swz<D>(row)) * 16);
       qa[rb] = *(const lds_bf16x8*)(ql + off);
       ga[rb] = *(const lds_bf16x8*)(gl + off);
     }
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      s[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rb], kf[dc], s[rb], 0, 0, 0);
-      dp[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga[rb], vf[dc], dp[rb], 0, 0, 0);
-    }
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rb], kf[kb][dc], s[rb][kb], 0, 0, 0);
+        dp[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga[rb], vf[kb][dc], dp[rb][kb], 0, 0, 0);
+      }
   }
   // A row that saw no key has L = -inf and gives exp2(+inf) here; every pair
   // of such a row is masked below (an unmasked tile holds only rows that see
   // all its keys), so no per-element test is needed.
-  float p[4][4], d[4][4];
+  float p[2][2][4], d[2][2][4];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    const f32x4 lse = *(const __attribute__((address_space(3))) f32x4*)(l2s + 16 * rb + 4 * lg);
-    const f32x4 dl = *(const __attribute__((address_space(3))) f32x4*)(dls + 16 * rb + 4 * lg);
+  for (int rb = 0; rb < 2; ++rb) {
+    const f32x4 lse = *(const __attribute__((address_space(3))) f32x4*)(l2s + 32 * h + 16 * rb + 4 * lg);
+    const f32x4 dl = *(const __attribute__((address_space(3))) f32x4*)(dls + 32 * h + 16 * rb + 4 * lg);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[rb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][i], c, -kLog2e * lse[i]));
-      d[rb][i] = p[rb][i] * (dp[rb][i] - dl[i]);
-    }
-  }
-  if (need_mask) {
-    // This lane's key is visible to flat rows f0 + r in [f_begin, f_end): from
-    // the first row of the first token at or after its position (causal) up
-    // to the last valid row; f_end is 0 for a key past the block's end.
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int f = f0 + 16 * rb + 4 * lg + i;
-        const bool vis = (f >= f_begin) & (f < f_end);
-        p[rb][i] = vis ? p[rb][i] : 0.f;
-        d[rb][i] = vis ? d[rb][i] : 0.f;
+        p[rb][kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][kb][i], c, -kLog2e * lse[i]));
+        d[rb][kb][i] = p[rb][kb][i] * (dp[rb][kb][i] - dl[i]);
       }
   }
-  // P and dS in the B-operand layout of the products over query rows: k-slot
-  // 8*lg + i of row chunk ch is row 32*ch + 4*lg + i (i < 4) or
-  // 32*ch + 16 + 4*lg + i - 4.
-  bf16x8 pf[2], df[2];
+  if (need_mask) {
+    // Key 16*kb + lr of this lane is visible to flat rows in [f_begin[kb],
+    // f_end[kb]): from the first row of the first token at or after its
+    // position (causal) up to the last valid row; f_end is 0 for a key past
+    // the block's end.
 #pragma unroll
-  for (int ch = 0; ch < 2; ++ch) {
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int f = f0 + 32 * h + 16 * rb + 4 * lg + i;
+          const bool vis = (f >= f_begin[kb]) & (f < f_end[kb]);
+          p[rb][kb][i] = vis ? p[rb][kb][i] : 0.f;
+          d[rb][kb][i] = vis ? d[rb][kb][i] : 0.f;
+        }
+  }
+  // P and dS of row chunk h (rows 32h .. 32h + 31) in the B-operand layout of
+  // the products over rows: k-slot 8*lg + i is row 32h + 4*lg + i (i < 4) or
+  // 32h + 16 + 4*lg + i - 4.
+  bf16x8 pf[2][2], df[2][2];   // [own chunk, other wave's chunk][kb]
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
     bf16x2 w[4], x[4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      w[2 * h] = pack_bf16x2(p[2 * ch + h][0], p[2 * ch + h][1]);
-      w[2 * h + 1] = pack_bf16x2(p[2 * ch + h][2], p[2 * ch + h][3]);
-      x[2 * h] = pack_bf16x2(d[2 * ch + h][0], d[2 * ch + h][1]);
-      x[2 * h + 1] = pack_bf16x2(d[2 * ch + h][2], d[2 * ch + h][3]);
+    for (int rb = 0; rb < 2; ++rb) {
+      w[2 * rb] = pack_bf16x2(p[rb][kb][0], p[rb][kb][1]);
+      w[2 * rb + 1] = pack_bf16x2(p[rb][kb][2], p[rb][kb][3]);
+      x[2 * rb] = pack_bf16x2(d[rb][kb][0], d[rb][kb][1]);
+      x[2 * rb + 1] = pack_bf16x2(d[rb][kb][2], d[rb][kb][3]);
     }
-    pf[ch] = __builtin_bit_cast(bf16x8, w);
-    df[ch] = __builtin_bit_cast(bf16x8, x);
+    pf[0][kb] = __builtin_bit_cast(bf16x8, w);
+    df[0][kb] = __builtin_bit_cast(bf16x8, x);
+    *(lds_bf16x8*)(xl + ((2 * kb) * 64 + lane) * 16) = pf[0][kb];
+    *(lds_bf16x8*)(xl + ((2 * kb + 1) * 64 + lane) * 16) = df[0][kb];
   }
-  // dV^T[d][key] += sum_row dO^T[d][row] P[row][key];  dK^T += Q^T dS, with the
-  // transposed operands read from the row-major dO and Q tiles.
+  // The other wave wrote the same lanes' fragments of its row chunk 1 - h.
+  lds_barrier();
 #pragma unroll
-  for (int ch = 0; ch < 2; ++ch) {
+  for (int kb = 0; kb < 2; ++kb) {
+    pf[1][kb] = *(const lds_bf16x8*)(xo + ((2 * kb) * 64 + lane) * 16);
+    df[1][kb] = *(const lds_bf16x8*)(xo + ((2 * kb + 1) * 64 + lane) * 16);
+  }
+  // dV^T[d][key] += sum_row dO^T[d][row] P[row][key];  dK^T += Q^T dS, over
+  // both row chunks, for d blocks DBH*h .. DBH*h + DBH - 1.
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
+  for (int j = 0; j < 2; ++j) {
+    const int ch = j == 0 ? h : 1 - h;
+#pragma unroll
+    for (int dbl = 0; dbl < C::DBH; ++dbl) {
+      const int db = C::DBH * h + dbl;
       const int row0 = 32 * ch + 4 * lg + (lr >> 2);
       const int row1 = row0 + 16;
       const int cidx = 2 * db + ((lr & 3) >> 1);
@@ -412,14 +451,17 @@ __device__ inline void dkdv_tile(const lds_char* ql, const lds_char* gl, const l
       const s16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(ql + o1));
       const bf16x8 gt = __builtin_bit_cast(bf16x8, s16x8{g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]});
       const bf16x8 qt = __builtin_bit_cast(bf16x8, s16x8{q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]});
-      dv[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gt, pf[ch], dv[db], 0, 0, 0);
-      dk[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt, df[ch], dk[db], 0, 0, 0);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        dv[dbl][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gt, pf[j][kb], dv[dbl][kb], 0, 0, 0);
+        dk[dbl][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt, df[j][kb], dk[dbl][kb], 0, 0, 0);
+      }
     }
   }
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * kDkvWaves, 1) void dkdv_kernel(BwdArgs a) {
   using C = BwdCfg<D>;
   __shared__ __attribute__((aligned(16))) char lds[C::LDSB];
   const QSide& qs = a.qs;
@@ -431,10 +473,10 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdArgs a) {
   int si = 0;
   while (si + 1 < a.n_seg && a.tile_begin[si + 1] <= tile) ++si;
   const Seg& sg = a.seg[si];
-  const int k0 = (tile - a.tile_begin[si]) * kTileKeys;
+  const int k0 = (tile - a.tile_begin[si]) * kDkvKeys;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int key_idx = k0 + 16 * wave + (lane & 15);   // this lane's key (column of S)
+  const int h = wave & 1;                       // half of the pair: its rows in S, its half of D in dK, dV
   const int n_keys = sg.n;
   const int total = qs.q_len * qs.G;
   // Flat row from which a key at position pos is visible (causal): the first
@@ -444,35 +486,44 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdArgs a) {
     const int64_t r = (pos - qs.q_pos0) * qs.G;
     return (int)(r < 0 ? 0 : (r > total ? total : r));
   };
-  const int f_begin = first_row(sg.pos0 + key_idx);
-  const int f_end = key_idx < n_keys ? total : 0;
+  // This lane's keys (columns of S): 16*kb + lane%16 of the pair's 32.
+  int key_idx[2], f_begin[2], f_end[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    key_idx[kb] = k0 + 32 * (wave >> 1) + 16 * kb + (lane & 15);
+    f_begin[kb] = first_row(sg.pos0 + key_idx[kb]);
+    f_end[kb] = key_idx[kb] < n_keys ? total : 0;
+  }
 
-  // The wave's 16 keys as B operands: key 16*wave + lane%16, d = 32*dc + 8*(lane/16) .. +7.
-  bf16x8 kf[C::DC], vf[C::DC];
-  {
-    const int kk = min(key_idx, n_keys - 1);
+  // The pair's keys as B operands: key 32*(wave/2) + 16*kb + lane%16, d = 32*dc + 8*(lane/16) .. +7.
+  bf16x8 kf[2][C::DC], vf[2][C::DC];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int kk = min(key_idx[kb], n_keys - 1);
     const uint16_t* kp = (const uint16_t*)sg.k + (int64_t)b * sg.ks_b + (int64_t)kk * sg.ks_t + (int64_t)g * sg.ks_h +
                          8 * (lane >> 4);
     const uint16_t* vp = (const uint16_t*)sg.v + (int64_t)b * sg.vs_b + (int64_t)kk * sg.vs_t + (int64_t)g * sg.vs_h +
                          8 * (lane >> 4);
 #pragma unroll
     for (int dc = 0; dc < C::DC; ++dc) {
-      kf[dc] = *(const bf16x8*)(kp + 32 * dc);
-      vf[dc] = *(const bf16x8*)(vp + 32 * dc);
+      kf[kb][dc] = *(const bf16x8*)(kp + 32 * dc);
+      vf[kb][dc] = *(const bf16x8*)(vp + 32 * dc);
     }
   }
-  f32x4 dk[C::DB], dv[C::DB];
+  f32x4 dk[C::DBH][2], dv[C::DBH][2];
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) {
-    dk[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    dv[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int dbl = 0; dbl < C::DBH; ++dbl)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      dk[dbl][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dv[dbl][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
   // Query-row tiles that can see a key of this tile: with the causal rule,
   // rows from the first token at or after the tile's first key position.  Rows
   // below full_from miss at least one of the tile's keys.
   const int r_begin = first_row(sg.pos0 + k0);
-  const int full_from = first_row(sg.pos0 + min(k0 + kTileKeys, n_keys) - 1);
+  const int full_from = first_row(sg.pos0 + min(k0 + kDkvKeys, n_keys) - 1);
   const int t_end = (total + kRowTile - 1) / kRowTile;
   const int t_begin = r_begin >= total ? t_end : r_begin / kRowTile;
 
@@ -486,6 +537,8 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdArgs a) {
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse + row0, a.rows_bytes);
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.delta + row0, a.rows_bytes);
     const uint32_t lds_addr = (uint32_t)(size_t)(lds_char*)lds;
+    lds_char* xl = (lds_char*)lds + C::XOFF + wave * C::XWAVE;
+    const lds_char* xo = (const lds_char*)lds + C::XOFF + (wave ^ 1) * C::XWAVE;
     // When the group size divides the row tile, the rows of tile t are those
     // of tile 0 moved by 64 t / G tokens: each lane's offsets are computed once
     // and stepped.  A tile that reaches past the last row (clamped loads), or
@@ -511,16 +564,18 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdArgs a) {
     };
     // One row tile in stage `cur` (a constant in each unrolled copy below, so
     // the stage's LDS offsets are immediates): wait for it, let the next one
-    // start loading into the other stage, multiply.
+    // start loading into the other stage, multiply.  The barrier also ends
+    // every wave's reads of the other stage and of the P/dS hand-over area
+    // from the previous tile.
     auto step = [&](int t, int cur) {
       wait_all_loads();
       __syncthreads();
       if (t > t_begin) issue(t - 1, cur ^ 1);
       const int f0 = t * kRowTile;
-      const bool need_mask = (k0 + kTileKeys > n_keys) || (f0 + kRowTile > total) || (f0 < full_from);
+      const bool need_mask = (k0 + kDkvKeys > n_keys) || (f0 + kRowTile > total) || (f0 < full_from);
       const lds_char* l = (const lds_char*)lds;
-      dkdv_tile<D>(l + C::QOFF + cur * C::TILEB, l + C::GOFF + cur * C::TILEB, l + C::LOFF + cur * C::LSTAGE, lane,
-                   kf, vf, dk, dv, qs.c, need_mask, f0, f_begin, f_end);
+      dkdv_tile<D>(l + C::QOFF + cur * C::TILEB, l + C::GOFF + cur * C::TILEB, l + C::LOFF + cur * C::LSTAGE, xl,
+                   xo, lane, h, kf, vf, dk, dv, qs.c, need_mask, f0, f_begin, f_end);
     };
     // Row tiles are walked from the last one down: every workgroup of a KV
     // head then starts at the same row tile and the resident ones stream Q
@@ -537,18 +592,23 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdArgs a) {
   }
 
   // dk[b, key, g, 16*db + 4*(lane/16) + i] += scale * dK^T; dv likewise, unscaled.
-  if (key_idx < n_keys && t_begin < t_end) {
-    const int64_t base = (((int64_t)b * n_keys + key_idx) * Hkv + g) * D + 4 * (lane >> 4);
-    float* dkp = a.dk[si] + base;
-    float* dvp = a.dv[si] + base;
+  if (t_begin < t_end) {
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
-      f32x4 x = *(f32x4*)(dkp + 16 * db);
-      x += dk[db] * a.scale;
-      *(f32x4*)(dkp + 16 * db) = x;
-      f32x4 y = *(f32x4*)(dvp + 16 * db);
-      y += dv[db];
-      *(f32x4*)(dvp + 16 * db) = y;
+    for (int kb = 0; kb < 2; ++kb) {
+      if (key_idx[kb] >= n_keys) continue;
+      const int64_t base = (((int64_t)b * n_keys + key_idx[kb]) * Hkv + g) * D + 4 * (lane >> 4);
+      float* dkp = a.dk[si] + base;
+      float* dvp = a.dv[si] + base;
+#pragma unroll
+      for (int dbl = 0; dbl < C::DBH; ++dbl) {
+        const int db = C::DBH * h + dbl;
+        f32x4 x = *(f32x4*)(dkp + 16 * db);
+        x += dk[dbl][kb] * a.scale;
+        *(f32x4*)(dkp + 16 * db) = x;
+        f32x4 y = *(f32x4*)(dvp + 16 * db);
+        y += dv[dbl][kb];
+        *(f32x4*)(dvp + 16 * db) = y;
+      }
     }
   }
 }
@@ -571,10 +631,10 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int n_key_tiles, int D, hipStream_t
   dim3 grid_k(n_key_tiles * a.qs.Hkv * a.qs.B);
   if (D == 128) {
     hipLaunchKernelGGL(dq_kernel<128>, grid_q, dim3(64 * kDqWaves), 0, s, a);
-    if (n_key_tiles > 0) hipLaunchKernelGGL(dkdv_kernel<128>, grid_k, dim3(kThreads), 0, s, a);
+    if (n_key_tiles > 0) hipLaunchKernelGGL(dkdv_kernel<128>, grid_k, dim3(64 * kDkvWaves), 0, s, a);
   } else {
     hipLaunchKernelGGL(dq_kernel<64>, grid_q, dim3(64 * kDqWaves), 0, s, a);
-    if (n_key_tiles > 0) hipLaunchKernelGGL(dkdv_kernel<64>, grid_k, dim3(kThreads), 0, s, a);
+    if (n_key_tiles > 0) hipLaunchKernelGGL(dkdv_kernel<64>, grid_k, dim3(64 * kDkvWaves), 0, s, a);
   }
   return hipGetLastError();
 }

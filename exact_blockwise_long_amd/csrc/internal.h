@@ -163,8 +163,10 @@ struct FinalizeArgs {
 // Backward of one call's visits: dq (fp32, state-row order [rows, D]) and the
 // visited blocks' dk, dv (fp32 [n, Hkv, D] each) accumulate.  dout uses Q's
 // strides; lse (natural log) and delta are per state row.  The dK/dV kernel's
-// grid covers tile_begin[n_seg] 64-key tiles: tiles [tile_begin[s],
+// grid covers tile_begin[n_seg] tiles of kDkvKeys keys: tiles [tile_begin[s],
 // tile_begin[s+1]) are segment s's.
+constexpr int kDkvKeys = 128;   // keys per workgroup of the dK/dV kernel
+
 struct BwdArgs {
   QSide qs;
   const void* dout;
