@@ -15,11 +15,13 @@
 //    forward walk (the same LDS tile pipeline): S^T = K Q^T and dP^T = V dO^T
 //    with Q and dO in registers, then dQ^T += K^T dS^T with K^T read from the
 //    row-major K tile by ds_read_b64_tr_b16.
-//  * dkdv_kernel owns 64 keys of one visited block (16 per wave, their K and V
-//    in registers) and walks tiles of 64 query rows staged in LDS:
-//    S = Q K^T and dP = dO V^T put keys along the accumulator columns, so P and
-//    dS come out in the B-operand layout of dV^T += dO^T P and dK^T += Q^T dS,
-//    whose A operands are transposing reads of the dO and Q tiles.
+//  * dkdv_kernel owns 128 keys of one visited block (32 per pair of waves,
+//    their K and V in registers) and walks tiles of 64 query rows staged in
+//    LDS: each wave forms S = Q K^T and dP = dO V^T for half the rows, keys
+//    along the accumulator columns, so P and dS come out in the B-operand
+//    layout of dV^T += dO^T P and dK^T += Q^T dS; the pair swaps them through
+//    LDS, and each wave accumulates dK and dV for half the head dim over all
+//    the rows, with transposing reads of the dO and Q tiles as A operands.
 #include "bf16_tiles.h"
 
 namespace ba {
