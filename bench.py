@@ -27,6 +27,7 @@ Prints exactly one JSON line (on stdout); progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import shutil
 import subprocess
 import threading
@@ -182,6 +183,7 @@ def bench_backward(torch, ba, H, w, steps, warmup):
     log(f"inputs: {w.name} (backward)")
     q, k, v = w.make_inputs()
     do = w.make_dout()
+    sha = input_sha256((q, k, v, do), ("q", "k", "v", "dout"))
     qd, kd, vd, dod = H.to_device(q), H.to_device(k), H.to_device(v), H.to_device(do)
     del q, k, v, do
     L = w.block_len
@@ -224,7 +226,7 @@ def bench_backward(torch, ba, H, w, steps, warmup):
             "bwd_block_ms_mean": round(kms, 3), "bwd_block_TFLOP/s": round(ktf, 1),
             "bwd_block_frac_of_bf16_peak": round(ktf / PEAK_BF16_TFLOPS, 4),
             "algorithmic_flops_per_step": alg, "executed_mfma_flops_per_step": 3.5 * w.flops(),
-            "step": "zero dq/dk/dv, bwd_delta, bwd_block (dq_kernel + dkdv_kernel)"}
+            "step": "zero dq/dk/dv, bwd_delta, bwd_block (dq_kernel + dkdv_kernel)", "input_sha256": sha}
 
 
 def _smi_sample():
@@ -393,9 +395,13 @@ def bench_fanout_paged(torch, ba, H, w, steps, warmup, page_len=256):
     q, pk, pv, sk, sv = w.make_inputs()
     g = np.random.Generator(np.random.PCG64(w.seed + 500))
     n_pool, pp, sp = wl.paged_layout(g, w.n_branches, w.prefix_len, w.suffix_len, page_len)
-    kd = H.to_device(wl.scatter_pages(g, pk, sk, n_pool, pp, sp, page_len))
-    vd = H.to_device(wl.scatter_pages(g, pv, sv, n_pool, pp, sp, page_len))
-    del pk, pv, sk, sv
+    kpool = wl.scatter_pages(g, pk, sk, n_pool, pp, sp, page_len)
+    vpool = wl.scatter_pages(g, pv, sv, n_pool, pp, sp, page_len)
+    sha = {"q": q.sha256(), "k_pool": kpool.sha256(), "v_pool": vpool.sha256(),
+           "prefix_pages": hashlib.sha256(pp.tobytes()).hexdigest(),
+           "suffix_pages": hashlib.sha256(sp.tobytes()).hexdigest()}
+    kd, vd = H.to_device(kpool), H.to_device(vpool)
+    del pk, pv, sk, sv, kpool, vpool
     qd = H.to_device(q)
     ppd, spd = torch.from_numpy(pp).cuda(), torch.from_numpy(sp).cuda()
     nb, Hq, D = qd.shape
@@ -423,7 +429,8 @@ def bench_fanout_paged(torch, ba, H, w, steps, warmup, page_len=256):
     log(f"fanout paged: {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
     return {"workload": w.name + f", paged (page_len {page_len}, random pool order)", "us": round(ms * 1e3, 2),
             "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "pool_pages": int(n_pool),
-            "timing": "median over steps, HIP events around the call, 1 GiB read between calls evicts the caches"}
+            "timing": "median over steps, HIP events around the call, 1 GiB read between calls evicts the caches",
+            "input_sha256": sha}
 
 
 def bench_shard_merge(torch, ba, H, w, steps, warmup):
@@ -476,6 +483,9 @@ def bench_merge_scaled(torch, ba, steps, warmup, n_parts=32, rows=131072, D=128)
         l = torch.rand(rows, device="cuda", generator=g) + 0.5
         o = torch.randn(rows, D, device="cuda", generator=g)
         parts.append((m, l, o))
+    h = hashlib.sha256()   # the bits of every part's m, l, O in order
+    for t in (x for part in parts for x in part):
+        h.update(t.cpu().numpy().tobytes())
     out = ba.new_state(rows, D)
     flush = flush_buffer(torch)
     for _ in range(warmup):
@@ -492,7 +502,9 @@ def bench_merge_scaled(torch, ba, steps, warmup, n_parts=32, rows=131072, D=128)
     gbs = nbytes / ms / 1e6
     log(f"merge scaled: {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
     return {"workload": f"{n_parts}-way merge, {rows} rows, D={D}, fp32", "us": round(ms * 1e3, 2),
-            "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes}
+            "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes,
+            "inputs": "torch CUDA generator, seed 6: per part m = 5 N(0,1), l = U(0.5, 1.5), O = N(0,1)",
+            "input_sha256": {"parts_m_l_o": h.hexdigest()}}
 
 
 def bench_fanout_prefill(torch, ba, H, w, steps, warmup):
@@ -501,6 +513,7 @@ def bench_fanout_prefill(torch, ba, H, w, steps, warmup):
     issued one branch at a time (the prefix then streams once per branch)."""
     log(f"inputs: {w.name}")
     ins = w.make_inputs()
+    sha = input_sha256(ins, FANOUT_NAMES)
     q, pk, pv, sk, sv = [H.to_device(t) for t in ins]
     del ins
     nb, T, Hq, D = q.shape
@@ -520,7 +533,7 @@ def bench_fanout_prefill(torch, ba, H, w, steps, warmup):
             ba.fanout_prefix_prefill(q[b:b + 1], pk, pv, sk[b:b + 1], sv[b:b + 1], workspace=ws1,
                                      out=out[b:b + 1], lse=lse[b:b + 1])
 
-    res = {"workload": w.name, "algorithmic_flops": w.flops(), "algorithmic_bytes": w.bytes()}
+    res = {"workload": w.name, "algorithmic_flops": w.flops(), "algorithmic_bytes": w.bytes(), "input_sha256": sha}
     for name, fn in (("batched", batched), ("per_branch", per_branch)):
         for _ in range(warmup):
             fn()
@@ -551,10 +564,11 @@ def bench_layouts(torch, ba, H, w, reps):
     from exact_blockwise_long_amd import layouts as L
     log(f"inputs: {w.name}")
     q, k, v = w.make_inputs()
+    sha = input_sha256((q, k, v))
     qd, kd, vd = H.to_device(q), H.to_device(k), H.to_device(v)
     del q, k, v
     n = w.n_devices
-    res = {"workload": w.name, "n_devices": n, "algorithmic_flops": w.flops(), "layouts": {}}
+    res = {"workload": w.name, "n_devices": n, "algorithmic_flops": w.flops(), "layouts": {}, "input_sha256": sha}
     for layout in L.LAYOUTS:
         calls = []
         for dev in range(n):
