@@ -139,6 +139,34 @@ def test_backward_matches_oracle(case, per_visit):
             assert not dk[dead].any() and not dv[dead].any(), "gradient on keys no query sees"
 
 
+# Key counts at the edges of the dK/dV workgroup (128 keys: four pairs of waves
+# on 32 keys each, in two 16-key blocks): a pair wholly past a block's end, a
+# block ending inside a pair or inside a 16-key block, one key past a
+# workgroup; with group sizes that do not divide the 64-row tile (each tile's
+# row offsets computed in full) and ones that do (offsets stepped per tile).
+EDGE_CASES = [
+    # (seed, T, Hq, Hkv, D, lens, q_pos0, causal)
+    (48, 65, 6, 2, 128, [31, 33, 96], 80, True),      # G = 3
+    (49, 40, 10, 2, 64, [127, 129], 0, False),        # G = 5
+    (50, 33, 16, 1, 128, [255, 257], 300, True),      # G = 16
+    (51, 129, 8, 1, 128, [32, 128, 1], 140, True),    # G = 8
+]
+
+
+@pytest.mark.parametrize("case", EDGE_CASES, ids=lambda c: f"seed{c[0]}")
+def test_backward_dkdv_workgroup_edges(case):
+    seed, T, Hq, Hkv, D, lens, q_pos0, causal = case
+    order = list(range(len(lens)))[::-1]
+    announce(f"bwd workgroup edges seed {seed} T={T} Hq={Hq} Hkv={Hkv} D={D} lens={lens} q_pos0={q_pos0} "
+             f"causal={causal}")
+    q, k, v, do = make_case(seed, T, Hq, Hkv, D, lens)
+    dq, dk, dv = gpu_grads(q, k, v, do, lens, order, Hkv=Hkv, q_pos0=q_pos0, causal=causal, per_visit=True)
+    rq, rk, rv = oracle_grads(q, k, v, do, q_pos0, causal)
+    check_grad(dq, rq, f"seed{seed} dQ")
+    check_grad(dk, rk, f"seed{seed} dK")
+    check_grad(dv, rv, f"seed{seed} dV")
+
+
 def test_backward_positions_beyond_32_bits():
     """The backward of a causal walk whose absolute positions start at 3e9."""
     seed, T, Hq, Hkv, D, lens, order = 47, 90, 8, 2, 128, [100, 64, 129], [2, 0, 1]
